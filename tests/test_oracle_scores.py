@@ -1,0 +1,97 @@
+"""Pins for the oracle's approximate scores and bin-midpoint reconstruction.
+
+Independent checks: at full depth the score is the plain 4-bit dequantized dot product
+(numpy fp64 matmul); at depth 0 every key scores the same constant; a brute-force
+reconstruction that averages every 4-bit code consistent with the planes read;
+hand-worked midpoints; linearity in the query.
+"""
+import numpy as np
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from bit_plane_kv_amd import synth
+
+
+def _head(n=700, d=128, G=3, seed=1):
+    x = synth.keys_np(seed, 7, [0], n, d)[0]
+    q = synth.queries_np(seed, 7, [0], G, d)[0]
+    s, z, codes = oracle.quantize(x)
+    return x, q, s, z, codes
+
+
+def test_full_depth_is_dequantized_dot_product():
+    x, q, s, z, codes = _head()
+    depth = np.full(128, 4, np.uint8)
+    got = oracle.scores(codes, s, z, depth, q)
+    deq = z[None, :].astype(np.float64) + s[None, :].astype(np.float64) * codes
+    ref = q.astype(np.float64) @ deq.T
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_zero_depth_scores_are_constant():
+    x, q, s, z, codes = _head()
+    depth = np.zeros(128, np.uint8)
+    got = oracle.scores(codes, s, z, depth, q)
+    const = q.astype(np.float64) @ (z.astype(np.float64) + 7.5 * s.astype(np.float64))
+    assert np.allclose(got, const[:, None], rtol=1e-12, atol=1e-12)
+    assert (got == got[:, :1]).all()
+    # every score equal: the top k are the k lowest token indices
+    assert oracle.topk(got[0].astype(np.float32), 16).tolist() == list(range(16))
+
+
+def test_hand_midpoints():
+    assert [oracle.midpoint_level(13, t) for t in (1, 2, 3, 4)] == [11.5, 13.5, 12.5, 13.0]
+    assert oracle.midpoint_level(13, 0) == 7.5 and oracle.midpoint_level(0, 0) == 7.5
+    assert [oracle.midpoint_level(0, t) for t in (1, 2, 3, 4)] == [3.5, 1.5, 0.5, 0.0]
+    assert [oracle.midpoint_level(15, t) for t in (1, 2, 3, 4)] == [11.5, 13.5, 14.5, 15.0]
+
+
+@settings(max_examples=15, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1))
+def test_brute_force_bin_average(seed):
+    """Reconstruct each read channel as the mean of all 4-bit levels whose top t bits
+    match the planes read; score = q . that reconstruction."""
+    rng = np.random.default_rng(seed)
+    n, d, G = 40, 12, 2
+    x = (rng.standard_normal((n, d)) * 10 ** rng.uniform(-1, 1, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    s, z, codes = oracle.quantize(x)
+    planes = oracle.pack_planes(codes)
+    depth = rng.integers(0, 5, d).astype(np.uint8)
+    got = oracle.scores(codes, s, z, depth, q)
+    ref = np.zeros((G, n))
+    for i in range(n):
+        khat = np.empty(d)
+        for c in range(d):
+            t = int(depth[c])
+            p = oracle.plane_prefix(planes, c, t, i)
+            match = [v for v in range(16) if (v >> (4 - t)) == p] if t else list(range(16))
+            khat[c] = float(z[c]) + float(s[c]) * np.mean(match)
+        ref[:, i] = q.astype(np.float64) @ khat
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+def test_linear_in_query():
+    x, q, s, z, codes = _head(G=2)
+    depth = np.random.default_rng(3).integers(0, 5, 128).astype(np.uint8)
+    a = oracle.scores(codes, s, z, depth, q[:1])
+    b = oracle.scores(codes, s, z, depth, q[1:])
+    qs = (q[:1].astype(np.float64) + q[1:]).astype(np.float32)
+    exact_sum = (q[:1].astype(np.float64) + q[1:]) == qs.astype(np.float64)
+    if exact_sum.all():
+        c = oracle.scores(codes, s, z, depth, qs)
+        assert np.allclose(c, a + b, rtol=1e-10, atol=1e-10 * np.abs(c).max())
+    two = oracle.scores(codes, s, z, depth, (2 * q[:1]).astype(np.float32))
+    assert np.allclose(two, 2 * a, rtol=1e-12, atol=0)
+
+
+def test_batched_scores_equal_per_head():
+    x = synth.keys_np(2, 0, [0, 1], 300, 128)
+    q = synth.queries_np(2, 0, [0, 1], 4, 128)
+    s, z, codes = oracle.quantize(x)
+    var = oracle.channel_var(codes, s)
+    depth = oracle.plan(q, var, 92)
+    got = oracle.scores(codes, s, z, depth, q)
+    for h in range(2):
+        one = oracle.scores(codes[h], s[h], z[h], depth[h], q[h])
+        assert (one == got[h]).all()
