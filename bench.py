@@ -1,0 +1,307 @@
+"""Benchmark of the Fathom key-scan decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Workload (default): the Qwen3-8B-shaped cache in HBM -- 36 layers x 8 KV heads = 288
+(layer, KV head) pairs, 4 queries per KV head, d = 128, n = 32768 tokens, budget
+B = 92 bits per token per KV head, k = 512 winners per query.  One step is one pass of
+the whole hot path over all 288 heads in a single fathom_step call: plan, scan, top-k
+and sparse attention.  Inputs are seeded synthetic caches (keys s_c N(0,1) with
+log-uniform s_c in [0.1, 10], queries N(0,1), V N(0,1) in bf16), resident in HBM before
+timing starts.  Before timing, sampled heads are checked against the CPU oracle.
+
+Prints ONE JSON line: value = keys ranked per second over the whole step (Gkeys/s);
+roofline = the scan kernel's algorithmic bytes (planes read + fp32 scores written) per
+launch / its mean launch time, against 8 TB/s; cpu_baseline = the oracle on the host
+cores over a bounded sample of heads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scan Gkeys/s + % of HBM / PCIe roofline; 1M-token decode-step ms"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_8b_32k_hbm")
+    ap.add_argument("--budget", type=int, default=92)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          f"--gpus {args.gpus} is not supported"}))
+        sys.exit(2)
+
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+
+    cfg = synth.CONFIGS[args.config]
+    H, G, n, k, B = cfg.H, cfg.G, cfg.n, cfg.k, args.budget
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sm_scale = float(np.float32(1.0 / np.sqrt(128)))
+
+    # ---------------- inputs, resident in HBM ----------------
+    t0 = time.time()
+    heads = list(range(H))
+    st = F.Store.empty(H, n, dev)
+    K = torch.empty((H, n, 128), dtype=torch.bfloat16, device=dev)
+    qws = torch.empty(F.workspace_size(F.OP_QUANTIZE, 32, 1, n, 1), dtype=torch.uint8,
+                      device=dev)
+    sample_heads = sorted({0, H // 2, H - 1})
+    sample_keys = {}
+    for h0 in range(0, H, 32):
+        h1 = min(H, h0 + 32)
+        keys = synth.keys_torch(args.seed, cfg.cfg_id, range(h0, h1), n, dev)
+        F.fathom_quantize_store(keys, st.view_heads(h0, h1), ws=qws)
+        K[h0:h1].copy_(keys)
+        for h in sample_heads:
+            if h0 <= h < h1:
+                sample_keys[h] = keys[h - h0].cpu().numpy()
+        del keys
+    V = synth.values_torch(args.seed, cfg.cfg_id, heads, n, dev)
+    q_np = synth.queries_np(args.seed, cfg.cfg_id, heads, G)
+    q = torch.from_numpy(q_np).to(dev)
+    ws = F.step_workspace(st, G, k, dev)
+    depth = torch.empty((H, 128), dtype=torch.uint8, device=dev)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    idx = torch.empty((H, G, k), dtype=torch.int32, device=dev)
+    out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s: H={H} G={G} n={n} B={B} k={k}")
+
+    # ---------------- bit-exact checks before timing ----------------
+    F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, depth_out=depth, scores_out=scores,
+                  idx_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    parity = check_sample(st, q_np, K, V, depth, scores, idx, out, sample_keys, B, k,
+                          sm_scale)
+    log(f"[bench] parity on heads {sample_heads}: {parity}")
+
+    # ---------------- timed region: K whole steps ----------------
+    for _ in range(args.warmup):
+        F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, ws=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = H * n / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms (GPU time), wall {wall / args.steps * 1e3:.3f} ms"
+        f" -> {value:.1f} Gkeys/s")
+
+    # ---------------- per-kernel times (cold caches between launches) ----------------
+    kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
+                        stream, reps=max(10, min(args.steps, 30)))
+    plane_bytes = B / 8 * n * H
+    score_bytes = 4 * G * n * H
+    scan_bytes = plane_bytes + score_bytes
+    scan_ms = kern["scan_ms"]
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = load_traffic(scan_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "k_scan_main<4>",
+                "algorithmic_bytes_per_launch": int(scan_bytes)}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm_scale, sample_keys)
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "Gkeys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "kv_heads_x_layers": H, "queries_per_kv_head": G,
+                   "tokens": n, "d": 128, "budget_bits": B, "k": k, "residency": "hbm",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
+        "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
+        "bytes_per_step": {"planes": int(plane_bytes), "scores_written": int(score_bytes),
+                           "winner_rows": int(H * G * k * 512)},
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "parity_before_timing": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def check_sample(st, q_np, K, V, depth, scores, idx, out, sample_keys, B, k, sm):
+    """Oracle checks on sampled heads of the full-size step (planes, plan exact;
+    scores to 1e-5 of the row maximum; top-k exact on the GPU scores; attention)."""
+    import torch
+
+    import oracle
+    res = {"heads": sorted(sample_keys), "planes": True, "plan": True, "topk": True}
+    worst, aerr = 0.0, 0.0
+    for h, keys in sample_keys.items():
+        s, z, codes = oracle.quantize(keys)
+        if not np.array_equal(st.planes[h].cpu().numpy().view(np.uint32),
+                              oracle.pack_planes(codes)):
+            res["planes"] = False
+        var = oracle.channel_var(codes, s)
+        ref_depth = oracle.plan(q_np[h], var, B)
+        if not np.array_equal(depth[h].cpu().numpy(), ref_depth):
+            res["plan"] = False
+        ref = oracle.scores(codes, s, z, ref_depth, q_np[h])
+        got = scores[h].cpu().numpy()
+        worst = max(worst, float((np.abs(got - ref).max(axis=1) /
+                                  np.abs(ref).max(axis=1)).max()))
+        gi = idx[h].cpu().numpy()
+        if not np.array_equal(gi, oracle.topk(got, k)):
+            res["topk"] = False
+        Kh = K[h].cpu().view(torch.int16).numpy().view(np.uint16)[None]
+        Vh = V[h].cpu().view(torch.int16).numpy().view(np.uint16)[None]
+        att = oracle.attention(q_np[h][None], Kh, Vh, gi[None], sm)
+        aerr = max(aerr, float(np.abs(out[h].float().cpu().numpy() - att[0]).max()))
+    res["score_rel_err"] = worst
+    res["attn_abs_err"] = aerr
+    res["ok"] = bool(res["planes"] and res["plan"] and res["topk"] and worst <= 1e-5
+                     and aerr <= 2e-2)
+    return res
+
+
+def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream, reps):
+    """Mean duration of each kernel of the step, timed with events on the launch stream,
+    with a 1 GiB streaming read between launches so that every launch starts with cold
+    caches (the 256 MB last-level cache would otherwise hold part of the planes)."""
+    import torch
+    H, G = q.shape[0], q.shape[1]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    scan_ws = F.scan_workspace(st, G, dev)
+    F.fathom_scan_prepare(st, q, depth, scan_ws)
+    calls = {
+        "plan_ms": lambda: F.fathom_plan(st, q, B, depth=depth),
+        "scan_prepare_ms": lambda: F.fathom_scan_prepare(st, q, depth, scan_ws),
+        "scan_ms": lambda: F.fathom_scan_prepared(st, G, scores, scan_ws),
+        "topk_ms": lambda: F.fathom_topk(scores, k, idx=idx),
+        "attn_ms": lambda: F.fathom_sparse_attn(q, K, V, idx, sm, out=out),
+    }
+    res = {}
+    for name, fn in calls.items():
+        fn()
+        tot = 0.0
+        for _ in range(reps):
+            F.fathom_stream_read(flush, flush.numel(), sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            tot += a.elapsed_time(b)
+        res[name] = tot / reps
+    # the 136-bit fixed-depth comparator through the same store and kernel
+    fixed = F.fathom_plan_fixed(st, 34)
+    F.fathom_scan_prepare(st, q, fixed, scan_ws)
+    tot = 0.0
+    for _ in range(reps):
+        F.fathom_stream_read(flush, flush.numel(), sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        F.fathom_scan_prepared(st, G, scores, scan_ws)
+        b.record(stream)
+        b.synchronize()
+        tot += a.elapsed_time(b)
+    res["scan_fixed136_ms"] = tot / reps
+    # HBM streaming-read rate of this device (1 GiB, warm launch) for context
+    F.fathom_stream_read(flush, flush.numel(), sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        F.fathom_stream_read(flush, flush.numel(), sink)
+    b.record(stream)
+    b.synchronize()
+    res["hbm_stream_read_GBps"] = 5 * flush.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+    del flush
+    return res
+
+
+def load_traffic(algorithmic_bytes):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
+    taken on the current scan kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "scan_traffic.json")
+    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", "scan.hip")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("scan_hip_sha256") != digest:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm, sample_keys):
+    """The oracle (as it stands) on the host cores: plan + scores + top-k + attention
+    for a bounded sample of heads of the same workload; keys/s scaled to Gkeys/s."""
+    import torch
+
+    import oracle
+    from bit_plane_kv_amd import synth
+    n, G = cfg.n, cfg.G
+    heads, elapsed, done = [], 0.0, 0
+    batch = 8
+    h = 0
+    while elapsed < args.cpu_seconds and h < cfg.H:
+        hs = list(range(h, min(cfg.H, h + batch)))
+        keys = synth.keys_torch(args.seed, cfg.cfg_id, hs, n, "cuda").cpu().numpy()
+        s, z, codes = oracle.quantize(keys)          # store build: not part of a step
+        var = oracle.channel_var(codes, s)
+        Kh = K[hs[0]:hs[-1] + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+        Vh = V[hs[0]:hs[-1] + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+        qh = q_np[hs[0]:hs[-1] + 1]
+        t0 = time.perf_counter()
+        depth = oracle.plan(qh, var, B)
+        sc = oracle.scores(codes, s, z, depth, qh)
+        idx = oracle.topk(sc.astype(np.float32).reshape(-1, n), k).reshape(len(hs), G, k)
+        oracle.attention(qh, Kh, Vh, idx, sm)
+        elapsed += time.perf_counter() - t0
+        done += len(hs)
+        h += len(hs)
+    return {"value": round(done * n / elapsed / 1e9, 6), "unit": "Gkeys/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} of {cfg.H} heads (n={n}, G={G}, B={B}, k={k}): plan + fp64 "
+                      f"scores + top-k + attention, {elapsed:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+// C-ABI entry points of libfathom.so: argument checks on the host (nothing is enqueued
+// when they fail), device-visibility checks of the pointers, then the launches.
+#include <algorithm>
+#include <cstring>
+
+#include "common.h"
+
+using namespace fathom;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return FATHOM_OK;
+    g_last_hip = (int)e;
+    return FATHOM_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The GPU must be able to dereference p: device memory, or host memory that HIP has
+// pinned and mapped (hipHostMalloc / torch pinned tensors).
+int check_visible(const void *p) {
+    if (!p) return FATHOM_ERR_INVALID_ARG;
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    const hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+        return FATHOM_ERR_NOT_MAPPED;
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+        attr.type == hipMemoryTypeArray)
+        return FATHOM_OK;
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer == p) return FATHOM_OK;
+    return FATHOM_ERR_NOT_MAPPED;
+}
+
+int check_all(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs) {
+        if (!p) continue;
+        const int rc = check_visible(p);
+        if (rc != FATHOM_OK) return rc;
+    }
+    return FATHOM_OK;
+}
+
+int check_store(const fathom_store *st) {
+    if (!st) return FATHOM_ERR_INVALID_ARG;
+    if (st->n_heads < 1 || st->n_heads > 65535 || st->n_tokens < 1)
+        return FATHOM_ERR_INVALID_ARG;
+    if (st->word_stride < (st->n_tokens + 31) / 32) return FATHOM_ERR_INVALID_ARG;
+    if (!st->planes || !st->scale || !st->zero || !st->var) return FATHOM_ERR_INVALID_ARG;
+    if (!aligned(st->planes, 16) || !aligned(st->scale, 4) || !aligned(st->zero, 4) ||
+        !aligned(st->var, 4))
+        return FATHOM_ERR_INVALID_ARG;
+    if (st->d != FATHOM_D) return FATHOM_ERR_UNSUPPORTED;
+    return FATHOM_OK;
+}
+
+int check_g(int G) {
+    if (G < 1) return FATHOM_ERR_INVALID_ARG;
+    if (G > FATHOM_MAX_G) return FATHOM_ERR_UNSUPPORTED;
+    return FATHOM_OK;
+}
+
+int check_topk_k(int n, int k) {
+    if (n < 1 || k < 1 || k > n) return FATHOM_ERR_INVALID_ARG;
+    if (n > FATHOM_TOPK_CHUNK && k > FATHOM_TOPK_CHUNK / 2) return FATHOM_ERR_UNSUPPORTED;
+    return FATHOM_OK;
+}
+
+size_t step_ws_bytes(int H, int G, int n, int k) {
+    return round256(scan_ws_bytes(H, G)) + round256((size_t)H * G * n * sizeof(float)) +
+           round256(topk_ws_bytes(H * G, n, k)) + round256((size_t)H * G * k * sizeof(int32_t)) +
+           round256((size_t)H * FATHOM_D);
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+#define FATHOM_TRY(expr)                                                                 \
+    do {                                                                                 \
+        const int rc__ = (expr);                                                         \
+        if (rc__ != FATHOM_OK) return rc__;                                              \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int fathom_version(void) { return FATHOM_VERSION; }
+
+int fathom_last_hip_error(void) { return g_last_hip; }
+
+const char *fathom_status_string(int status) {
+    switch (status) {
+    case FATHOM_OK: return "ok";
+    case FATHOM_ERR_INVALID_ARG: return "invalid argument (null pointer, size or alignment)";
+    case FATHOM_ERR_BUDGET: return "bit budget outside [0, 4d]";
+    case FATHOM_ERR_UNSUPPORTED: return "unsupported shape (d != 128, G > 8 or k too large)";
+    case FATHOM_ERR_WORKSPACE: return "workspace too small";
+    case FATHOM_ERR_NOT_MAPPED: return "pointer not accessible by the GPU";
+    case FATHOM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int fathom_workspace_size(int op, int H, int G, int n, int k, size_t *bytes) {
+    if (!bytes) return FATHOM_ERR_INVALID_ARG;
+    *bytes = 0;
+    switch (op) {
+    case FATHOM_OP_QUANTIZE:
+        if (H < 1 || n < 1) return FATHOM_ERR_INVALID_ARG;
+        *bytes = quantize_ws_bytes(H, n);
+        return FATHOM_OK;
+    case FATHOM_OP_SCAN:
+        if (H < 1) return FATHOM_ERR_INVALID_ARG;
+        FATHOM_TRY(check_g(G));
+        *bytes = scan_ws_bytes(H, G);
+        return FATHOM_OK;
+    case FATHOM_OP_TOPK:
+        if (H < 1) return FATHOM_ERR_INVALID_ARG;
+        FATHOM_TRY(check_topk_k(n, k));
+        *bytes = topk_ws_bytes(H, n, k);
+        return FATHOM_OK;
+    case FATHOM_OP_STEP:
+        if (H < 1) return FATHOM_ERR_INVALID_ARG;
+        FATHOM_TRY(check_g(G));
+        FATHOM_TRY(check_topk_k(n, k));
+        *bytes = step_ws_bytes(H, G, n, k);
+        return FATHOM_OK;
+    default: return FATHOM_ERR_INVALID_ARG;
+    }
+}
+
+int fathom_quantize_store(const float *keys, int H, int n, int d, const fathom_store *st,
+                          void *ws, size_t ws_bytes, void *stream) {
+    if (!keys || !aligned(keys, 16)) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_store(st));
+    if (H != st->n_heads || n != st->n_tokens) return FATHOM_ERR_INVALID_ARG;
+    if (d != FATHOM_D) return FATHOM_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 16)) return FATHOM_ERR_INVALID_ARG;
+    if (ws_bytes < quantize_ws_bytes(H, n)) return FATHOM_ERR_WORKSPACE;
+    FATHOM_TRY(check_all({keys, st->planes, st->scale, st->zero, st->var, ws}));
+    return hip_status(launch_quantize_store(keys, H, n, *st, ws, as_stream(stream)));
+}
+
+int fathom_plan(const fathom_store *st, const float *q, int G, int B, uint8_t *depth,
+                void *stream) {
+    FATHOM_TRY(check_store(st));
+    if (!q || !depth || !aligned(q, 16)) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_g(G));
+    if (B < 0 || B > FATHOM_D * FATHOM_PLANES) return FATHOM_ERR_BUDGET;
+    FATHOM_TRY(check_all({st->var, q, depth}));
+    return hip_status(launch_plan(*st, q, G, B, depth, as_stream(stream)));
+}
+
+int fathom_plan_fixed(const fathom_store *st, int n_channels, uint8_t *depth, void *stream) {
+    FATHOM_TRY(check_store(st));
+    if (!depth) return FATHOM_ERR_INVALID_ARG;
+    if (n_channels < 0 || n_channels > FATHOM_D) return FATHOM_ERR_BUDGET;
+    FATHOM_TRY(check_all({st->var, depth}));
+    return hip_status(launch_plan_fixed(*st, n_channels, depth, as_stream(stream)));
+}
+
+static int scan_common(const fathom_store *st, int G, void *ws, size_t ws_bytes) {
+    FATHOM_TRY(check_store(st));
+    FATHOM_TRY(check_g(G));
+    if (!ws || !aligned(ws, 16)) return FATHOM_ERR_INVALID_ARG;
+    if (ws_bytes < scan_ws_bytes(st->n_heads, G)) return FATHOM_ERR_WORKSPACE;
+    return FATHOM_OK;
+}
+
+int fathom_scan_prepare(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                        void *ws, size_t ws_bytes, void *stream) {
+    FATHOM_TRY(scan_common(st, G, ws, ws_bytes));
+    if (!q || !depth || !aligned(q, 16)) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({q, depth, st->scale, st->zero, ws}));
+    return hip_status(launch_scan_prepare(*st, q, G, depth, ws, as_stream(stream)));
+}
+
+int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
+                         size_t ws_bytes, void *stream) {
+    FATHOM_TRY(scan_common(st, G, ws, ws_bytes));
+    if (!scores || !aligned(scores, 16)) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({st->planes, scores, ws}));
+    return hip_status(launch_scan_main(*st, G, scores, ws, as_stream(stream)));
+}
+
+int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                float *scores, void *ws, size_t ws_bytes, void *stream) {
+    FATHOM_TRY(scan_common(st, G, ws, ws_bytes));
+    if (!q || !depth || !scores || !aligned(q, 16) || !aligned(scores, 16))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({q, depth, st->planes, st->scale, st->zero, scores, ws}));
+    const hipStream_t s = as_stream(stream);
+    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, ws, s)));
+    return hip_status(launch_scan_main(*st, G, scores, ws, s));
+}
+
+int fathom_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
+                size_t ws_bytes, void *stream) {
+    if (!scores || !idx || !aligned(scores, 16) || !aligned(idx, 4) || R < 1)
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_topk_k(n, k));
+    const size_t need = topk_ws_bytes(R, n, k);
+    if (need > 0 && (!ws || !aligned(ws, 16))) return FATHOM_ERR_INVALID_ARG;
+    if (ws_bytes < need) return FATHOM_ERR_WORKSPACE;
+    FATHOM_TRY(check_all({scores, idx, need > 0 ? ws : nullptr}));
+    return hip_status(launch_topk(scores, R, n, k, idx, ws, as_stream(stream)));
+}
+
+int fathom_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H, int G,
+                       int n, int d, const int32_t *idx, int k, float sm_scale,
+                       uint16_t *out, void *stream) {
+    if (!q || !K || !V || !idx || !out) return FATHOM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(idx, 4) ||
+        !aligned(out, 2))
+        return FATHOM_ERR_INVALID_ARG;
+    if (H < 1 || n < 1 || k < 1 || k > n) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_g(G));
+    if (d != FATHOM_D) return FATHOM_ERR_UNSUPPORTED;
+    FATHOM_TRY(check_all({q, K, V, idx, out}));
+    return hip_status(
+        launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, as_stream(stream)));
+}
+
+int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const uint16_t *V,
+                int G, int B, int k, float sm_scale, uint16_t *out, uint8_t *depth_out,
+                float *scores_out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                void *stream) {
+    FATHOM_TRY(check_store(st));
+    if (!q || !K || !V || !out || !ws) return FATHOM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 2) ||
+        !aligned(ws, 16) || (scores_out && !aligned(scores_out, 16)) ||
+        (idx_out && !aligned(idx_out, 4)))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_g(G));
+    if (B < 0 || B > FATHOM_D * FATHOM_PLANES) return FATHOM_ERR_BUDGET;
+    const int H = st->n_heads, n = st->n_tokens;
+    FATHOM_TRY(check_topk_k(n, k));
+    if (ws_bytes < step_ws_bytes(H, G, n, k)) return FATHOM_ERR_WORKSPACE;
+    FATHOM_TRY(check_all({st->planes, st->scale, st->zero, st->var, q, K, V, out, depth_out,
+                          scores_out, idx_out, ws}));
+
+    char *w = static_cast<char *>(ws);
+    void *scan_ws = w;
+    w += round256(scan_ws_bytes(H, G));
+    float *scores = scores_out ? scores_out : reinterpret_cast<float *>(w);
+    w += round256((size_t)H * G * n * sizeof(float));
+    void *topk_ws = w;
+    w += round256(topk_ws_bytes(H * G, n, k));
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(w);
+    w += round256((size_t)H * G * k * sizeof(int32_t));
+    uint8_t *depth = depth_out ? depth_out : reinterpret_cast<uint8_t *>(w);
+
+    const hipStream_t s = as_stream(stream);
+    FATHOM_TRY(hip_status(launch_plan(*st, q, G, B, depth, s)));
+    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, scan_ws, s)));
+    FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
+    FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
+    return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
+}
+
+int fathom_stream_read(const void *src, size_t bytes, uint64_t *sink, void *stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(src, 16) ||
+        !aligned(sink, 8))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({src, sink}));
+    return hip_status(launch_stream_read(src, bytes, sink, as_stream(stream)));
+}
+
+int fathom_host_alloc(size_t bytes, int flags, void **ptr) {
+    if (!ptr || bytes == 0 || (flags != 0 && flags != 1)) return FATHOM_ERR_INVALID_ARG;
+    *ptr = nullptr;
+    const unsigned f = flags == 1 ? (hipHostMallocMapped | hipHostMallocNonCoherent)
+                                  : (hipHostMallocMapped | hipHostMallocCoherent);
+    return hip_status(hipHostMalloc(ptr, bytes, f));
+}
+
+int fathom_host_free(void *ptr) {
+    if (!ptr) return FATHOM_ERR_INVALID_ARG;
+    return hip_status(hipHostFree(ptr));
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// Exact attention over the winners' bf16 K/V rows (blog, "The first fix": compute
+// attention over just those k tokens; reading the values for k tokens).
+//
+// One workgroup per (head, query).  A wave works on 8 winner rows at once, 8 lanes per
+// row, 16 channels (32 bytes of K and of V) per lane; each of the 32 row slots of the
+// workgroup keeps an online softmax (running max, running sum, 128-wide output), and
+// the slots are merged through LDS at the end.  Rows are gathered straight from HBM or
+// from pinned host memory; the gather is memory-bound, so there is no matrix-core use.
+#include "common.h"
+
+namespace fathom {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kSlots = kAttnThreads / 8;  // 32 rows in flight per workgroup
+
+__device__ __forceinline__ void unpack8(const uint4 u, float *f) {
+    f[0] = bf16_bits_to_float(u.x & 0xFFFFu);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = bf16_bits_to_float(u.y & 0xFFFFu);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    f[4] = bf16_bits_to_float(u.z & 0xFFFFu);
+    f[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    f[6] = bf16_bits_to_float(u.w & 0xFFFFu);
+    f[7] = __uint_as_float(u.w & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
+    const float *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
+    float sm_scale, uint16_t *__restrict__ out) {
+    __shared__ float so[kSlots][kD + 1];
+    __shared__ float smax[kSlots], ssum[kSlots];
+    const int hg = blockIdx.x, h = hg / G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = wave * 8 + (lane >> 3), sub = lane & 7;
+
+    float qv[16];
+    {
+        const float4 *qp = reinterpret_cast<const float4 *>(q + (size_t)hg * kD + sub * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 t = qp[i];
+            qv[4 * i] = t.x;
+            qv[4 * i + 1] = t.y;
+            qv[4 * i + 2] = t.z;
+            qv[4 * i + 3] = t.w;
+        }
+    }
+    float m = -INFINITY, l = 0.0f, o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = 0.0f;
+
+    const int32_t *ix = idx + (size_t)hg * k;
+    const uint16_t *Kh = K + (size_t)h * n * kD + sub * 16;
+    const uint16_t *Vh = V + (size_t)h * n * kD + sub * 16;
+    for (int r = slot; r < k; r += kSlots) {
+        const int row = ix[r];
+        if ((unsigned)row >= (unsigned)n) continue;  // out-of-range index: skipped
+        const uint4 *kp = reinterpret_cast<const uint4 *>(Kh + (size_t)row * kD);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(Vh + (size_t)row * kD);
+        const uint4 ka = kp[0], kb = kp[1], va = vp[0], vb = vp[1];
+        float kf[16], vf[16];
+        unpack8(ka, kf);
+        unpack8(kb, kf + 8);
+        unpack8(va, vf);
+        unpack8(vb, vf + 8);
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], kf[i], dot);
+        dot += __shfl_xor(dot, 1, 64);
+        dot += __shfl_xor(dot, 2, 64);
+        dot += __shfl_xor(dot, 4, 64);
+        const float s = dot * sm_scale;
+        const float mn = fmaxf(m, s);
+        const float a = expf(m - mn);  // 0 while m is still -inf
+        const float b = expf(s - mn);
+        l = l * a + b;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] = o[i] * a + b * vf[i];
+        m = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) so[slot][sub * 16 + i] = o[i];
+    if (sub == 0) {
+        smax[slot] = m;
+        ssum[slot] = l;
+    }
+    __syncthreads();
+    if (tid < kD) {
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < kSlots; ++s2) M = fmaxf(M, smax[s2]);
+        float L = 0.0f, O = 0.0f;
+        for (int s2 = 0; s2 < kSlots; ++s2) {
+            const float f = smax[s2] == -INFINITY ? 0.0f : expf(smax[s2] - M);
+            L += ssum[s2] * f;
+            O += so[s2][tid] * f;
+        }
+        const float res = L > 0.0f ? O / L : 0.0f;
+        out[(size_t)hg * kD + tid] = float_to_bf16_bits(res);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src,
+                                                     size_t nvec, uint64_t *__restrict__ sink) {
+    uint32_t a = 0, b = 0, c = 0, d = 0;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nvec;
+         i += (size_t)gridDim.x * 256) {
+        const uint4 v = src[i];
+        a ^= v.x;
+        b ^= v.y;
+        c ^= v.z;
+        d ^= v.w;
+    }
+    const uint32_t x = a ^ b ^ c ^ d;
+    if (x == 0x9E3779B9u) sink[0] = ((uint64_t)a << 32) | b;  // keeps the loads live
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
+                              int G, int n, const int32_t *idx, int k, float sm_scale,
+                              uint16_t *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_sparse_attn, dim3(H * G), dim3(kAttnThreads), 0, s, q, K, V, G, n,
+                       idx, k, sm_scale, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void *src, size_t bytes, uint64_t *sink,
+                              hipStream_t s) {
+    const size_t nvec = bytes / 16;
+    const int grid = (int)std::min<size_t>((nvec + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_stream_read, dim3(std::max(grid, 1)), dim3(256), 0, s,
+                       static_cast<const uint4 *>(src), nvec, sink);
+    return hipGetLastError();
+}
+
+}  // namespace fathom

@@ -1,0 +1,219 @@
+/*
+ * fathom.h -- C-ABI of libfathom.so, the MI355X (gfx950) Fathom bit-plane key scan.
+ *
+ * The method (sources: the author's blog post on vivekkalyanarangan.hashnode.dev, by
+ * section heading; the Glonce summary "Fathom speeds long-context KV cache decoding
+ * 1.67x with per-query reads"; the Rootconf proposal "Decoding at a million tokens when
+ * the KV cache lives in host memory"):
+ *   score every cached key cheaply, take the top k, attend exactly over those k
+ *   (blog, "The first fix: stop attending to everything"); the cheap scores come from a
+ *   4-bit per-channel copy of K stored channel-major as bit planes, most significant
+ *   plane first, so that a prefix of t planes is that channel's t-bit quantizer (blog,
+ *   "Bit planes: how a partial read becomes a valid read"); each query spends a budget
+ *   of B planes over the channels by reverse water-filling on the importance
+ *   var_c * q_c^2 (blog, "How each query picks its own depth"; Glonce).
+ *
+ * Conventions for every call below.
+ *   - Status: every call returns FATHOM_OK (0) or one of the FATHOM_ERR_* codes.
+ *     Argument errors are found on the host before anything is enqueued; then nothing
+ *     is enqueued.  A failed launch returns FATHOM_ERR_HIP and the HIP error code is
+ *     available from fathom_last_hip_error() on the calling thread.
+ *   - Execution: every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     default stream) and returns once its kernels are enqueued.  No call synchronizes,
+ *     allocates device memory, prints, or keeps a pointer after it returns.
+ *   - Memory: the caller owns every buffer, including the workspace `ws`.  Pointers are
+ *     device-visible addresses: HBM, or pinned host memory the GPU can read (for the
+ *     store's planes and the K/V rows, which may live in host memory).  A pointer the
+ *     GPU cannot access is rejected with FATHOM_ERR_NOT_MAPPED.  Large buffers (keys,
+ *     planes, scores, K, V, ws) must be 16-byte aligned; everything else 4-byte aligned
+ *     (depth: 1-byte).
+ *   - Shapes: H = (layer, KV head) pairs in the call, G = queries per KV head (1..8),
+ *     d = channels per head (must be 128), n = tokens, B = planes per head (0..4d),
+ *     k = winners per query.  All arrays are dense row-major in the order given.
+ *   - Thread safety: calls may be made from several threads; the library has no state
+ *     besides the per-thread last HIP error.
+ */
+#ifndef FATHOM_H
+#define FATHOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FATHOM_VERSION 100 /* 1.0.0 */
+
+enum fathom_status {
+    FATHOM_OK = 0,
+    FATHOM_ERR_INVALID_ARG = 1, /* null pointer, bad size or misaligned buffer */
+    FATHOM_ERR_BUDGET = 2,      /* B outside [0, 4d] */
+    FATHOM_ERR_UNSUPPORTED = 3, /* d != 128, G > 8, or k beyond the top-k limits */
+    FATHOM_ERR_WORKSPACE = 4,   /* ws too small (see fathom_workspace_size) */
+    FATHOM_ERR_NOT_MAPPED = 5,  /* a pointer the GPU cannot read or write */
+    FATHOM_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+};
+
+#define FATHOM_D 128          /* channels per head this build supports */
+#define FATHOM_PLANES 4       /* 4-bit codes: planes 0 (MSB) .. 3 (LSB) */
+#define FATHOM_MAX_G 8        /* queries per KV head */
+#define FATHOM_TOPK_CHUNK 32768 /* elements one top-k workgroup ranks at once */
+
+/*
+ * The bit-plane store of H heads (blog, "Bit planes"; Glonce: "stored channel-major as
+ * bit planes").  A plain descriptor of caller-owned buffers:
+ *   planes [H][d][4][word_stride] uint32: plane j of channel c of head h; plane 0 holds
+ *          the most significant bit of every 4-bit code.  Word w holds tokens
+ *          32w .. 32w+31, token 32w+i at bit i (least significant bit first).  Bits of
+ *          tokens >= n_tokens are zero.  HBM or pinned host memory.
+ *   scale, zero, var [H][d] fp32: per channel s, z and the variance of the dequantized
+ *          channel z + s*code (see fathom_quantize_store).  Device memory.
+ */
+typedef struct fathom_store {
+    int32_t n_heads;     /* H */
+    int32_t n_tokens;    /* n, >= 1 */
+    int32_t d;           /* channels, must be FATHOM_D */
+    int32_t word_stride; /* uint32 words per plane row, >= ceil(n/32) */
+    uint32_t *planes;
+    float *scale;
+    float *zero;
+    float *var;
+} fathom_store;
+
+/* Operations for fathom_workspace_size. */
+enum fathom_op {
+    FATHOM_OP_QUANTIZE = 0, /* fathom_quantize_store: uses H, n */
+    FATHOM_OP_SCAN = 1,     /* fathom_scan / fathom_scan_prepare(d): uses H, G */
+    FATHOM_OP_TOPK = 2,     /* fathom_topk: uses H as the row count R, n, k */
+    FATHOM_OP_STEP = 3      /* fathom_step: uses H, G, n, k */
+};
+
+/* Bytes of workspace `op` needs for the given sizes (0 is possible).  Status only. */
+int fathom_workspace_size(int op, int H, int G, int n, int k, size_t *bytes);
+
+/* Text for a status code (static storage). */
+const char *fathom_status_string(int status);
+
+/* The HIP error code behind the last FATHOM_ERR_HIP on the calling thread (0 if none). */
+int fathom_last_hip_error(void);
+
+/* FATHOM_VERSION of the built library. */
+int fathom_version(void);
+
+/*
+ * Build the store from fp32 keys (blog, "How to read fewer bits per key": 4-bit
+ * storage; "Bit planes": the plane layout; Glonce: 4-bit per-channel K cache).
+ *   keys [H][n][d] fp32, device-visible, finite.
+ * Per channel over all n tokens: s = (max - min)/15 and z = min, each one fp32
+ * operation; code = clamp(floor((x - z)/s + 0.5), 0, 15) with every step an fp32
+ * operation (a constant channel, s == 0, gets code 0).  The codes are packed into
+ * st->planes (words from ceil(n/32) to word_stride are zeroed), and
+ * var = s^2 (n*S2 - S1^2) / n^2 from the exact integer sums S1 = sum code and
+ * S2 = sum code^2, evaluated in fp64 and rounded once to fp32.
+ * st->n_heads == H and st->n_tokens == n are required.  ws: FATHOM_OP_QUANTIZE bytes.
+ */
+int fathom_quantize_store(const float *keys, int H, int n, int d, const fathom_store *st,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Per-head plan (blog, "How each query picks its own depth": reverse water-filling).
+ *   q [H][G][d] fp32: the G queries that share each KV head.
+ *   depth [H][d] uint8 out: planes read per channel, 0..4, summing to B per head.
+ * Importance w_c = var_c * sum_g q_gc^2 in fp64 (each square exact, sum over g in
+ * ascending order, then one product).  The B planes go, one at a time, to the channel
+ * with the largest w_c * 4^-t_c among channels with t_c < 4 (each plane cuts a
+ * channel's error by four); equal values go to the lower channel index.  Exact.
+ */
+int fathom_plan(const fathom_store *st, const float *q, int G, int B, uint8_t *depth,
+                void *stream);
+
+/*
+ * A query-independent comparator plan: depth 4 on the `n_channels` channels with the
+ * largest var (equal var: lower channel index), 0 elsewhere, i.e. 4*n_channels planes
+ * per head -- the fixed-depth index of the size the blog's "The catch" section gives
+ * for the 136-bit scans (n_channels = 34).  0 <= n_channels <= d.
+ */
+int fathom_plan_fixed(const fathom_store *st, int n_channels, uint8_t *depth,
+                      void *stream);
+
+/*
+ * Approximate scores of every key from the planes each channel reads (blog, "The first
+ * fix": score every key; "Bit planes": a t-plane prefix is the t-bit quantizer).
+ *   q [H][G][d] fp32; depth [H][d] (any values 0..4, e.g. from fathom_plan or
+ *   fathom_plan_fixed); scores [H][G][n] fp32 out.
+ * For token i and query g:  score = sum_c q_gc * (z_c + s_c * m_ic), where m_ic is the
+ * middle of the 4-bit codes the t_c planes read allow: p * 2^(4-t) + (2^(4-t) - 1)/2
+ * with p the t-plane prefix (t = 0 reads nothing: m = 7.5).  fp32 result; the order of
+ * the fp32 additions is the library's (it sums plane groups through lookup tables).
+ * ws: FATHOM_OP_SCAN bytes.  fathom_scan = fathom_scan_prepare + fathom_scan_prepared.
+ */
+int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/* First half of fathom_scan: per-head plane list, constant term and lookup tables
+ * into ws (one small kernel). */
+int fathom_scan_prepare(const fathom_store *st, const float *q, int G,
+                        const uint8_t *depth, void *ws, size_t ws_bytes, void *stream);
+
+/* Second half of fathom_scan: the plane-reading kernel, using the tables that
+ * fathom_scan_prepare left in ws for the same store and G. */
+int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/*
+ * Top k of each row (blog, "The first fix": take the top k).
+ *   scores [R][n] fp32, finite; idx [R][k] int32 out, ascending by token index.
+ * Order: score descending, then token index ascending (equal scores go to the lower
+ * index; -0 equals +0).  1 <= k <= n; when n > FATHOM_TOPK_CHUNK, k must be at most
+ * FATHOM_TOPK_CHUNK/2 (else FATHOM_ERR_UNSUPPORTED).  ws: FATHOM_OP_TOPK bytes.
+ */
+int fathom_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
+                size_t ws_bytes, void *stream);
+
+/*
+ * Exact attention over the winners (blog, "The first fix": attention over just those k
+ * tokens, reading the values for k tokens).
+ *   q [H][G][d] fp32; K, V [H][n][d] bf16 bits (HBM or pinned host); idx [H][G][k]
+ *   int32 in [0, n); out [H][G][d] bf16 bits.
+ * l_r = sm_scale * (q_g . K[idx_r]), p = softmax(l), out = sum_r p_r V[idx_r];
+ * fp32 arithmetic, output rounded to nearest-even bf16.  Rows are not deduplicated.
+ */
+int fathom_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H, int G,
+                       int n, int d, const int32_t *idx, int k, float sm_scale,
+                       uint16_t *out, void *stream);
+
+/*
+ * One decode step for the H heads of the store: plan -> scan -> top-k -> attention,
+ * all enqueued on `stream` with no host synchronization (blog, "That is the whole
+ * method"; Rootconf: sync-free accounting).  Same arguments as the calls above.
+ * depth_out [H][d], scores_out [H][G][n] and idx_out [H][G][k] are optional (NULL: the
+ * intermediate lives in ws).  ws: FATHOM_OP_STEP bytes.
+ */
+int fathom_step(const fathom_store *st, const float *q, const uint16_t *K,
+                const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                size_t ws_bytes, void *stream);
+
+/*
+ * Measurement helper for the roofline denominators (blog, "One measurement worth
+ * carrying around": contiguous reads from pinned host memory): streams `bytes`
+ * (multiple of 16) from the device-visible address `src` (HBM or pinned host) with
+ * coalesced 16-byte loads and writes a checksum to *sink (device memory, 16 bytes).
+ */
+int fathom_stream_read(const void *src, size_t bytes, uint64_t *sink, void *stream);
+
+/*
+ * Pinned host memory the GPU can read directly (hipHostMalloc).  flags: 0 = coherent
+ * (fine-grained), 1 = non-coherent (coarse-grained).  fathom_host_free releases it.
+ * These are the only calls that allocate; they exist so that callers can place the
+ * store or the K/V rows in host memory.
+ */
+int fathom_host_alloc(size_t bytes, int flags, void **ptr);
+int fathom_host_free(void *ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATHOM_H */

@@ -56,6 +56,7 @@ def _load():
         "oracle_pack_planes_batch": (None, [P, I, I, I, I, P]),
         "oracle_var_batch": (None, [P, P, I, I, I, P]),
         "oracle_plan_batch": (I, [P, P, I, I, I, I, P]),
+        "oracle_plan_fixed": (I, [P, I, I, P]),
         "oracle_scores_batch": (None, [P, P, P, P, P, I, I, I, I, P]),
         "oracle_topk_batch": (I, [P, I, I, I, P]),
         "oracle_attention_batch": (None, [P, P, P, I, I, I, I, P, I, D, P]),
@@ -66,6 +67,7 @@ def _load():
         "oracle_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "oracle_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
         "oracle_f32_to_bf16_array": (None, [P, ctypes.c_size_t, P]),
+        "oracle_threads": (I, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -82,6 +84,11 @@ def _c(a, dtype):
 
 def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """OpenMP threads the batched oracle calls use."""
+    return int(_load().oracle_threads())
 
 
 def n_words(n: int) -> int:
@@ -159,6 +166,21 @@ def plan(q, var, B: int):
     rc = _load().oracle_plan_batch(_p(qq), _p(vv), H, G, d, int(B), _p(depth))
     if rc != 0:
         raise ValueError(f"oracle plan rejected B={B} for d={d}")
+    return depth[0] if squeeze else depth
+
+
+def plan_fixed(var, n_channels: int):
+    """Comparator plan: depth 4 on the n_channels largest-variance channels [H][d]."""
+    vv = _c(var, np.float32)
+    squeeze = vv.ndim == 1
+    if squeeze:
+        vv = vv[None]
+    H, d = vv.shape
+    depth = np.empty((H, d), np.uint8)
+    for h in range(H):
+        rc = _load().oracle_plan_fixed(_p(vv[h]), d, int(n_channels), _p(depth[h]))
+        if rc != 0:
+            raise ValueError(f"oracle fixed plan rejected n_channels={n_channels}")
     return depth[0] if squeeze else depth
 
 

@@ -20,11 +20,15 @@
  * _batch forms only loop the per-head function over heads (OpenMP over heads).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_PLANES 4 /* 4-bit codes -> 4 bit planes (blog, "Bit planes") */
+
+/* Threads the _batch forms use (OpenMP's default team size). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------ */
 /* Quantize (blog, "How to read fewer bits per key": 4-bit storage; Glonce: "4-bit  */
@@ -163,6 +167,24 @@ int oracle_plan(const float *q, const float *var, int G, int d, int B, uint8_t *
         depth[best] += 1;
     }
     free(w);
+    return 0;
+}
+
+/* Query-independent comparator of the size the blog's "The catch" section gives for  */
+/* the fixed 136-bit scans: all four planes of the n_channels channels with the      */
+/* largest variance (equal variances: lower channel index first), nothing elsewhere. */
+int oracle_plan_fixed(const float *var, int d, int n_channels, uint8_t *depth)
+{
+    if (n_channels < 0 || n_channels > d) return -1;
+    for (int c = 0; c < d; ++c) depth[c] = 0;
+    for (int taken = 0; taken < n_channels; ++taken) {
+        int best = -1;
+        for (int c = 0; c < d; ++c) {
+            if (depth[c] != 0) continue;
+            if (best < 0 || var[c] > var[best]) best = c;
+        }
+        depth[best] = ORACLE_PLANES;
+    }
     return 0;
 }
 

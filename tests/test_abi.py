@@ -1,0 +1,144 @@
+"""CPU tests of the C-ABI: the library loads, exports every call include/fathom.h
+declares, and rejects bad arguments on the host (no GPU needed: these paths return
+before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_plane_kv_amd import fathom as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fathom.h")
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fathom_\w+)\s*\(", text)))
+
+
+def test_every_declared_call_is_exported():
+    L = F.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    # and the binding wraps exactly the declared calls
+    assert sorted(F.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    L = F.lib()
+    assert L.fathom_version() == 100
+    for s in range(7):
+        assert F.status_string(s)
+    assert F.status_string(99) == "unknown status"
+    assert L.fathom_last_hip_error() == 0
+
+
+def _st(H=2, n=100, d=128, stride=None, planes=FAKE):
+    return F.fathom_store(H, n, d, (n + 31) // 32 if stride is None else stride, planes,
+                          FAKE, FAKE, FAKE)
+
+
+def test_store_checks():
+    L = F.lib()
+    r = lambda st: L.fathom_plan(ctypes.byref(st) if st is not None else None, FAKE, 1, 8,
+                                 FAKE, None)
+    assert r(None) == F.ERR_INVALID_ARG
+    assert r(_st(d=64)) == F.ERR_UNSUPPORTED
+    assert r(_st(n=0)) == F.ERR_INVALID_ARG
+    assert r(_st(H=0)) == F.ERR_INVALID_ARG
+    assert r(_st(stride=3)) == F.ERR_INVALID_ARG          # < ceil(100/32)
+    assert r(_st(planes=None)) == F.ERR_INVALID_ARG
+    assert r(_st(planes=FAKE + 4)) == F.ERR_INVALID_ARG   # planes must be 16-aligned
+
+
+def test_plan_checks():
+    L = F.lib()
+    st = _st()
+    assert L.fathom_plan(ctypes.byref(st), FAKE, 1, 513, FAKE, None) == F.ERR_BUDGET
+    assert L.fathom_plan(ctypes.byref(st), FAKE, 1, -1, FAKE, None) == F.ERR_BUDGET
+    assert L.fathom_plan(ctypes.byref(st), FAKE, 9, 8, FAKE, None) == F.ERR_UNSUPPORTED
+    assert L.fathom_plan(ctypes.byref(st), FAKE, 0, 8, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_plan(ctypes.byref(st), None, 1, 8, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_plan(ctypes.byref(st), FAKE, 1, 8, None, None) == F.ERR_INVALID_ARG
+    assert L.fathom_plan_fixed(ctypes.byref(st), 129, FAKE, None) == F.ERR_BUDGET
+    assert L.fathom_plan_fixed(ctypes.byref(st), 34, None, None) == F.ERR_INVALID_ARG
+
+
+def test_scan_checks():
+    L = F.lib()
+    st = _st()
+    need = F.workspace_size(F.OP_SCAN, 2, 4)
+    assert L.fathom_scan(ctypes.byref(st), FAKE, 4, FAKE, FAKE, FAKE, need - 1,
+                         None) == F.ERR_WORKSPACE
+    assert L.fathom_scan(ctypes.byref(st), FAKE, 4, FAKE, FAKE, None, need,
+                         None) == F.ERR_INVALID_ARG
+    assert L.fathom_scan(ctypes.byref(st), FAKE, 4, FAKE, FAKE + 4, FAKE, need,
+                         None) == F.ERR_INVALID_ARG
+    assert L.fathom_scan_prepared(ctypes.byref(st), 9, FAKE, FAKE, need,
+                                  None) == F.ERR_UNSUPPORTED
+    assert L.fathom_scan_prepare(ctypes.byref(st), None, 4, FAKE, FAKE, need,
+                                 None) == F.ERR_INVALID_ARG
+
+
+def test_topk_checks():
+    L = F.lib()
+    assert L.fathom_topk(FAKE, 4, 100, 0, FAKE, None, 0, None) == F.ERR_INVALID_ARG
+    assert L.fathom_topk(FAKE, 4, 100, 101, FAKE, None, 0, None) == F.ERR_INVALID_ARG
+    assert L.fathom_topk(FAKE, 0, 100, 10, FAKE, None, 0, None) == F.ERR_INVALID_ARG
+    assert L.fathom_topk(FAKE, 4, 40000, 16385, FAKE, FAKE, 1 << 30,
+                         None) == F.ERR_UNSUPPORTED
+    need = F.workspace_size(F.OP_TOPK, 4, 1, 40000, 512)
+    assert need > 0
+    assert L.fathom_topk(FAKE, 4, 40000, 512, FAKE, FAKE, need - 1, None) == F.ERR_WORKSPACE
+    assert L.fathom_topk(FAKE, 4, 40000, 512, FAKE, None, need, None) == F.ERR_INVALID_ARG
+
+
+def test_attn_and_step_checks():
+    L = F.lib()
+    assert L.fathom_sparse_attn(FAKE, FAKE, FAKE, 1, 1, 100, 64, FAKE, 5, 0.1, FAKE,
+                                None) == F.ERR_UNSUPPORTED
+    assert L.fathom_sparse_attn(FAKE, FAKE, FAKE, 1, 1, 100, 128, FAKE, 101, 0.1, FAKE,
+                                None) == F.ERR_INVALID_ARG
+    assert L.fathom_sparse_attn(FAKE, FAKE + 2, FAKE, 1, 1, 100, 128, FAKE, 5, 0.1, FAKE,
+                                None) == F.ERR_INVALID_ARG
+    st = _st()
+    need = F.workspace_size(F.OP_STEP, 2, 4, 100, 10)
+    args = lambda B, k, ws_bytes: (ctypes.byref(st), FAKE, FAKE, FAKE, 4, B, k, 0.1, FAKE,
+                                   None, None, None, FAKE, ws_bytes, None)
+    assert L.fathom_step(*args(92, 10, need - 1)) == F.ERR_WORKSPACE
+    assert L.fathom_step(*args(600, 10, need)) == F.ERR_BUDGET
+    assert L.fathom_step(*args(92, 101, need)) == F.ERR_INVALID_ARG
+
+
+def test_stream_read_and_host_alloc_checks():
+    L = F.lib()
+    assert L.fathom_stream_read(FAKE, 15, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_stream_read(None, 16, FAKE, None) == F.ERR_INVALID_ARG
+    p = ctypes.c_void_p()
+    assert L.fathom_host_alloc(0, 0, ctypes.byref(p)) == F.ERR_INVALID_ARG
+    assert L.fathom_host_alloc(16, 2, ctypes.byref(p)) == F.ERR_INVALID_ARG
+    assert L.fathom_host_free(None) == F.ERR_INVALID_ARG
+
+
+def test_workspace_formulas():
+    # scan: 2 KiB meta + 64 groups x 256 entries x G padded to 1/2/4/8 floats, per head
+    for G, gp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
+        assert F.workspace_size(F.OP_SCAN, 3, G) == 3 * (2048 + 64 * 256 * gp * 4)
+    # top-k: rows that fit one chunk need nothing
+    assert F.workspace_size(F.OP_TOPK, 1152, 1, 32768, 512) == 0
+    # 1M tokens: 32 chunks x 512 candidates x (4 + 4) bytes per row, one level
+    assert F.workspace_size(F.OP_TOPK, 32, 1, 1 << 20, 512) == 32 * 32 * 512 * 8
+    # quantize: min/max partials + integer sums
+    q = F.workspace_size(F.OP_QUANTIZE, 2, 1, 4096, 1)
+    assert q == 2 * 2 * 2 * 128 * 4 + 2 * 128 * 16
+    with pytest.raises(F.FathomError):
+        F.workspace_size(F.OP_STEP, 8, 9, 100, 10)
+    with pytest.raises(F.FathomError):
+        F.workspace_size(7, 8, 1, 100, 10)

@@ -137,3 +137,15 @@ def test_importance_sums_queries_of_one_kv_head():
     var = np.array([0.5, 2.0], np.float32)
     assert oracle.importance(q, var, 0) == (1 + 9) * 0.5
     assert oracle.importance(q, var, 1) == (4 + 1) * 2.0
+
+
+@pytest.mark.parametrize("F", [0, 1, 34, 127, 128])
+def test_fixed_plan_matches_stable_argsort(F):
+    rng = np.random.default_rng(F)
+    var = rng.choice(np.array([0, 0.5, 1, 2, 3], np.float32), 128)   # many ties
+    depth = oracle.plan_fixed(var, F)
+    order = np.argsort(-var.astype(np.float64), kind="stable")    # ties: lower index
+    ref = np.zeros(128, np.uint8)
+    ref[order[:F]] = 4
+    assert (depth == ref).all()
+    assert int(depth.sum()) == 4 * F
