@@ -19,16 +19,17 @@ constexpr int kLutEntries = 1 << kGroupBits;  // 256
 // ---------------------------------------------------------------------------------
 // Scan workspace, per head:  a meta block (plane list, constant term, counts) and the
 // lookup tables.  meta: int32 n_planes, int32 n_groups, int32 pad[2], float C[8],
-// uint16 plane[512] (c*4 + j, channels ascending, planes ascending within a channel).
+// uint32 plane[512] (c*4 + j, channels ascending, planes ascending within a channel;
+// entries past n_planes repeat the group's first plane so reads stay in bounds).
 // lut: [kMaxGroups][256][gp] fp32, gp = G padded to 1, 2, 4 or 8.
 // ---------------------------------------------------------------------------------
-constexpr size_t kMetaBytes = 2048;
+constexpr size_t kMetaBytes = 4096;
 struct ScanMeta {
     int32_t n_planes;
     int32_t n_groups;
     int32_t pad[2];
     float C[FATHOM_MAX_G];
-    uint16_t plane[kMaxPlanesPerHead];
+    uint32_t plane[kMaxPlanesPerHead];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
 

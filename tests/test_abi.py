@@ -128,9 +128,9 @@ def test_stream_read_and_host_alloc_checks():
 
 
 def test_workspace_formulas():
-    # scan: 2 KiB meta + 64 groups x 256 entries x G padded to 1/2/4/8 floats, per head
+    # scan: 4 KiB meta + 64 groups x 256 entries x G padded to 1/2/4/8 floats, per head
     for G, gp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
-        assert F.workspace_size(F.OP_SCAN, 3, G) == 3 * (2048 + 64 * 256 * gp * 4)
+        assert F.workspace_size(F.OP_SCAN, 3, G) == 3 * (4096 + 64 * 256 * gp * 4)
     # top-k: rows that fit one chunk need nothing
     assert F.workspace_size(F.OP_TOPK, 1152, 1, 32768, 512) == 0
     # 1M tokens: 32 chunks x 512 candidates x (4 + 4) bytes per row, one level
