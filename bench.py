@@ -43,6 +43,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--kernel", default=None,
+                    choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136"],
+                    help="set up the workload, time only this kernel (for profiler runs)")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="with --kernel: also run a 1 GiB streaming read and a 256 MiB "
+                         "copy, whose byte counts scale the profiler's HBM counters")
     return ap.parse_args()
 
 
@@ -96,6 +103,23 @@ def main():
     out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s: H={H} G={G} n={n} B={B} k={k}")
+
+    if args.kernel:
+        kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
+                            stream, reps=args.reps, only=args.kernel)
+        if args.calibrate:
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            sink = torch.zeros(2, dtype=torch.int64, device=dev)
+            a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                F.fathom_stream_read(flush, flush.numel(), sink)
+                b.copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps({"kernel": args.kernel, "reps": args.reps,
+                          "ms": round(kern[args.kernel + "_ms"], 4),
+                          "config": cfg.name, "budget_bits": B}), flush=True)
+        return
 
     # ---------------- bit-exact checks before timing ----------------
     F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, depth_out=depth, scores_out=scores,
@@ -196,7 +220,8 @@ def check_sample(st, q_np, K, V, depth, scores, idx, out, sample_keys, B, k, sm)
     return res
 
 
-def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream, reps):
+def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream, reps,
+                 only=None):
     """Mean duration of each kernel of the step, timed with events on the launch stream,
     with a 1 GiB streaming read between launches so that every launch starts with cold
     caches (the 256 MB last-level cache would otherwise hold part of the planes)."""
@@ -205,7 +230,10 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(2, dtype=torch.int64, device=dev)
     scan_ws = F.scan_workspace(st, G, dev)
+    F.fathom_plan(st, q, B, depth=depth)
     F.fathom_scan_prepare(st, q, depth, scan_ws)
+    F.fathom_scan_prepared(st, G, scores, scan_ws)
+    F.fathom_topk(scores, k, idx=idx)
     calls = {
         "plan_ms": lambda: F.fathom_plan(st, q, B, depth=depth),
         "scan_prepare_ms": lambda: F.fathom_scan_prepare(st, q, depth, scan_ws),
@@ -214,8 +242,8 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
         "attn_ms": lambda: F.fathom_sparse_attn(q, K, V, idx, sm, out=out),
     }
     res = {}
-    for name, fn in calls.items():
-        fn()
+
+    def timed(fn):
         tot = 0.0
         for _ in range(reps):
             F.fathom_stream_read(flush, flush.numel(), sink)
@@ -225,20 +253,24 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
             b.record(stream)
             b.synchronize()
             tot += a.elapsed_time(b)
-        res[name] = tot / reps
+        return tot / reps
+
+    if only == "scan_fixed136":
+        fixed = F.fathom_plan_fixed(st, 34)
+        F.fathom_scan_prepare(st, q, fixed, scan_ws)
+        return {"scan_fixed136_ms": timed(lambda: F.fathom_scan_prepared(st, G, scores,
+                                                                          scan_ws))}
+    if only is not None:
+        fn = calls[only + "_ms"]
+        fn()
+        return {only + "_ms": timed(fn)}
+    for name, fn in calls.items():
+        fn()
+        res[name] = timed(fn)
     # the 136-bit fixed-depth comparator through the same store and kernel
     fixed = F.fathom_plan_fixed(st, 34)
     F.fathom_scan_prepare(st, q, fixed, scan_ws)
-    tot = 0.0
-    for _ in range(reps):
-        F.fathom_stream_read(flush, flush.numel(), sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        F.fathom_scan_prepared(st, G, scores, scan_ws)
-        b.record(stream)
-        b.synchronize()
-        tot += a.elapsed_time(b)
-    res["scan_fixed136_ms"] = tot / reps
+    res["scan_fixed136_ms"] = timed(lambda: F.fathom_scan_prepared(st, G, scores, scan_ws))
     # HBM streaming-read rate of this device (1 GiB, warm launch) for context
     F.fathom_stream_read(flush, flush.numel(), sink)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

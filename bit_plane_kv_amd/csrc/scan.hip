@@ -131,143 +131,94 @@ __device__ __forceinline__ void transpose8x8(uint32_t &lo, uint32_t &hi) {
     lo = lo ^ (t << 4);
 }
 
-constexpr int kScanThreads = 256;
-constexpr int kTokensPerLane = 16;                                     // half a word
-constexpr int kTileWords = kScanThreads * kTokensPerLane / 32;         // 128 words
-constexpr int kLdsBudget = 48 * 1024;                                  // tables per batch
+// Shape of the main kernel.  A workgroup of 8 waves scores a tile of 128 words (4096
+// tokens) of one head.  In a wave, the 4 lanes of a quad share one 32-token word: lane
+// (4w + s) loads planes s and s+4 of word w, a 4x4 byte transpose across the quad gives
+// every lane byte s (8 tokens) of all 8 planes of the group, and lane (4w + s) scores
+// tokens 8s .. 8s+7 of the word.  Each lane thus issues 2 loads per group of 8 planes.
+constexpr int kScanThreads = 512;
+constexpr int kWordsPerWave = 16;
+constexpr int kTileWords = (kScanThreads / 64) * kWordsPerWave;  // 128 words
+constexpr int kTokensPerLane = 8;
+constexpr int kInflight = 4;   // table reads issued before their adds
+constexpr int kPrefetch = 4;   // groups of plane words in flight per lane
+constexpr int kLdsBudget = 48 * 1024;  // tables per batch (LDS also stages the scores)
 
-template <int GP>
-struct Lut;
-template <>
-struct Lut<1> {
-    static __device__ __forceinline__ void add(float (&a)[1], const float *p) { a[0] += p[0]; }
-};
-template <>
-struct Lut<2> {
-    static __device__ __forceinline__ void add(float (&a)[2], const float *p) {
-        const float2 v = *reinterpret_cast<const float2 *>(p);
-        a[0] += v.x;
-        a[1] += v.y;
-    }
-};
-template <>
-struct Lut<4> {
-    static __device__ __forceinline__ void add(float (&a)[4], const float *p) {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        a[0] += v.x;
-        a[1] += v.y;
-        a[2] += v.z;
-        a[3] += v.w;
-    }
-};
-template <>
-struct Lut<8> {
-    static __device__ __forceinline__ void add(float (&a)[8], const float *p) {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        const float4 u = *reinterpret_cast<const float4 *>(p + 4);
-        a[0] += v.x;
-        a[1] += v.y;
-        a[2] += v.z;
-        a[3] += v.w;
-        a[4] += u.x;
-        a[5] += u.y;
-        a[6] += u.z;
-        a[7] += u.w;
-    }
-};
-
-// Lane layout: lane L of wave w reads word (tile*128 + w*32 + L%32) of every plane in a
-// group and scores that word's tokens 16*(L/32) .. 16*(L/32)+15; both halves of a word
-// read the same address (one 128-byte line per wave per plane).
-// Loads one group's 8 plane words for this lane's word.  ids are uniform (SGPRs).
-__device__ __forceinline__ void load_group(const uint32_t *__restrict__ hp,
-                                           const uint32_t (&ids)[kGroupBits],
-                                           int word_stride, int gwc,
-                                           uint32_t (&w)[kGroupBits]) {
-#pragma unroll
-    for (int r = 0; r < kGroupBits; ++r)
-        w[r] = hp[(size_t)ids[r] * (size_t)word_stride + gwc];
+// Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
+// result is byte s of M_p (p = 0..3).  Two butterfly stages, each one DPP move of the
+// partner's word and one byte permute.
+__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t m, int s) {
+    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+    const uint32_t a = __builtin_amdgcn_perm(p, m, s < 2 ? 0x05040100u : 0x03020706u);
+    const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);
+    return __builtin_amdgcn_perm(q, a, (s & 1) ? 0x03070105u : 0x06020400u);
 }
 
-// Uniform read of a group's 8 plane ids from LDS (every lane reads the same address).
-__device__ __forceinline__ void lds_ids(const uint32_t *lids, int gi,
-                                        uint32_t (&ids)[kGroupBits]) {
-    const uint4 a = reinterpret_cast<const uint4 *>(lids)[2 * gi];
-    const uint4 b = reinterpret_cast<const uint4 *>(lids)[2 * gi + 1];
-    ids[0] = __builtin_amdgcn_readfirstlane(a.x);
-    ids[1] = __builtin_amdgcn_readfirstlane(a.y);
-    ids[2] = __builtin_amdgcn_readfirstlane(a.z);
-    ids[3] = __builtin_amdgcn_readfirstlane(a.w);
-    ids[4] = __builtin_amdgcn_readfirstlane(b.x);
-    ids[5] = __builtin_amdgcn_readfirstlane(b.y);
-    ids[6] = __builtin_amdgcn_readfirstlane(b.z);
-    ids[7] = __builtin_amdgcn_readfirstlane(b.w);
-}
-
+// Adds the table entries of tokens m0 .. m0+kInflight-1 (reads first, then adds).
 template <int GP>
-__device__ __forceinline__ void lookup_add(const uint32_t (&x)[4], int m0, const float *lg,
+__device__ __forceinline__ void lookup_add(const uint32_t (&x)[2], int m0, const float *lg,
                                            float (&acc)[kTokensPerLane][GP]) {
-    // 8 table reads in flight, then the adds
-    float e[8][GP];
+    float e[kInflight][GP];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < kInflight; ++m) {
         const uint32_t pat = (x[(m0 + m) >> 2] >> (8 * ((m0 + m) & 3))) & 0xFFu;
         const float *p = lg + pat * GP;
+        if constexpr (GP >= 4) {
 #pragma unroll
-        for (int g = 0; g < GP; g += (GP >= 4 ? 4 : GP)) {
-            if constexpr (GP >= 4) {
+            for (int g = 0; g < GP; g += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(p + g);
                 e[m][g] = v.x;
                 e[m][g + 1] = v.y;
                 e[m][g + 2] = v.z;
                 e[m][g + 3] = v.w;
-            } else if constexpr (GP == 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(p);
-                e[m][0] = v.x;
-                e[m][1] = v.y;
-            } else {
-                e[m][0] = p[0];
             }
+        } else if constexpr (GP == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(p);
+            e[m][0] = v.x;
+            e[m][1] = v.y;
+        } else {
+            e[m][0] = p[0];
         }
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < kInflight; ++m)
 #pragma unroll
         for (int g = 0; g < GP; ++g) acc[m0 + m][g] += e[m][g];
 }
 
+// One group: quad byte transposes give x[0] = byte s of planes 0-3 and x[1] = planes
+// 4-7 (an 8x8 bit block: 8 planes x 8 tokens); the bit transpose turns byte m into
+// token m's 8-plane pattern; then the table lookups.
 template <int GP>
-__device__ __forceinline__ void process_group(const uint32_t (&w)[kGroupBits],
-                                              uint32_t sel_pair, const float *lg,
+__device__ __forceinline__ void process_group(const uint32_t (&w)[2], int s, const float *lg,
                                               float (&acc)[kTokensPerLane][GP]) {
-    const uint32_t t01 = __builtin_amdgcn_perm(w[1], w[0], sel_pair);
-    const uint32_t t23 = __builtin_amdgcn_perm(w[3], w[2], sel_pair);
-    const uint32_t t45 = __builtin_amdgcn_perm(w[5], w[4], sel_pair);
-    const uint32_t t67 = __builtin_amdgcn_perm(w[7], w[6], sel_pair);
-    uint32_t x[4];
-    x[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);  // tokens 0-7: rows 0-3
-    x[1] = __builtin_amdgcn_perm(t67, t45, 0x05040100u);  //             rows 4-7
-    x[2] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);  // tokens 8-15: rows 0-3
-    x[3] = __builtin_amdgcn_perm(t67, t45, 0x07060302u);  //              rows 4-7
+    uint32_t x[2];
+    x[0] = quad_byte_transpose(w[0], s);
+    x[1] = quad_byte_transpose(w[1], s);
     transpose8x8(x[0], x[1]);
-    transpose8x8(x[2], x[3]);
-    lookup_add<GP>(x, 0, lg, acc);
-    lookup_add<GP>(x, 8, lg, acc);
+#pragma unroll
+    for (int m0 = 0; m0 < kTokensPerLane; m0 += kInflight) lookup_add<GP>(x, m0, lg, acc);
 }
 
-// Lane layout: lane L of wave w reads word (tile*128 + w*32 + L%32) of every plane in a
-// group and scores that word's tokens 16*(L/32) .. 16*(L/32)+15; both halves of a word
-// read the same address (one 128-byte line per wave per plane).  The plane words of the
-// next two groups are in flight while a group is transposed and looked up; the plane
-// ids of a batch sit in LDS next to its tables.
+// Issues this lane's two plane-word loads of group gi (row offsets of the batch's planes
+// are staged in LDS, in words).
+__device__ __forceinline__ void issue_group(const uint32_t *lane_base, const uint64_t *lrow,
+                                            int gi, int s, uint32_t (&w)[2]) {
+    const uint64_t r0 = lrow[gi * kGroupBits + s];
+    const uint64_t r1 = lrow[gi * kGroupBits + s + 4];
+    w[0] = lane_base[r0];
+    w[1] = lane_base[r1];
+}
+
 template <int GP>
 __global__ __launch_bounds__(kScanThreads) void k_scan_main(
     const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H,
     int tiles_per_head, const char *__restrict__ ws, float *__restrict__ scores) {
-    extern __shared__ float4 lds_v4[];  // 16-byte aligned: tables, then plane ids
+    extern __shared__ float4 lds_v4[];  // 16-byte aligned: tables, then plane rows
     constexpr int kBatchGroups = kLdsBudget / (kLutEntries * GP * (int)sizeof(float));
     float *lds = reinterpret_cast<float *>(lds_v4);
-    uint32_t *lids = reinterpret_cast<uint32_t *>(lds_v4 + kBatchGroups * kLutEntries * GP / 4);
+    uint64_t *lrow =
+        reinterpret_cast<uint64_t *>(lds_v4 + kBatchGroups * kLutEntries * GP / 4);
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int h = lb / tiles_per_head, tile = lb - h * tiles_per_head;
     const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(ws + (size_t)h * kMetaBytes);
@@ -277,13 +228,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_main(
     // clamped so that any workspace content keeps every read inside this head's data
     const int ngroups = min(max(meta->n_groups, 0), kMaxGroups);
     const uint32_t *pids = meta->plane;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = lane & 3;  // quad position: byte of the word = tokens 8s .. 8s+7
     const int W = (n + 31) >> 5;
-    const int gw = tile * kTileWords + wave * 32 + (lane & 31);
+    const int gw = tile * kTileWords + wave * kWordsPerWave + (lane >> 2);
     const int gwc = min(gw, W - 1);  // lanes past the end re-read the last word
-    const uint32_t *hp = planes + (size_t)h * kMaxPlanesPerHead * word_stride;
-    // byte selectors: pairs (w_a, w_b) -> [a.b(2h), b.b(2h), a.b(2h+1), b.b(2h+1)]
-    const uint32_t sel_pair = half ? 0x07030602u : 0x05010400u;
+    const uint32_t *lane_base = planes + (size_t)h * kMaxPlanesPerHead * word_stride + gwc;
 
     float acc[kTokensPerLane][GP];
 #pragma unroll
@@ -295,57 +245,69 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_main(
 
     for (int gb0 = 0; gb0 < ngroups; gb0 += kBatchGroups) {
         const int gcount = min(kBatchGroups, ngroups - gb0);
-        uint32_t wa[kGroupBits], wb[kGroupBits];
-        {
-            uint32_t ida[kGroupBits], idb[kGroupBits];
-#pragma unroll
-            for (int r = 0; r < kGroupBits; ++r) {
-                ida[r] = pids[gb0 * kGroupBits + r] & (kMaxPlanesPerHead - 1);
-                idb[r] = pids[min(gb0 + 1, gb0 + gcount - 1) * kGroupBits + r] &
-                         (kMaxPlanesPerHead - 1);
-            }
-            load_group(hp, ida, word_stride, gwc, wa);
-            load_group(hp, idb, word_stride, gwc, wb);
-        }
-        __syncthreads();
+        __syncthreads();  // the previous batch's tables are no longer read
         {
             const float4 *src =
                 reinterpret_cast<const float4 *>(lut + (size_t)gb0 * kLutEntries * GP);
             const int nvec = gcount * kLutEntries * GP / 4;
             for (int e = tid; e < nvec; e += kScanThreads) lds_v4[e] = src[e];
             for (int e = tid; e < gcount * kGroupBits; e += kScanThreads)
-                lids[e] = pids[gb0 * kGroupBits + e] & (kMaxPlanesPerHead - 1);
+                lrow[e] = (uint64_t)(pids[gb0 * kGroupBits + e] & (kMaxPlanesPerHead - 1)) *
+                          (uint64_t)word_stride;
         }
         __syncthreads();
-        for (int gi = 0; gi < gcount; gi += 2) {
-            uint32_t ida[kGroupBits], idb[kGroupBits];
-            lds_ids(lids, min(gi + 2, gcount - 1), ida);
-            lds_ids(lids, min(gi + 3, gcount - 1), idb);
-            process_group<GP>(wa, sel_pair, lds + gi * kLutEntries * GP, acc);
-            load_group(hp, ida, word_stride, gwc, wa);
-            if (gi + 1 < gcount)
-                process_group<GP>(wb, sel_pair, lds + (gi + 1) * kLutEntries * GP, acc);
-            load_group(hp, idb, word_stride, gwc, wb);
+        uint32_t buf[kPrefetch][2];
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u) issue_group(lane_base, lrow, min(u, gcount - 1), s, buf[u]);
+        for (int gi = 0; gi < gcount; gi += kPrefetch) {
+#pragma unroll
+            for (int u = 0; u < kPrefetch; ++u) {
+                if (gi + u < gcount)
+                    process_group<GP>(buf[u], s, lds + (gi + u) * kLutEntries * GP, acc);
+                issue_group(lane_base, lrow, min(gi + u + kPrefetch, gcount - 1), s, buf[u]);
+            }
         }
     }
 
-    const int tok0 = gw * 32 + half * kTokensPerLane;
-    if (tok0 >= n) return;
-    const bool full = (tok0 + kTokensPerLane <= n) && ((n & 3) == 0);
+    // Scores leave through LDS so that every store instruction writes 1 KB of one row:
+    // each wave stages its 512 tokens for two queries at a time in its own 4 KB.
+    __syncthreads();  // all table reads of the workgroup are done
+    float *stage = lds + wave * 2 * 512;
+    const int wtok0 = (tile * kTileWords + wave * kWordsPerWave) * 32;  // wave's first token
+    const int pos = (lane >> 2) * 32 + s * kTokensPerLane;             // lane's first token
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        if (g >= G) break;
-        float *out = scores + ((size_t)h * G + g) * n + tok0;
-        if (full) {
+    for (int g0 = 0; g0 < GP; g0 += 2) {
+        if (g0 >= G) break;
 #pragma unroll
-            for (int m = 0; m < kTokensPerLane; m += 4)
-                *reinterpret_cast<float4 *>(out + m) =
-                    make_float4(acc[m][g], acc[m + 1][g], acc[m + 2][g], acc[m + 3][g]);
-        } else {
-#pragma unroll
-            for (int m = 0; m < kTokensPerLane; ++m)
-                if (tok0 + m < n) out[m] = acc[m][g];
+        for (int gg = 0; gg < 2 && g0 + gg < GP; ++gg) {
+            float *d = stage + gg * 512 + pos;
+            *reinterpret_cast<float4 *>(d) =
+                make_float4(acc[0][g0 + gg], acc[1][g0 + gg], acc[2][g0 + gg], acc[3][g0 + gg]);
+            *reinterpret_cast<float4 *>(d + 4) =
+                make_float4(acc[4][g0 + gg], acc[5][g0 + gg], acc[6][g0 + gg], acc[7][g0 + gg]);
         }
+        __builtin_amdgcn_wave_barrier();  // the wave's staged rows are complete
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+            const int g = g0 + gg;
+            if (g >= G) break;
+            float *row = scores + ((size_t)h * G + g) * n;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t = half * 256 + lane * 4;  // token within the wave's 512
+                const float4 v = *reinterpret_cast<const float4 *>(stage + gg * 512 + t);
+                const int tok = wtok0 + t;
+                if (tok + 4 <= n && (n & 3) == 0) {
+                    *reinterpret_cast<float4 *>(row + tok) = v;
+                } else {
+                    if (tok < n) row[tok] = v.x;
+                    if (tok + 1 < n) row[tok + 1] = v.y;
+                    if (tok + 2 < n) row[tok + 2] = v.z;
+                    if (tok + 3 < n) row[tok + 3] = v.w;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();  // reads done before the next pair is staged
     }
 }
 
@@ -357,7 +319,7 @@ hipError_t launch_main_gp(const fathom_store &st, int G, float *scores, const ch
     const int nblocks = st.n_heads * tiles;
     constexpr int kBatchGroups = kLdsBudget / (kLutEntries * GP * (int)sizeof(float));
     const size_t lds = (size_t)kBatchGroups * kLutEntries * GP * sizeof(float) +
-                       (size_t)kBatchGroups * kGroupBits * sizeof(uint32_t);
+                       (size_t)kBatchGroups * kGroupBits * sizeof(uint64_t);
     hipLaunchKernelGGL(k_scan_main<GP>, dim3(nblocks), dim3(kScanThreads), lds, s,
                        st.planes, st.n_tokens, st.word_stride, G, st.n_heads, tiles, ws,
                        scores);
