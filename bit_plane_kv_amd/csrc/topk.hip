@@ -86,17 +86,52 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t *total) {
     return r;
 }
 
+// One radix step over a set of keys: histogram of digit (key >> sh) & (nb - 1) of the
+// keys whose top bits equal `prefix` (all keys when `all`), then find the bin holding
+// the need-th largest.  Returns (via pick) the bin, the count above it and its count.
+__device__ __forceinline__ void find_bin(uint32_t *hist, uint32_t *scan_sh, uint32_t *pick,
+                                         int nb, uint32_t need) {
+    const int tid = threadIdx.x;
+    uint32_t c4[4];
+    uint32_t local = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int b = nb - 1 - (4 * tid + e);  // thread t owns 4 bins, highest first
+        c4[e] = b >= 0 ? hist[b] : 0u;
+        local += c4[e];
+    }
+    uint32_t total;
+    const uint32_t above = block_excl_scan(local, scan_sh, &total);
+    if (above < need && need <= above + local) {
+        uint32_t cum = above;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (cum < need && need <= cum + c4[e]) {
+                pick[0] = (uint32_t)(nb - 1 - (4 * tid + e));
+                pick[1] = cum;
+                pick[2] = c4[e];
+            }
+            cum += c4[e];
+        }
+    }
+    __syncthreads();
+}
+
+constexpr int kCandCap = 4096;  // threshold-bin entries refined in LDS
+
 // kExplicit: input entries carry their own int32 index (candidate levels); otherwise
 // the index is the position in the row.  kCandOut: write (value, index) candidates
 // (at column chunk*kk of the output row) instead of final indices.
 template <bool kExplicit, bool kCandOut>
-__global__ __launch_bounds__(kThreads) void k_topk_chunk(
+__global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
     const float *__restrict__ vals, const int32_t *__restrict__ in_idx, int64_t row_len,
     int64_t in_stride, int row0, int k, float *__restrict__ out_val,
     int32_t *__restrict__ out_idx, int64_t out_stride) {
     __shared__ uint32_t hist[4096];
+    __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t scan_sh[17];
     __shared__ uint32_t pick[3];
+    __shared__ uint32_t ncand;
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const int64_t row = (int64_t)row0 + blockIdx.y;
@@ -104,12 +139,12 @@ __global__ __launch_bounds__(kThreads) void k_topk_chunk(
     const int len = (int)min((int64_t)kTopkChunk, row_len - start);
     const int kr = min(k, len);
     const float *v = vals + row * in_stride + start;
-    const int p0 = tid * kEPT;
+    const int p0 = tid * kEPT;  // this thread's positions p0 .. p0+31
     const int nvalid = max(0, min(kEPT, len - p0));
+    const uint32_t vmask = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
 
     uint32_t key[kEPT];
-    const bool vec = ((((uintptr_t)(v + p0)) & 15u) == 0) && nvalid == kEPT;
-    if (vec) {
+    if (((((uintptr_t)(v + p0)) & 15u) == 0) && nvalid == kEPT) {
 #pragma unroll
         for (int e = 0; e < kEPT; e += 4) {
             const float4 f = *reinterpret_cast<const float4 *>(v + p0 + e);
@@ -123,95 +158,113 @@ __global__ __launch_bounds__(kThreads) void k_topk_chunk(
         for (int e = 0; e < kEPT; ++e) key[e] = e < nvalid ? order_key(v[p0 + e]) : 0u;
     }
 
-    // ---- radix select: after each pass the k-th largest key is known to share
-    //      `prefix` in its top (32 - shift) bits; `need` of the entries still to pick
-    //      lie in that bin.
-    uint32_t prefix = 0u;
-    uint32_t need = (uint32_t)kr;
-    int shift = 32;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-        const int nb = pass == 2 ? 256 : 4096;
-        for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
-        __syncthreads();
+    // ---- pass 1: top 12 bits of every key
+    for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
+    if (tid == 0) ncand = 0u;
+    __syncthreads();
+    if (nvalid == kEPT) {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
-            if (e < nvalid && (pass == 0 || (key[e] >> shift) == prefix))
-                atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        // thread t owns bins nb-1-4t .. nb-4-4t (highest first)
-        uint32_t c4[4];
-        uint32_t local = 0u;
+        for (int e = 0; e < kEPT; ++e) atomicAdd(&hist[key[e] >> 20], 1u);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int b = nb - 1 - (4 * tid + e);
-            c4[e] = b >= 0 ? hist[b] : 0u;
-            local += c4[e];
-        }
-        uint32_t total;
-        const uint32_t above = block_excl_scan(local, scan_sh, &total);
-        if (above < need && need <= above + local) {
-            uint32_t cum = above;
+        for (int e = 0; e < kEPT; ++e)
+            if (e < nvalid) atomicAdd(&hist[key[e] >> 20], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, scan_sh, pick, 4096, (uint32_t)kr);
+    uint32_t prefix = pick[0];
+    uint32_t need = (uint32_t)kr - pick[1];
+    uint32_t in_bin = pick[2];
+    int shift = 20;
+
+    if (in_bin != need) {
+        // The k-th largest key lies inside bin `prefix`; refine on its in_bin entries.
+        const bool in_lds = in_bin <= (uint32_t)kCandCap;
+        const int ncands = (int)in_bin;  // entries of the first bin (the list's length)
+        if (in_lds) {  // compact the bin's keys into LDS (any order)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (cum < need && need <= cum + c4[e]) {
-                    pick[0] = (uint32_t)(nb - 1 - (4 * tid + e));
-                    pick[1] = cum;
-                    pick[2] = c4[e];
-                }
-                cum += c4[e];
+            for (int e = 0; e < kEPT; ++e) {
+                if (((vmask >> e) & 1u) && (key[e] >> 20) == prefix)
+                    cand[atomicAdd(&ncand, 1u)] = key[e];
             }
         }
-        __syncthreads();
-        const int bits = pass == 2 ? 8 : 12;
-        prefix = (shift == 32 ? 0u : (prefix << bits)) | pick[0];
-        shift = sh;
-        need -= pick[1];
-        const uint32_t in_bin = pick[2];
-        __syncthreads();
-        if (in_bin == need) break;  // every entry of the bin is a winner
+        for (int pass = 1; pass < 3; ++pass) {
+            const int sh = pass == 1 ? 8 : 0;
+            const int nb = pass == 1 ? 4096 : 256;
+            __syncthreads();  // previous readers of hist / pick are done
+            for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
+            __syncthreads();
+            if (in_lds) {
+                for (int c = tid; c < ncands; c += kThreads) {
+                    const uint32_t kv = cand[c];
+                    if ((kv >> shift) == prefix) atomicAdd(&hist[(kv >> sh) & (nb - 1)], 1u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < kEPT; ++e) {
+                    if (((vmask >> e) & 1u) && (key[e] >> shift) == prefix)
+                        atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
+                }
+            }
+            __syncthreads();
+            find_bin(hist, scan_sh, pick, nb, need);
+            prefix = (prefix << (pass == 1 ? 12 : 8)) | pick[0];
+            shift = sh;
+            need -= pick[1];
+            in_bin = pick[2];
+            if (in_bin == need) break;  // every entry of the bin is a winner
+        }
     }
 
-    // ---- ordered output: greater entries all win, equal entries by lowest position
-    uint32_t ngt = 0u, neq = 0u;
+    // ---- ordered output: greater entries all win; of the entries equal to the
+    //      threshold prefix, the `need` lowest positions win.  Masks over the thread's
+    //      32 positions, one packed scan, then the set bits in ascending order.
+    uint32_t mgt = 0u, meq = 0u;
 #pragma unroll
     for (int e = 0; e < kEPT; ++e) {
-        if (e < nvalid) {
-            const uint32_t kv = key[e] >> shift;
-            ngt += kv > prefix;
-            neq += kv == prefix;
-        }
+        const uint32_t kv = key[e] >> shift;
+        mgt |= (uint32_t)(kv > prefix) << e;
+        meq |= (uint32_t)(kv == prefix) << e;
     }
+    mgt &= vmask;
+    meq &= vmask;
     uint32_t total;
-    const uint32_t before = block_excl_scan(ngt | (neq << 16), scan_sh, &total);
-    uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
+    const uint32_t before =
+        block_excl_scan((uint32_t)__popc(mgt) | ((uint32_t)__popc(meq) << 16), scan_sh, &total);
+    const uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
     const uint32_t r = need;
+    // Equal entries of earlier threads that win, and this thread's that still win (the
+    // lowest `take` bits of meq).  Written as a clamp followed by a subtraction that
+    // cannot wrap: the form "eqb < r ? r - eqb : 0" was compiled (hipcc 7.2) into an
+    // unconditional no-wrap subtraction, from which the clamp below was folded away.
+    const uint32_t eq_won_before = min(eqb, r);
+    const uint32_t eq_left = r - eq_won_before;
+    uint32_t take = min(eq_left, (uint32_t)__popc(meq));
+    uint32_t sel = mgt, m = meq;
+    while (take > 0u) {
+        const uint32_t low = m & (0u - m);
+        sel |= low;
+        m ^= low;
+        --take;
+    }
+    int slot = (int)(gtb + eq_won_before);
     const int32_t *vi = kExplicit ? in_idx + row * in_stride + start : nullptr;
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
-        if (e < nvalid) {
-            const uint32_t kv = key[e] >> shift;
-            int slot = -1;
-            if (kv > prefix) {
-                slot = (int)(gtb + min(eqb, r));
-                ++gtb;
-            } else if (kv == prefix) {
-                if (eqb < r) slot = (int)(gtb + eqb);
-                ++eqb;
-            }
-            if (slot >= 0 && slot < kr) {
-                const int p = p0 + e;
-                const int32_t index = kExplicit ? vi[p] : (int32_t)(start + p);
-                if (kCandOut) {
-                    const int64_t o = row * out_stride + (int64_t)chunk * min(k, kTopkChunk) + slot;
-                    out_val[o] = key_value(key[e]);
-                    out_idx[o] = index;
-                } else {
-                    out_idx[row * (int64_t)k + slot] = index;
-                }
+    while (sel != 0u) {
+        const int e = __ffs(sel) - 1;
+        sel &= sel - 1u;
+        if (slot < kr) {
+            const int p = p0 + e;
+            const int32_t index = kExplicit ? vi[p] : (int32_t)(start + p);
+            if (kCandOut) {
+                const int64_t o =
+                    row * out_stride + (int64_t)chunk * min(k, kTopkChunk) + slot;
+                out_val[o] = key_value(key[e]);  // dynamic index: the key is re-read
+                out_idx[o] = index;
+            } else {
+                out_idx[row * (int64_t)k + slot] = index;
             }
         }
+        ++slot;
     }
 }
 
