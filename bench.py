@@ -47,6 +47,10 @@ def parse():
                     choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--no-host", action="store_true",
+                    help="skip the host-resident 1M-token single-layer step")
+    ap.add_argument("--host-only", action="store_true",
+                    help="run only the host-resident 1M-token single-layer step")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --kernel: also run a 1 GiB streaming read and a 256 MiB "
                          "copy, whose byte counts scale the profiler's HBM counters")
@@ -67,6 +71,10 @@ def main():
     import torch
     from bit_plane_kv_amd import fathom as F
     from bit_plane_kv_amd import synth
+
+    if args.host_only:
+        print(json.dumps(host_resident_step(args)), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.config]
     H, G, n, k, B = cfg.H, cfg.G, cfg.n, cfg.k, args.budget
@@ -165,6 +173,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm_scale, sample_keys)
 
+    host = None
+    if not args.no_host:
+        del K, V, st, ws, scores
+        torch.cuda.empty_cache()
+        host = host_resident_step(args)
+
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "Gkeys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -181,6 +195,7 @@ def main():
                            "winner_rows": int(H * G * k * 512)},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "parity_before_timing": parity,
+        "host_resident_1m_layer_step": host,
     }
     print(json.dumps(result), flush=True)
 
@@ -300,6 +315,120 @@ def load_traffic(algorithmic_bytes):
         return rec.get("traffic_bytes_per_launch")
     except Exception:
         return None
+
+
+def timed_ms(fn, stream, reps, flush=None, sink=None):
+    """Mean GPU time of fn over reps launches (events on the launch stream); with flush,
+    a 1 GiB streaming read precedes every launch so it starts with cold caches."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    fn()
+    tot = 0.0
+    for _ in range(reps):
+        if flush is not None:
+            F.fathom_stream_read(flush, flush.numel(), sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        tot += a.elapsed_time(b)
+    return tot / reps
+
+
+def link_rate(dev, stream, nbytes=1 << 30):
+    """Host-to-GPU link rate L = max(DMA copy from a pinned buffer, zero-copy streaming
+    read of the same pinned buffer by a kernel), GB/s."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h.fill_(1)
+    d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    dma = nbytes / (timed_ms(lambda: d.copy_(h, non_blocking=True), stream, 3) * 1e-3) / 1e9
+    zc = nbytes / (timed_ms(lambda: F.fathom_stream_read(h, nbytes, sink), stream, 3) * 1e-3) / 1e9
+    del h, d
+    return {"dma_h2d_GBps": round(dma, 2), "zero_copy_read_GBps": round(zc, 2),
+            "L_GBps": round(max(dma, zc), 2)}
+
+
+def host_resident_step(args):
+    """One layer's decode step at n = 1M (8 KV heads x 4 queries, B = 92, k = 512) with
+    the bit-plane store and the bf16 K/V rows in pinned host memory (read by the GPU over
+    the host link), against the same store mirrored in HBM; plus the measured link rate
+    and the scan's plane-byte rate over the link."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS["qwen3_8b_1m_layer_step"]
+    H, G, n, k, B = cfg.H, cfg.G, cfg.n, cfg.k, args.budget
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sm = float(np.float32(1.0 / np.sqrt(128)))
+    t0 = time.time()
+    st_d = F.Store.empty(H, n, dev)
+    K_d = torch.empty((H, n, 128), dtype=torch.bfloat16, device=dev)
+    for h in range(H):
+        keys = synth.keys_torch(args.seed, cfg.cfg_id, [h], n, dev)
+        F.fathom_quantize_store(keys, st_d.view_heads(h, h + 1))
+        K_d[h].copy_(keys[0])
+        del keys
+    V_d = synth.values_torch(args.seed, cfg.cfg_id, range(H), n, dev)
+    q = torch.from_numpy(synth.queries_np(args.seed, cfg.cfg_id, range(H), G)).to(dev)
+    planes_h = torch.empty(st_d.planes.shape, dtype=torch.int32, pin_memory=True)
+    planes_h.copy_(st_d.planes)
+    K_h = torch.empty(K_d.shape, dtype=torch.bfloat16, pin_memory=True)
+    K_h.copy_(K_d)
+    V_h = torch.empty(V_d.shape, dtype=torch.bfloat16, pin_memory=True)
+    V_h.copy_(V_d)
+    st_h = F.Store(planes_h, st_d.scale, st_d.zero, st_d.var, n)
+    torch.cuda.synchronize()
+    log(f"[bench] host-resident 1M layer ready in {time.time() - t0:.1f}s")
+
+    ws = F.step_workspace(st_d, G, k, dev)
+    out_d = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty_like(out_d)
+    idx_d = torch.empty((H, G, k), dtype=torch.int32, device=dev)
+    idx_h = torch.empty_like(idx_d)
+    F.fathom_step(st_d, q, K_d, V_d, B, k, sm, out=out_d, idx_out=idx_d, ws=ws)
+    F.fathom_step(st_h, q, K_h, V_h, B, k, sm, out=out_h, idx_out=idx_h, ws=ws)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx_d, idx_h) and torch.equal(out_d, out_h))
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    step_h = timed_ms(lambda: F.fathom_step(st_h, q, K_h, V_h, B, k, sm, out=out_h, ws=ws),
+                      stream, 10, flush, sink)
+    step_d = timed_ms(lambda: F.fathom_step(st_d, q, K_d, V_d, B, k, sm, out=out_d, ws=ws),
+                      stream, 10, flush, sink)
+    depth = F.fathom_plan(st_d, q, B)
+    sws = F.scan_workspace(st_d, G, dev)
+    F.fathom_scan_prepare(st_d, q, depth, sws)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    scan_h = timed_ms(lambda: F.fathom_scan_prepared(st_h, G, scores, sws), stream, 10,
+                      flush, sink)
+    scan_d = timed_ms(lambda: F.fathom_scan_prepared(st_d, G, scores, sws), stream, 10,
+                      flush, sink)
+    fixed = F.fathom_plan_fixed(st_d, 34)
+    F.fathom_scan_prepare(st_d, q, fixed, sws)
+    scan136_h = timed_ms(lambda: F.fathom_scan_prepared(st_h, G, scores, sws), stream, 10,
+                         flush, sink)
+    del flush
+    L = link_rate(dev, stream)
+    plane_bytes = B / 8 * n * H
+    plane_gbps = plane_bytes / (scan_h * 1e-3) / 1e9
+    return {
+        "workload": cfg.name, "kv_heads": H, "queries_per_kv_head": G, "tokens": n,
+        "budget_bits": B, "k": k, "host_equals_hbm": same,
+        "step_ms_host": round(step_h, 3), "step_ms_hbm": round(step_d, 3),
+        "scan_ms_host": round(scan_h, 3), "scan_ms_hbm": round(scan_d, 3),
+        "scan_fixed136_ms_host": round(scan136_h, 3),
+        "scan_plane_bytes": int(plane_bytes),
+        "scan_plane_GBps_host": round(plane_gbps, 2),
+        "link": L, "scan_frac_of_link": round(plane_gbps / L["L_GBps"], 4),
+        "scan_gkeys_per_s_host": round(H * n / (scan_h * 1e-3) / 1e9, 2),
+        "pinned_host_bytes": int(planes_h.numel() * 4 + 2 * K_h.numel() * 2),
+    }
 
 
 def cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm, sample_keys):
