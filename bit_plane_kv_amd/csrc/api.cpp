@@ -52,7 +52,8 @@ int check_store(const fathom_store *st) {
     if (!st) return FATHOM_ERR_INVALID_ARG;
     if (st->n_heads < 1 || st->n_heads > 65535 || st->n_tokens < 1)
         return FATHOM_ERR_INVALID_ARG;
-    if (st->word_stride < (st->n_tokens + 31) / 32) return FATHOM_ERR_INVALID_ARG;
+    if (st->word_stride < (st->n_tokens + 31) / 32 || (st->word_stride & 3) != 0)
+        return FATHOM_ERR_INVALID_ARG;
     if (!st->planes || !st->scale || !st->zero || !st->var) return FATHOM_ERR_INVALID_ARG;
     if (!aligned(st->planes, 16) || !aligned(st->scale, 4) || !aligned(st->zero, 4) ||
         !aligned(st->var, 4))

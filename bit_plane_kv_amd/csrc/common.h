@@ -12,41 +12,42 @@ namespace fathom {
 constexpr int kD = FATHOM_D;                 // channels per head
 constexpr int kPlanes = FATHOM_PLANES;       // 4 planes per channel
 constexpr int kMaxPlanesPerHead = kD * kPlanes;  // 512
-constexpr int kGroupBits = 8;                // planes per lookup-table group
+constexpr int kGroupBits = 8;                // planes per matrix-core byte operand
 constexpr int kMaxGroups = kMaxPlanesPerHead / kGroupBits;  // 64
-constexpr int kLutEntries = 1 << kGroupBits;  // 256
+constexpr int kKBlockGroups = 4;             // groups summed by one i8 MFMA (K = 32)
+constexpr int kMaxKBlocks = kMaxGroups / kKBlockGroups;     // 16
+constexpr int kDigits = 4;                   // signed base-256 digits per weight
 
 // ---------------------------------------------------------------------------------
-// Scan workspace, per head:  a meta block (plane list, constant term, counts) and the
-// lookup tables.  meta: int32 n_planes, int32 n_groups, int32 pad[2], float C[8],
-// uint32 plane[512] (c*4 + j, channels ascending, planes ascending within a channel;
-// entries past n_planes repeat the group's first plane so reads stay in bounds).
-// lut: [kMaxGroups][256][gp] fp32, gp = G padded to 1, 2, 4 or 8.
+// Scan workspace, per head: a meta block, then per K-block (4 groups of 8 planes) and
+// per wave lane one record of the MFMA operands that lane supplies.
+//   meta: int32 n_planes, n_groups, n_kblocks, pad; float C[8] (constant term of each
+//   query); float S[8] (power-of-two weight unit of each query); uint32 plane[512]
+//   (c*4 + j, channels ascending, planes ascending within a channel).
+//   record (kblock, lane), lane = 16*kb + 4*w + s:  uint32 row of plane s and of plane
+//   s+4 of group 4*kblock + kb (kSkipRow: no plane, load nothing), then for each set of
+//   4 queries the 8 bytes of A row (lane & 15) = (query 4*set + ((lane & 15) >> 2),
+//   digit lane & 3) over that group's 8 planes.  QS = 1 (G <= 4): 16 bytes; QS = 2: 32.
 // ---------------------------------------------------------------------------------
 constexpr size_t kMetaBytes = 4096;
+constexpr uint32_t kSkipRow = 0xFFFFFFFFu;
 struct ScanMeta {
     int32_t n_planes;
     int32_t n_groups;
-    int32_t pad[2];
+    int32_t n_kblocks;
+    int32_t pad;
     float C[FATHOM_MAX_G];
+    float S[FATHOM_MAX_G];
     uint32_t plane[kMaxPlanesPerHead];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
 
-inline int padded_g(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
-inline size_t scan_lut_bytes_per_head(int G) {
-    return (size_t)kMaxGroups * kLutEntries * padded_g(G) * sizeof(float);
+inline int query_sets(int G) { return G <= 4 ? 1 : 2; }
+inline size_t scan_rec_bytes_per_head(int G) {
+    return (size_t)kMaxKBlocks * 64 * 16 * query_sets(G);
 }
 inline size_t scan_ws_bytes(int H, int G) {
-    return (size_t)H * (kMetaBytes + scan_lut_bytes_per_head(G));
-}
-// meta blocks first (H * kMetaBytes), then the tables
-inline ScanMeta *scan_meta(void *ws, int h) {
-    return reinterpret_cast<ScanMeta *>(static_cast<char *>(ws) + (size_t)h * kMetaBytes);
-}
-inline float *scan_lut(void *ws, int H, int G, int h) {
-    return reinterpret_cast<float *>(static_cast<char *>(ws) + (size_t)H * kMetaBytes +
-                                     (size_t)h * scan_lut_bytes_per_head(G));
+    return (size_t)H * (kMetaBytes + scan_rec_bytes_per_head(G));
 }
 
 // ---------------------------------------------------------------------------------

@@ -7,35 +7,58 @@
 //
 // Arithmetic.  With m = p 2^(4-t) + h(t) (bin midpoint, h(t) = (2^(4-t) - 1)/2) and p
 // the t-plane prefix, p 2^(4-t) = sum_{j<t} bit_j 2^(3-j), so
-//   score_g(i) = C_g + sum over the head's planes (c, j) of bit_cj(i) * q_gc s_c 2^(3-j),
-//   C_g = sum_c q_gc (z_c + s_c h(t_c)).
-// The B planes of a head are cut into groups of 8; for each group a 256-entry table
-// holds, for every 8-bit pattern, the sum of the weights of the planes whose bit is set.
-// A token then costs one table lookup per group (per query: G adds) instead of one add
-// per plane: the integer work per byte of planes -- what bounds the HBM-resident scan
-// -- is a byte gather plus an 8x8 bit transpose per 8 tokens and 8 planes.
+//   score_g(i) = C_g + sum over the head's planes P = (c, j) of bit_P(i) * w_gP,
+//   w_gP = q_gc s_c 2^(3-j),   C_g = sum_c q_gc (z_c + s_c h(t_c)).
+// The sum over planes is the product of the token-by-plane bit matrix and the
+// plane-by-query weight matrix, so it runs on the matrix cores in int8: each weight
+// becomes an integer count of a per-query unit S_g = 2^(e_g - 30) (e_g: the binary
+// exponent just above the largest |w_gP| of the head, so the error is at most 2^-31 of
+// the largest weight), written as 4 signed base-256 digits.  One 16x16x32 i8 MFMA takes
+// 16 rows = 4 queries x 4 digits, K = 32 planes (4 groups of 8) and 16 columns = 16
+// tokens whose plane bits are bytes; the int32 sums are exact, and one fp32 combine per
+// score gives C_g + S_g * sum_d 256^d D_d.  Per 8 tokens and 8 planes a lane spends two
+// byte transposes across its quad and two masks per token; no table lookups.
+#include <algorithm>
+#include <mutex>
+
 #include "common.h"
 
 namespace fathom {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------------
-// prepare: plane list, constant term and lookup tables of one head (one workgroup)
+// prepare: plane list, constant terms, weight units and MFMA operand records of one
+// head (one workgroup)
 // ---------------------------------------------------------------------------------
-template <int GP>
+// Digit d (0..3) of M in signed base 256: M = sum_d 256^d digit_d, digits 0..2 in
+// [-128, 127]; for |M| <= 2^30 the top digit lies in [-64, 64].
+__device__ int weight_digit(long long M, int d) {
+    for (int k = 0; k < d; ++k) {
+        const long long low = ((M & 255) ^ 128) - 128;
+        M = (M - low) >> 8;
+    }
+    if (d == kDigits - 1) return (int)M;
+    return (int)(((M & 255) ^ 128) - 128);
+}
+
+template <int QS>
 __global__ __launch_bounds__(256) void k_scan_prepare(
     const float *__restrict__ q, const uint8_t *__restrict__ depth,
     const float *__restrict__ scale, const float *__restrict__ zero, int H, int G,
     char *__restrict__ ws) {
+    constexpr int NQ = 4 * QS;
     __shared__ int tc[kD];
     __shared__ int off[kD + 1];
-    __shared__ double wt[GP][kMaxPlanesPerHead];
-    __shared__ double red[GP][kD];
+    __shared__ uint32_t pl[kMaxPlanesPerHead];
+    __shared__ double wt[NQ][kMaxPlanesPerHead];
+    __shared__ double red[NQ][kD];
+    __shared__ double unit[NQ];
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     ScanMeta *meta = reinterpret_cast<ScanMeta *>(ws + (size_t)h * kMetaBytes);
-    float *lut = reinterpret_cast<float *>(ws + (size_t)H * kMetaBytes +
-                                           (size_t)h * kMaxGroups * kLutEntries * GP *
-                                               sizeof(float));
+    uint32_t *rec = reinterpret_cast<uint32_t *>(ws + (size_t)H * kMetaBytes +
+                                                 (size_t)h * kMaxKBlocks * 64 * 16 * QS);
     if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
     __syncthreads();
     if (tid < 64) {  // one wave: exclusive prefix sum of the depths, 2 channels a lane
@@ -54,276 +77,435 @@ __global__ __launch_bounds__(256) void k_scan_prepare(
     __syncthreads();
     const int nplanes = off[kD];
     const int ngroups = (nplanes + kGroupBits - 1) / kGroupBits;
+    // at least one K-block, so that a head with no planes still writes its constants
+    const int nkb = max(1, (ngroups + kKBlockGroups - 1) / kKBlockGroups);
     if (tid < kD) {
         const int c = tid, t = tc[c], o = off[c];
         const double s = (double)scale[(size_t)h * kD + c];
         const double z = (double)zero[(size_t)h * kD + c];
         const double hm = (double)((16 >> t) - 1) * 0.5;  // bin-midpoint offset h(t)
-        for (int j = 0; j < t; ++j) meta->plane[o + j] = (uint32_t)(c * kPlanes + j);
+        for (int j = 0; j < t; ++j) pl[o + j] = (uint32_t)(c * kPlanes + j);
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
+        for (int g = 0; g < NQ; ++g) {
             const double qv = g < G ? (double)q[((size_t)h * G + g) * kD + c] : 0.0;
             for (int j = 0; j < t; ++j) wt[g][o + j] = (qv * s) * (double)(8 >> j);
             red[g][c] = qv * (z + s * hm);  // this channel's share of C_g
         }
     }
     __syncthreads();
-    // pad the last group with a valid plane so the scan's loads stay in bounds
-    if (tid < ngroups * kGroupBits - nplanes) {
-        meta->plane[nplanes + tid] = meta->plane[nplanes - 1 < 0 ? 0 : nplanes - 1];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) wt[g][nplanes + tid] = 0.0;
-    }
     for (int s2 = kD / 2; s2 > 0; s2 >>= 1) {  // C_g: fixed-order tree sum over channels
         if (tid < s2) {
 #pragma unroll
-            for (int g = 0; g < GP; ++g) red[g][tid] += red[g][tid + s2];
+            for (int g = 0; g < NQ; ++g) red[g][tid] += red[g][tid + s2];
         }
         __syncthreads();
     }
-    if (tid < FATHOM_MAX_G) meta->C[tid] = tid < G ? (float)red[tid < GP ? tid : 0][0] : 0.0f;
+    // weight unit of each query: one wave per query
+    for (int g = tid >> 6; g < NQ; g += 4) {
+        double mx = 0.0;
+        for (int p = lane; p < nplanes; p += 64) mx = fmax(mx, fabs(wt[g][p]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+        if (lane == 0) {
+            int e = 0;
+            frexp(mx, &e);  // mx < 2^e
+            unit[g] = mx > 0.0 ? ldexp(1.0, e - 30) : 1.0;
+        }
+    }
+    __syncthreads();
+    for (int p = tid; p < nplanes; p += 256) meta->plane[p] = pl[p];
+    if (tid < FATHOM_MAX_G) {
+        meta->C[tid] = tid < G ? (float)red[tid][0] : 0.0f;
+        meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
+    }
     if (tid == 0) {
         meta->n_planes = nplanes;
         meta->n_groups = ngroups;
+        meta->n_kblocks = nkb;
+        meta->pad = 0;
     }
-    // tables: entry (group, pattern) = sum of the weights of the planes set in pattern
-    for (int e = tid; e < ngroups * kLutEntries; e += 256) {
-        const int grp = e >> 8, pat = e & (kLutEntries - 1);
-        float v[GP];
+    // operand records: lane ln of K-block kbl serves group 4*kbl + (ln >> 4)
+    for (int e = tid; e < nkb * 64; e += 256) {
+        const int kbl = e >> 6, ln = e & 63;
+        const int grp = kbl * kKBlockGroups + (ln >> 4);
+        const int s = ln & 3, r = ln & 15;
+        const int p0 = grp * kGroupBits + s, p1 = p0 + 4;
+        uint32_t *dst = rec + (size_t)e * 4 * QS;
+        dst[0] = p0 < nplanes ? pl[p0] : kSkipRow;
+        dst[1] = p1 < nplanes ? pl[p1] : kSkipRow;
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            double a = 0.0;
-#pragma unroll
-            for (int r = 0; r < kGroupBits; ++r)
-                a += ((pat >> r) & 1) ? wt[g][grp * kGroupBits + r] : 0.0;
-            v[g] = (float)a;
+        for (int set = 0; set < QS; ++set) {
+            const int g = 4 * set + (r >> 2), dg = r & 3;
+            uint32_t wlo = 0, whi = 0;
+            for (int i = 0; i < kGroupBits; ++i) {
+                const int p = grp * kGroupBits + i;
+                const long long M =
+                    (g < G && p < nplanes) ? llrint(wt[g][p] / unit[g]) : 0LL;
+                const uint32_t byte = (uint32_t)(weight_digit(M, dg) & 0xFF);
+                if (i < 4) wlo |= byte << (8 * i);
+                else whi |= byte << (8 * (i - 4));
+            }
+            dst[2 + 2 * set] = wlo;
+            dst[3 + 2 * set] = whi;
         }
-        float *dst = lut + (size_t)e * GP;
-        if constexpr (GP == 1) {
-            dst[0] = v[0];
-        } else if constexpr (GP == 2) {
-            *reinterpret_cast<float2 *>(dst) = make_float2(v[0], v[1]);
-        } else {
-#pragma unroll
-            for (int g = 0; g < GP; g += 4)
-                *reinterpret_cast<float4 *>(dst + g) = make_float4(v[g], v[g + 1], v[g + 2], v[g + 3]);
-        }
+        if (QS == 2) dst[6] = dst[7] = 0;
     }
 }
 
 // ---------------------------------------------------------------------------------
 // main scan
 // ---------------------------------------------------------------------------------
-// 8x8 bit-matrix transpose: byte r of (lo: rows 0-3, hi: rows 4-7) is row r, bit c of
-// that byte is column c; afterwards byte c holds column c.
-__device__ __forceinline__ void transpose8x8(uint32_t &lo, uint32_t &hi) {
-    uint32_t t;
-    t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
-    lo = lo ^ t ^ (t << 7);
-    t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
-    hi = hi ^ t ^ (t << 7);
-    t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
-    lo = lo ^ t ^ (t << 14);
-    t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
-    hi = hi ^ t ^ (t << 14);
-    t = ((lo >> 4) ^ hi) & 0x0F0F0F0Fu;
-    hi = hi ^ t;
-    lo = lo ^ (t << 4);
-}
+// Shape.  A workgroup of 4 waves scores one super-step -- 1024 tokens (32 words) of one
+// head -- at a time, K-block by K-block (4 groups of 8 planes).  For each K-block, wave
+// kb copies the 8 rows of group kb, 128 contiguous bytes (whole cache lines) each,
+// straight from global memory into an LDS tile, 16 bytes a lane; after a barrier, wave
+// v takes tokens 256v .. 256v+255 (words 8v .. 8v+7) of all 32 rows from the tile:
+// lane 16*kb + 4*w + s reads words 8v+2w and 8v+2w+1 of planes s and s+4 of group kb.
+// A byte transpose across the quad then gives lane s byte s (8 tokens) of the group's 8
+// planes, so bit m of byte i is plane i's bit of token 8s + m; masking bit m of every
+// byte makes the MFMA column of token 8s + m (byte values 0 / 2^m, and -128 for m = 7,
+// divided out in the combine).  The MFMA output lane 16*j + 4*w + s then holds query
+// j's 4 digit sums for that token.  kTiles tiles rotate, so the copies of the next
+// K-blocks are in flight while one is used.
+constexpr int kScanThreads = 256;
+constexpr int kSuperWords = 32;       // words per super-step
+constexpr int kTileKbBytes = 1152;    // a group's 8 rows x 128 bytes; the extra 128 bytes
+                                      // start odd groups half-way round the LDS banks
+constexpr int kTileBytes = 4 * kTileKbBytes;
+#ifndef FATHOM_SCAN_TILES
+#define FATHOM_SCAN_TILES 4
+#endif
+#ifndef FATHOM_SCAN_ROUNDS
+#define FATHOM_SCAN_ROUNDS 1
+#endif
+#ifndef FATHOM_SCAN_WAVES_PER_EU
+#define FATHOM_SCAN_WAVES_PER_EU 4
+#endif
+constexpr int kTiles = FATHOM_SCAN_TILES;
+static_assert(kTiles >= 2 && kTiles <= 8, "tile ring");
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 
-// Shape of the main kernel.  A workgroup of 8 waves scores a tile of 128 words (4096
-// tokens) of one head.  In a wave, the 4 lanes of a quad share one 32-token word: lane
-// (4w + s) loads planes s and s+4 of word w, a 4x4 byte transpose across the quad gives
-// every lane byte s (8 tokens) of all 8 planes of the group, and lane (4w + s) scores
-// tokens 8s .. 8s+7 of the word.  Each lane thus issues 2 loads per group of 8 planes.
-constexpr int kScanThreads = 512;
-constexpr int kWordsPerWave = 16;
-constexpr int kTileWords = (kScanThreads / 64) * kWordsPerWave;  // 128 words
-constexpr int kTokensPerLane = 8;
-constexpr int kInflight = 4;   // table reads issued before their adds
-constexpr int kPrefetch = 4;   // groups of plane words in flight per lane
-constexpr int kLdsBudget = 48 * 1024;  // tables per batch (LDS also stages the scores)
+// 16-byte LDS slot of row i (0..7), chunk c (4 words, 0..7) in a group's region; the
+// xor spreads the operand reads (chunk 2v + w/2 of rows s = 0..3) over all banks.
+__device__ __forceinline__ int tile_slot(int i, int c) { return 8 * i + (c ^ ((2 * i) & 6)); }
+
+template <int QS>
+__device__ __forceinline__ size_t lds_head_bytes() {
+    return (size_t)kMaxKBlocks * 64 * QS * 8 + (size_t)kMaxKBlocks * 32 * 4;
+}
+template <int QS>
+size_t scan_lds_bytes() {
+    return 2 * ((size_t)kMaxKBlocks * 64 * QS * 8 + (size_t)kMaxKBlocks * 32 * 4) +
+           (size_t)kTiles * kTileBytes;
+}
 
 // Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
 // result is byte s of M_p (p = 0..3).  Two butterfly stages, each one DPP move of the
 // partner's word and one byte permute.
 __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t m, int s) {
-    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+    const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
     const uint32_t a = __builtin_amdgcn_perm(p, m, s < 2 ? 0x05040100u : 0x03020706u);
-    const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);
+    const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
     return __builtin_amdgcn_perm(q, a, (s & 1) ? 0x03070105u : 0x06020400u);
 }
 
-// Adds the table entries of tokens m0 .. m0+kInflight-1 (reads first, then adds).
-template <int GP>
-__device__ __forceinline__ void lookup_add(const uint32_t (&x)[2], int m0, const float *lg,
-                                           float (&acc)[kTokensPerLane][GP]) {
-    float e[kInflight][GP];
+template <int QS, bool kFirst>
+__device__ __forceinline__ void mma_kblock(const uint32_t (&w)[2][2], const long (&A)[QS],
+                                           int s, v4i (&acc)[2][8][QS]) {
+    uint32_t x[2][2];
 #pragma unroll
-    for (int m = 0; m < kInflight; ++m) {
-        const uint32_t pat = (x[(m0 + m) >> 2] >> (8 * ((m0 + m) & 3))) & 0xFFu;
-        const float *p = lg + pat * GP;
-        if constexpr (GP >= 4) {
-#pragma unroll
-            for (int g = 0; g < GP; g += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(p + g);
-                e[m][g] = v.x;
-                e[m][g + 1] = v.y;
-                e[m][g + 2] = v.z;
-                e[m][g + 3] = v.w;
-            }
-        } else if constexpr (GP == 2) {
-            const float2 v = *reinterpret_cast<const float2 *>(p);
-            e[m][0] = v.x;
-            e[m][1] = v.y;
-        } else {
-            e[m][0] = p[0];
-        }
+    for (int pos = 0; pos < 2; ++pos) {
+        x[pos][0] = quad_byte_transpose(w[0][pos], s);  // planes 0-3, byte s
+        x[pos][1] = quad_byte_transpose(w[1][pos], s);  // planes 4-7, byte s
     }
 #pragma unroll
-    for (int m = 0; m < kInflight; ++m)
+    for (int pos = 0; pos < 2; ++pos) {
 #pragma unroll
-        for (int g = 0; g < GP; ++g) acc[m0 + m][g] += e[m][g];
-}
-
-// One group: quad byte transposes give x[0] = byte s of planes 0-3 and x[1] = planes
-// 4-7 (an 8x8 bit block: 8 planes x 8 tokens); the bit transpose turns byte m into
-// token m's 8-plane pattern; then the table lookups.
-template <int GP>
-__device__ __forceinline__ void process_group(const uint32_t (&w)[2], int s, const float *lg,
-                                              float (&acc)[kTokensPerLane][GP]) {
-    uint32_t x[2];
-    x[0] = quad_byte_transpose(w[0], s);
-    x[1] = quad_byte_transpose(w[1], s);
-    transpose8x8(x[0], x[1]);
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t mask = 0x01010101u << m;
+            const long b = (long)(((uint64_t)(x[pos][1] & mask) << 32) | (x[pos][0] & mask));
 #pragma unroll
-    for (int m0 = 0; m0 < kTokensPerLane; m0 += kInflight) lookup_add<GP>(x, m0, lg, acc);
+            for (int set = 0; set < QS; ++set) {
+                const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[pos][m][set];
+                acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[set], b, c, 0, 0, 0);
+            }
+        }
+    }
 }
 
-// Issues this lane's two plane-word loads of group gi (row offsets of the batch's planes
-// are staged in LDS, in words).
-__device__ __forceinline__ void issue_group(const uint32_t *lane_base, const uint64_t *lrow,
-                                            int gi, int s, uint32_t (&w)[2]) {
-    const uint64_t r0 = lrow[gi * kGroupBits + s];
-    const uint64_t r1 = lrow[gi * kGroupBits + s + 4];
-    w[0] = lane_base[r0];
-    w[1] = lane_base[r1];
+// score = C + (D0 + 256 D1 + 65536 (D2 + 256 D3)) * S / (byte value of bit m); the
+// digit sums of a head with at most 480 planes fit D0 + 256 D1 in int32.
+template <int QS>
+__device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const float (&Cq)[QS],
+                                              const float (&Sq)[QS], bool small, int G, int jq,
+                                              int s, int wi, int n, float *hscores) {
+#pragma unroll
+    for (int set = 0; set < QS; ++set) {
+        const int g = 4 * set + jq;
+        if (g >= G) continue;
+        float *row = hscores + (size_t)g * n;
+#pragma unroll
+        for (int pos = 0; pos < 2; ++pos) {
+            float v[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const v4i d = acc[pos][m][set];
+                const float lo = small ? (float)(d[0] + d[1] * 256)
+                                       : fmaf((float)d[1], 256.0f, (float)d[0]);
+                const float hi = (float)(d[2] + d[3] * 256);
+                const float f = fmaf(hi, 65536.0f, lo);
+                const float mult = m < 7 ? Sq[set] * (1.0f / (float)(1 << m))
+                                         : Sq[set] * (-1.0f / 128.0f);
+                v[m] = fmaf(f, mult, Cq[set]);
+            }
+            const int tok = (wi + pos) * 32 + 8 * s;
+            if ((n & 3) == 0 && tok + 8 <= n) {
+                *reinterpret_cast<float4 *>(row + tok) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(row + tok + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if (tok + m < n) row[tok + m] = v[m];
+            }
+        }
+    }
 }
 
-template <int GP>
-__global__ __launch_bounds__(kScanThreads) void k_scan_main(
-    const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H,
-    int tiles_per_head, const char *__restrict__ ws, float *__restrict__ scores) {
-    extern __shared__ float4 lds_v4[];  // 16-byte aligned: tables, then plane rows
-    constexpr int kBatchGroups = kLdsBudget / (kLutEntries * GP * (int)sizeof(float));
-    float *lds = reinterpret_cast<float *>(lds_v4);
-    uint64_t *lrow =
-        reinterpret_cast<uint64_t *>(lds_v4 + kBatchGroups * kLutEntries * GP / 4);
+// Global -> LDS copy of 16 bytes a lane: lane l's bytes land at dst + 16 l (dst is the
+// same for the whole wave).  Written as inline assembly so that the compiler's own wait
+// insertion does not treat every later LDS read as depending on it (it cannot tell the
+// tiles apart); the tile reads wait for it explicitly (wait_vm).
+__device__ __forceinline__ void copy16_to_lds(const uint32_t *src, char *dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src), "s"(m0)
+                     : "memory", "m0");
+}
+
+// Wait until at most `later` of this wave's vector memory operations are outstanding.
+__device__ __forceinline__ void wait_vm(int later) {
+    // vmcnt lives in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at "any"
+    switch (later) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    }
+}
+
+// Work split.  The (head, super-step) pairs of a launch are numbered head-major;
+// workgroup w takes a run of `run` consecutive ones.  With `flat`, runs are cut without
+// regard to heads (one run per resident workgroup; a run is at most one head long, so
+// it touches at most two heads); otherwise a run never leaves its head.
+struct ScanSplit {
+    int nss;           // super-steps per head
+    int run;           // super-steps per workgroup
+    int wgs_per_head;  // !flat: workgroups per head
+    int flat;
+};
+
+template <int QS>
+__device__ __forceinline__ void load_head_consts(const ScanMeta *meta, int G, int jq,
+                                                 float (&C)[QS], float (&S)[QS]) {
+#pragma unroll
+    for (int set = 0; set < QS; ++set) {
+        const int g = 4 * set + jq;
+        C[set] = g < G ? meta->C[g] : 0.0f;
+        S[set] = g < G ? meta->S[g] : 0.0f;
+    }
+}
+
+template <int QS, bool kWide>
+__global__ __launch_bounds__(kScanThreads)
+__attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) void k_scan_main(
+    const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H, ScanSplit sp,
+    const char *__restrict__ ws, float *__restrict__ scores) {
+    extern __shared__ uint4 lds_u4[];
+    char *lds = reinterpret_cast<char *>(lds_u4);
+    // per head slot: MFMA A operands [K-block][lane][QS] (8 bytes), then the word offsets
+    // of the K-block's 32 rows [K-block][32]; then the tile ring
+    const size_t head_bytes = lds_head_bytes<QS>();
+    char *tiles = lds + 2 * head_bytes;
+    const int nss = sp.nss;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lb / tiles_per_head, tile = lb - h * tiles_per_head;
-    const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(ws + (size_t)h * kMetaBytes);
-    const float *lut = reinterpret_cast<const float *>(
-        ws + (size_t)H * kMetaBytes +
-        (size_t)h * kMaxGroups * kLutEntries * GP * sizeof(float));
-    // clamped so that any workspace content keeps every read inside this head's data
-    const int ngroups = min(max(meta->n_groups, 0), kMaxGroups);
-    const uint32_t *pids = meta->plane;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = lane & 3;  // quad position: byte of the word = tokens 8s .. 8s+7
-    const int W = (n + 31) >> 5;
-    const int gw = tile * kTileWords + wave * kWordsPerWave + (lane >> 2);
-    const int gwc = min(gw, W - 1);  // lanes past the end re-read the last word
-    const uint32_t *lane_base = planes + (size_t)h * kMaxPlanesPerHead * word_stride + gwc;
-
-    float acc[kTokensPerLane][GP];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        const float c0 = g < G ? meta->C[g] : 0.0f;
-#pragma unroll
-        for (int m = 0; m < kTokensPerLane; ++m) acc[m][g] = c0;
+    long a, b;  // this workgroup's run of (head, super-step) pairs
+    if (sp.flat) {
+        a = (long)lb * sp.run;
+        b = min(a + (long)sp.run, (long)H * nss);
+    } else {
+        const int h = lb / sp.wgs_per_head, c = lb - h * sp.wgs_per_head;
+        a = (long)h * nss + (long)c * sp.run;
+        b = min(a + (long)sp.run, (long)(h + 1) * nss);
     }
-
-    for (int gb0 = 0; gb0 < ngroups; gb0 += kBatchGroups) {
-        const int gcount = min(kBatchGroups, ngroups - gb0);
-        __syncthreads();  // the previous batch's tables are no longer read
-        {
-            const float4 *src =
-                reinterpret_cast<const float4 *>(lut + (size_t)gb0 * kLutEntries * GP);
-            const int nvec = gcount * kLutEntries * GP / 4;
-            for (int e = tid; e < nvec; e += kScanThreads) lds_v4[e] = src[e];
-            for (int e = tid; e < gcount * kGroupBits; e += kScanThreads)
-                lrow[e] = (uint64_t)(pids[gb0 * kGroupBits + e] & (kMaxPlanesPerHead - 1)) *
-                          (uint64_t)word_stride;
-        }
-        __syncthreads();
-        uint32_t buf[kPrefetch][2];
+    const int h0 = (int)(a / nss);
+    const int h1 = (int)((b - 1) / nss);          // h0 or h0 + 1
+    const long h1start = (long)(h0 + 1) * nss;    // first super-step of slot 1 (head h1)
+    const ScanMeta *meta0 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h0 * kMetaBytes);
+    const ScanMeta *meta1 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h1 * kMetaBytes);
+    // clamped so that any workspace content keeps every read inside the head's data
+    const int nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);
+    const int nkb1 = min(max(meta1->n_kblocks, 1), kMaxKBlocks);
+    const int tid = threadIdx.x;
 #pragma unroll
-        for (int u = 0; u < kPrefetch; ++u) issue_group(lane_base, lrow, min(u, gcount - 1), s, buf[u]);
-        for (int gi = 0; gi < gcount; gi += kPrefetch) {
-#pragma unroll
-            for (int u = 0; u < kPrefetch; ++u) {
-                if (gi + u < gcount)
-                    process_group<GP>(buf[u], s, lds + (gi + u) * kLutEntries * GP, acc);
-                issue_group(lane_base, lrow, min(gi + u + kPrefetch, gcount - 1), s, buf[u]);
+    for (int k = 0; k < 2; ++k) {
+        if (k && h1 == h0) break;
+        const int hk = k ? h1 : h0, nk = k ? nkb1 : nkb0;
+        const uint4 *grec = reinterpret_cast<const uint4 *>(
+            ws + (size_t)H * kMetaBytes + (size_t)hk * kMaxKBlocks * 64 * 16 * QS);
+        uint2 *la = reinterpret_cast<uint2 *>(lds + k * head_bytes);
+        uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + k * head_bytes +
+                                                      (size_t)kMaxKBlocks * 64 * QS * 8);
+        for (int e = tid; e < nk * 64; e += kScanThreads) {
+            const uint4 r = grec[(size_t)e * QS];
+            la[e * QS] = make_uint2(r.z, r.w);
+            if constexpr (QS == 2) {
+                const uint4 r2 = grec[(size_t)e * QS + 1];
+                la[e * QS + 1] = make_uint2(r2.x, r2.y);
+            }
+            const int ln = e & 63;
+            if ((ln & 15) < 4) {  // lane 16*kb + s names planes s and s+4 of group kb
+                const int row = (e >> 6) * 32 + 8 * (ln >> 4) + (ln & 3);
+                lrow[row] = r.x < (uint32_t)kMaxPlanesPerHead
+                                ? (kWide ? r.x : r.x * (uint32_t)word_stride) : kNoRow;
+                lrow[row + 4] = r.y < (uint32_t)kMaxPlanesPerHead
+                                    ? (kWide ? r.y : r.y * (uint32_t)word_stride) : kNoRow;
             }
         }
     }
+    __syncthreads();
 
-    // Scores leave through LDS so that every store instruction writes 1 KB of one row:
-    // each wave stages its 512 tokens for two queries at a time in its own 4 KB.
-    __syncthreads();  // all table reads of the workgroup are done
-    float *stage = lds + wave * 2 * 512;
-    const int wtok0 = (tile * kTileWords + wave * kWordsPerWave) * 32;  // wave's first token
-    const int pos = (lane >> 2) * 32 + s * kTokensPerLane;             // lane's first token
-#pragma unroll
-    for (int g0 = 0; g0 < GP; g0 += 2) {
-        if (g0 >= G) break;
-#pragma unroll
-        for (int gg = 0; gg < 2 && g0 + gg < GP; ++gg) {
-            float *d = stage + gg * 512 + pos;
-            *reinterpret_cast<float4 *>(d) =
-                make_float4(acc[0][g0 + gg], acc[1][g0 + gg], acc[2][g0 + gg], acc[3][g0 + gg]);
-            *reinterpret_cast<float4 *>(d + 4) =
-                make_float4(acc[4][g0 + gg], acc[5][g0 + gg], acc[6][g0 + gg], acc[7][g0 + gg]);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4, kbq = lane >> 4;
+    const size_t head_words = (size_t)kMaxPlanesPerHead * word_stride;
+    float C0[QS], S0[QS], C1[QS], S1[QS];
+    load_head_consts<QS>(meta0, G, jq, C0, S0);
+    load_head_consts<QS>(meta1, G, jq, C1, S1);
+    const bool small = max(nkb0, nkb1) < kMaxKBlocks;
+    const long c0 = min(b, h1start) - a;  // super-steps of head h0
+    const int nitems = (int)(c0 * nkb0 + (b - a - c0) * nkb1);
+
+    // copy engine: item fi = (super-step iss, K-block ikb); this lane moves chunk
+    // (lane & 7) ^ (2i & 6) of row i = lane >> 3 of group `wave`
+    long iss = a;
+    int ikb = 0, fi = 0;
+    const int crow = lane >> 3;
+    const int cchunk = (lane & 7) ^ ((2 * crow) & 6);
+    auto issue = [&]() {
+        const int k = iss >= h1start ? 1 : 0;
+        const int hh = k ? h1 : h0;
+        const uint32_t *lrow = reinterpret_cast<const uint32_t *>(
+            lds + k * head_bytes + (size_t)kMaxKBlocks * 64 * QS * 8);
+        uint32_t row = lrow[ikb * 32 + 8 * wave + crow];
+        int word = (int)(iss - (long)hh * nss) * kSuperWords + 4 * cchunk;
+        if (row == kNoRow || word >= word_stride) {  // nothing to read: any valid chunk
+            row = 0;
+            word = 0;
         }
-        __builtin_amdgcn_wave_barrier();  // the wave's staged rows are complete
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-            const int g = g0 + gg;
-            if (g >= G) break;
-            float *row = scores + ((size_t)h * G + g) * n;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int t = half * 256 + lane * 4;  // token within the wave's 512
-                const float4 v = *reinterpret_cast<const float4 *>(stage + gg * 512 + t);
-                const int tok = wtok0 + t;
-                if (tok + 4 <= n && (n & 3) == 0) {
-                    *reinterpret_cast<float4 *>(row + tok) = v;
-                } else {
-                    if (tok < n) row[tok] = v.x;
-                    if (tok + 1 < n) row[tok + 1] = v.y;
-                    if (tok + 2 < n) row[tok + 2] = v.z;
-                    if (tok + 3 < n) row[tok + 3] = v.w;
-                }
-            }
+        const uint32_t *src = planes + (size_t)hh * head_words +
+                              (kWide ? (size_t)row * (size_t)word_stride : (size_t)row) + word;
+        char *dst = tiles + (fi % kTiles) * kTileBytes + wave * kTileKbBytes;
+        copy16_to_lds(src, dst);
+        ++fi;
+        if (++ikb == (k ? nkb1 : nkb0)) {
+            ikb = 0;
+            ++iss;
         }
-        __builtin_amdgcn_wave_barrier();  // reads done before the next pair is staged
+    };
+    for (int u = 0; u < kTiles - 1; ++u)
+        if (fi < nitems) issue();
+
+    v4i acc[2][8][QS];
+    long pss = a;
+    int pkb = 0;  // item being used
+    const int rchunk = 2 * wave + (wq >> 1);  // operand chunk and half of this lane
+    const int rhalf = 8 * (wq & 1);
+    for (int f = 0; f < nitems; ++f) {
+        wait_vm(fi - f - 1);  // this wave's copy of item f has landed
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; tile f-1 is free again
+        __asm__ volatile("" ::: "memory");
+        if (fi < nitems) issue();
+        const int k = pss >= h1start ? 1 : 0;
+        const char *t = tiles + (f % kTiles) * kTileBytes + kbq * kTileKbBytes;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(t + 16 * tile_slot(s, rchunk) + rhalf);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(t + 16 * tile_slot(s + 4, rchunk) + rhalf);
+        const uint2 *la = reinterpret_cast<const uint2 *>(lds + k * head_bytes) +
+                          (size_t)(pkb * 64 + lane) * QS;
+        long A[QS];
+#pragma unroll
+        for (int set = 0; set < QS; ++set) {
+            const uint2 av = la[set];
+            A[set] = (long)(((uint64_t)av.y << 32) | av.x);
+        }
+        const uint32_t w[2][2] = {{lo.x, lo.y}, {hi.x, hi.y}};
+        if (pkb == 0) mma_kblock<QS, true>(w, A, s, acc);
+        else mma_kblock<QS, false>(w, A, s, acc);
+        if (++pkb == (k ? nkb1 : nkb0)) {
+            const int hh = k ? h1 : h0;
+            const int wi = ((int)(pss - (long)hh * nss) * 4 + wave) * 8 + 2 * wq;
+            combine_store<QS>(acc, k ? C1 : C0, k ? S1 : S0, small, G, jq, s, wi, n,
+                              scores + (size_t)hh * G * n);
+            pkb = 0;
+            ++pss;
+        }
     }
 }
 
-template <int GP>
-hipError_t launch_main_gp(const fathom_store &st, int G, float *scores, const char *ws,
+// Resident workgroups of a kernel instance over the device (asked once per device).
+template <int QS, bool kWide>
+int resident_slots() {
+    static std::mutex mu;
+    static int slots[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!slots[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_scan_main<QS, kWide>,
+                                                         kScanThreads,
+                                                         scan_lds_bytes<QS>()) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess)
+            return 0;
+        slots[dev] = std::max(1, per_cu) * std::max(1, cus);
+    }
+    return slots[dev];
+}
+
+template <int QS, bool kWide>
+hipError_t launch_main_qs(const fathom_store &st, int G, float *scores, const char *ws,
                           hipStream_t s) {
     const int W = (st.n_tokens + 31) >> 5;
-    const int tiles = (W + kTileWords - 1) / kTileWords;
-    const int nblocks = st.n_heads * tiles;
-    constexpr int kBatchGroups = kLdsBudget / (kLutEntries * GP * (int)sizeof(float));
-    const size_t lds = (size_t)kBatchGroups * kLutEntries * GP * sizeof(float) +
-                       (size_t)kBatchGroups * kGroupBits * sizeof(uint64_t);
-    hipLaunchKernelGGL(k_scan_main<GP>, dim3(nblocks), dim3(kScanThreads), lds, s,
-                       st.planes, st.n_tokens, st.word_stride, G, st.n_heads, tiles, ws,
-                       scores);
+    ScanSplit sp;
+    sp.nss = (W + kSuperWords - 1) / kSuperWords;
+    const long total = (long)st.n_heads * sp.nss;
+    int slots = resident_slots<QS, kWide>();
+    if (slots <= 0) slots = 1024;
+    slots *= FATHOM_SCAN_ROUNDS;
+    sp.run = (int)std::max(1L, (total + slots - 1) / slots);
+    sp.flat = sp.run <= sp.nss;
+    if (!sp.flat) sp.run = sp.nss;
+    sp.wgs_per_head = (sp.nss + sp.run - 1) / sp.run;
+    const long nblocks = sp.flat ? (total + sp.run - 1) / sp.run
+                                 : (long)st.n_heads * sp.wgs_per_head;
+    hipLaunchKernelGGL((k_scan_main<QS, kWide>), dim3((unsigned)nblocks), dim3(kScanThreads),
+                       scan_lds_bytes<QS>(), s, st.planes, st.n_tokens, st.word_stride, G,
+                       st.n_heads, sp, ws, scores);
     return hipGetLastError();
+}
+
+template <int QS>
+hipError_t launch_main_q(const fathom_store &st, int G, float *scores, const char *ws,
+                         hipStream_t s) {
+    // word offsets of a head's 512 rows fit 32 bits (below the no-row marker)?
+    const bool wide = (uint64_t)kMaxPlanesPerHead * (uint64_t)st.word_stride >= 0xFFFFFFFFull;
+    return wide ? launch_main_qs<QS, true>(st, G, scores, ws, s)
+                : launch_main_qs<QS, false>(st, G, scores, ws, s);
 }
 
 }  // namespace
@@ -332,24 +514,20 @@ hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     const dim3 grid(st.n_heads), block(256);
-    switch (padded_g(G)) {
-    case 1: hipLaunchKernelGGL(k_scan_prepare<1>, grid, block, 0, s, q, depth, st.scale, st.zero, st.n_heads, G, w); break;
-    case 2: hipLaunchKernelGGL(k_scan_prepare<2>, grid, block, 0, s, q, depth, st.scale, st.zero, st.n_heads, G, w); break;
-    case 4: hipLaunchKernelGGL(k_scan_prepare<4>, grid, block, 0, s, q, depth, st.scale, st.zero, st.n_heads, G, w); break;
-    default: hipLaunchKernelGGL(k_scan_prepare<8>, grid, block, 0, s, q, depth, st.scale, st.zero, st.n_heads, G, w); break;
-    }
+    if (query_sets(G) == 1)
+        hipLaunchKernelGGL(k_scan_prepare<1>, grid, block, 0, s, q, depth, st.scale, st.zero,
+                           st.n_heads, G, w);
+    else
+        hipLaunchKernelGGL(k_scan_prepare<2>, grid, block, 0, s, q, depth, st.scale, st.zero,
+                           st.n_heads, G, w);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
                             hipStream_t s) {
     const char *w = static_cast<const char *>(ws);
-    switch (padded_g(G)) {
-    case 1: return launch_main_gp<1>(st, G, scores, w, s);
-    case 2: return launch_main_gp<2>(st, G, scores, w, s);
-    case 4: return launch_main_gp<4>(st, G, scores, w, s);
-    default: return launch_main_gp<8>(st, G, scores, w, s);
-    }
+    return query_sets(G) == 1 ? launch_main_q<1>(st, G, scores, w, s)
+                              : launch_main_q<2>(st, G, scores, w, s);
 }
 
 }  // namespace fathom

@@ -150,7 +150,7 @@ class Store:
     def empty(H: int, n: int, device, word_stride: int | None = None, planes=None) -> "Store":
         """Allocate the store's buffers; `planes` may be supplied (e.g. pinned host)."""
         import torch
-        W = (n + 31) // 32 if word_stride is None else word_stride
+        W = ((n + 31) // 32 + 3) // 4 * 4 if word_stride is None else word_stride
         if planes is None:
             planes = torch.empty((H, D, PLANES, W), dtype=torch.int32, device=device)
         kw = dict(dtype=torch.float32, device=device)

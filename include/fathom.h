@@ -74,7 +74,8 @@ typedef struct fathom_store {
     int32_t n_heads;     /* H */
     int32_t n_tokens;    /* n, >= 1 */
     int32_t d;           /* channels, must be FATHOM_D */
-    int32_t word_stride; /* uint32 words per plane row, >= ceil(n/32) */
+    int32_t word_stride; /* uint32 words per plane row: >= ceil(n/32) and a multiple
+                            of 4 (rows start on 16-byte boundaries) */
     uint32_t *planes;
     float *scale;
     float *zero;

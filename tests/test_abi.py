@@ -41,8 +41,8 @@ def test_version_and_status_strings():
 
 
 def _st(H=2, n=100, d=128, stride=None, planes=FAKE):
-    return F.fathom_store(H, n, d, (n + 31) // 32 if stride is None else stride, planes,
-                          FAKE, FAKE, FAKE)
+    return F.fathom_store(H, n, d, ((n + 31) // 32 + 3) // 4 * 4 if stride is None else stride,
+                          planes, FAKE, FAKE, FAKE)
 
 
 def test_store_checks():
@@ -54,6 +54,7 @@ def test_store_checks():
     assert r(_st(n=0)) == F.ERR_INVALID_ARG
     assert r(_st(H=0)) == F.ERR_INVALID_ARG
     assert r(_st(stride=3)) == F.ERR_INVALID_ARG          # < ceil(100/32)
+    assert r(_st(stride=6)) == F.ERR_INVALID_ARG          # rows not 16-byte multiples
     assert r(_st(planes=None)) == F.ERR_INVALID_ARG
     assert r(_st(planes=FAKE + 4)) == F.ERR_INVALID_ARG   # planes must be 16-aligned
 
@@ -128,9 +129,9 @@ def test_stream_read_and_host_alloc_checks():
 
 
 def test_workspace_formulas():
-    # scan: 4 KiB meta + 64 groups x 256 entries x G padded to 1/2/4/8 floats, per head
-    for G, gp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
-        assert F.workspace_size(F.OP_SCAN, 3, G) == 3 * (4096 + 64 * 256 * gp * 4)
+    # scan: 4 KiB meta + 16 K-blocks x 64 lanes x 16 bytes per set of 4 queries, per head
+    for G, qs in [(1, 1), (2, 1), (3, 1), (4, 1), (5, 2), (8, 2)]:
+        assert F.workspace_size(F.OP_SCAN, 3, G) == 3 * (4096 + 16 * 64 * 16 * qs)
     # top-k: rows that fit one chunk need nothing
     assert F.workspace_size(F.OP_TOPK, 1152, 1, 32768, 512) == 0
     # 1M tokens: 32 chunks x 512 candidates x (4 + 4) bytes per row, one level

@@ -22,13 +22,13 @@ pytestmark = pytest.mark.gpu
 # store build
 # ---------------------------------------------------------------------------------
 @pytest.mark.parametrize("H,n,extra", [(1, 4096, 0), (3, 1013, 0), (2, 33, 0), (1, 1, 0),
-                                       (2, 5000, 3), (1, 70, 5), (4, 2048, 0),
-                                       (2, 64 * 9 + 7, 1)])
+                                       (2, 5000, 4), (1, 70, 8), (4, 2048, 0),
+                                       (2, 64 * 9 + 7, 4)])
 def test_quantize_store_matches_oracle(H, n, extra):
     print(f"[quantize] H={H} n={n} extra={extra}", flush=True)
     keys = synth.keys_np(1, 50, range(H), n)
     W = (n + 31) // 32
-    st, _ = store_from_keys(keys, word_stride=W + extra)
+    st, _ = store_from_keys(keys, word_stride=(W + 3) // 4 * 4 + extra)
     s, z, codes = oracle.quantize(keys)
     ref_planes = oracle.pack_planes(codes)
     got = u32(st.planes)
@@ -45,7 +45,10 @@ def test_quantize_constant_channels():
     keys[1, :, 0] = 0.0
     st, _ = store_from_keys(keys)
     s, z, codes = oracle.quantize(keys)
-    assert np.array_equal(u32(st.planes), oracle.pack_planes(codes))
+    ref = oracle.pack_planes(codes)
+    got = u32(st.planes)
+    assert np.array_equal(got[..., :ref.shape[-1]], ref)
+    assert (got[..., ref.shape[-1]:] == 0).all()
     assert st.scale.cpu().numpy()[0, 5] == 0 and st.var.cpu().numpy()[0, 5] == 0
 
 
@@ -121,6 +124,49 @@ def test_scan_matches_oracle(H, G, n, kind):
     torch.cuda.synchronize()
     ref = oracle.scores(codes, s, z, depth, q)
     check_rows(scores.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("kind", ["plan92", "random"])
+def test_scan_long_runs_sampled_heads(kind):
+    """72 heads x 32768 tokens: the scan's workgroups take runs of several 256-token
+    steps that straddle head boundaries (with different plane counts per head under
+    random depths); sampled heads, boundary neighbours included, against the oracle."""
+    torch = torch_cuda()
+    H, G, n = 72, 4, 32768
+    print(f"[scan-long] H={H} G={G} n={n} {kind}", flush=True)
+    keys = synth.keys_torch(0, 70, range(H), n, "cuda")
+    st = F.Store.empty(H, n, "cuda")
+    F.fathom_quantize_store(keys, st)
+    del keys
+    q = synth.queries_np(0, 70, range(H), G)
+    q_t = to_dev(q)
+    if kind == "plan92":
+        depth_t = F.fathom_plan(st, q_t, 92)
+    else:
+        depth_t = to_dev(np.random.default_rng(7).integers(0, 5, (H, 128)).astype(np.uint8))
+    scores = F.fathom_scan(st, q_t, depth_t)
+    torch.cuda.synchronize()
+    depth = depth_t.cpu().numpy()
+    for h in [0, 1, 35, 36, 70, 71]:
+        kh = synth.keys_torch(0, 70, [h], n, "cuda")[0].cpu().numpy()
+        s, z, codes = oracle.quantize(kh[None])
+        if kind == "plan92":
+            assert np.array_equal(depth[h], oracle.plan(q[h][None], oracle.channel_var(codes, s), 92)[0])
+        ref = oracle.scores(codes, s, z, depth[h][None], q[h][None])
+        check_rows(scores[h].cpu().numpy(), ref[0])
+
+
+@pytest.mark.parametrize("H,n", [(600, 100), (37, 300)])
+def test_scan_many_small_heads(H, n):
+    """Heads shorter than one workgroup's run: runs are cut at head boundaries."""
+    torch = torch_cuda()
+    keys, q, _, _ = inputs(71, H, 4, n)
+    st, _ = store_from_keys(keys)
+    s, z, codes = oracle.quantize(keys)
+    depth = np.random.default_rng(H).integers(0, 5, (H, 128)).astype(np.uint8)
+    scores = F.fathom_scan(st, to_dev(q), to_dev(depth))
+    torch.cuda.synchronize()
+    check_rows(scores.cpu().numpy(), oracle.scores(codes, s, z, depth, q))
 
 
 def test_scan_prepared_equals_scan():
@@ -267,7 +313,7 @@ def test_host_resident_store_and_rows_match_hbm():
     H, G, n, k = 2, 4, 5000, 128
     keys, q, K, V = inputs(90, H, G, n)
     st_d, _ = store_from_keys(keys)
-    W = (n + 31) // 32
+    W = ((n + 31) // 32 + 3) // 4 * 4
     pinned = torch.empty((H, 128, 4, W), dtype=torch.int32, pin_memory=True)
     st_h, _ = store_from_keys(keys, planes=pinned)
     assert torch.equal(st_d.planes.cpu(), st_h.planes.cpu())
