@@ -165,7 +165,7 @@ def main():
     traffic = load_traffic(scan_bytes)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "k_scan_main<4>",
+                "traffic": traffic, "kernel": "k_scan_main<1,false>",
                 "algorithmic_bytes_per_launch": int(scan_bytes)}
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------

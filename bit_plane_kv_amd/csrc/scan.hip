@@ -155,25 +155,32 @@ __global__ __launch_bounds__(256) void k_scan_prepare(
 // ---------------------------------------------------------------------------------
 // main scan
 // ---------------------------------------------------------------------------------
-// Shape.  A workgroup of 4 waves scores one super-step -- 1024 tokens (32 words) of one
-// head -- at a time, K-block by K-block (4 groups of 8 planes).  For each K-block, wave
-// kb copies the 8 rows of group kb, 128 contiguous bytes (whole cache lines) each,
-// straight from global memory into an LDS tile, 16 bytes a lane; after a barrier, wave
-// v takes tokens 256v .. 256v+255 (words 8v .. 8v+7) of all 32 rows from the tile:
-// lane 16*kb + 4*w + s reads words 8v+2w and 8v+2w+1 of planes s and s+4 of group kb.
-// A byte transpose across the quad then gives lane s byte s (8 tokens) of the group's 8
-// planes, so bit m of byte i is plane i's bit of token 8s + m; masking bit m of every
-// byte makes the MFMA column of token 8s + m (byte values 0 / 2^m, and -128 for m = 7,
-// divided out in the combine).  The MFMA output lane 16*j + 4*w + s then holds query
-// j's 4 digit sums for that token.  kTiles tiles rotate, so the copies of the next
-// K-blocks are in flight while one is used.
-constexpr int kScanThreads = 256;
-constexpr int kSuperWords = 32;       // words per super-step
-constexpr int kTileKbBytes = 1152;    // a group's 8 rows x 128 bytes; the extra 128 bytes
-                                      // start odd groups half-way round the LDS banks
-constexpr int kTileBytes = 4 * kTileKbBytes;
+// Shape.  A workgroup of kWaves waves scores one super-step -- 256 tokens (8 words) per
+// wave, 8*kWaves words of one head -- at a time, K-pair by K-pair: 8 groups of 8 planes,
+// the K of one 16x16x64 i8 MFMA.  For each K-pair the waves copy its 64 plane rows,
+// 32*kWaves contiguous bytes (whole cache lines) each, straight from global memory
+// into an LDS tile, 16 bytes a lane; after a barrier, wave v takes words 8v .. 8v+7 of
+// all 64 rows from the tile: lane 16*q + 4*w + s reads words 8v+2w and 8v+2w+1 of
+// planes s and s+4 of groups q and q+4.  A byte transpose across the quad gives lane s
+// byte s (8 tokens) of a group's 8 planes, so bit m of byte i is plane i's bit of token
+// 8s + m; masking bit m of every byte makes the MFMA column of token 8s + m (byte values
+// 0 / 2^m, and -128 for m = 7, divided out in the combine).  The MFMA output lane
+// 16*j + 4*w + s then holds query j's 4 digit sums for that token.  kTiles tiles
+// rotate, so the copies of the next K-pairs are in flight while one is used.
+#ifndef FATHOM_SCAN_WAVES
+#define FATHOM_SCAN_WAVES 8
+#endif
+constexpr int kWaves = FATHOM_SCAN_WAVES;     // waves per workgroup (4, 8 or 16)
+static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "workgroup shape");
+constexpr int kScanThreads = 64 * kWaves;
+constexpr int kSuperWords = 8 * kWaves;       // words per super-step
+constexpr int kRowChunks = kSuperWords / 4;   // 16-byte chunks of a row per super-step
+constexpr int kCopyRows = 64 / kRowChunks;    // rows one copy instruction moves
+constexpr int kGroupBytes = 8 * 16 * kRowChunks + 128;  // a group's 8 rows; the extra
+                                      // 128 bytes start odd groups half-way round the banks
+constexpr int kTileBytes = 8 * kGroupBytes;   // one K-pair
 #ifndef FATHOM_SCAN_TILES
-#define FATHOM_SCAN_TILES 4
+#define FATHOM_SCAN_TILES 3
 #endif
 #ifndef FATHOM_SCAN_ROUNDS
 #define FATHOM_SCAN_ROUNDS 1
@@ -182,21 +189,24 @@ constexpr int kTileBytes = 4 * kTileKbBytes;
 #define FATHOM_SCAN_WAVES_PER_EU 4
 #endif
 constexpr int kTiles = FATHOM_SCAN_TILES;
-static_assert(kTiles >= 2 && kTiles <= 8, "tile ring");
+static_assert(kTiles >= 2 && kTiles <= 6, "tile ring");
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 
-// 16-byte LDS slot of row i (0..7), chunk c (4 words, 0..7) in a group's region; the
-// xor spreads the operand reads (chunk 2v + w/2 of rows s = 0..3) over all banks.
-__device__ __forceinline__ int tile_slot(int i, int c) { return 8 * i + (c ^ ((2 * i) & 6)); }
+// 16-byte LDS slot of row i (0..7), chunk c in a group's region; the xor spreads the
+// operand reads (chunk 2v + w/2 of rows s = 0..3) over all banks.
+__device__ __forceinline__ int tile_slot(int i, int c) {
+    return kRowChunks * i + (c ^ (2 * (i & 3)));
+}
 
+// LDS per head slot: A operand halves [K-block of 4 groups][lane][QS] (8 bytes), then
+// the word offsets of each K-block's 32 rows [K-block][32]; then the tile ring.
 template <int QS>
-__device__ __forceinline__ size_t lds_head_bytes() {
+constexpr size_t lds_head_bytes() {
     return (size_t)kMaxKBlocks * 64 * QS * 8 + (size_t)kMaxKBlocks * 32 * 4;
 }
 template <int QS>
-size_t scan_lds_bytes() {
-    return 2 * ((size_t)kMaxKBlocks * 64 * QS * 8 + (size_t)kMaxKBlocks * 32 * 4) +
-           (size_t)kTiles * kTileBytes;
+constexpr size_t scan_lds_bytes() {
+    return 2 * lds_head_bytes<QS>() + (size_t)kTiles * kTileBytes;
 }
 
 // Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
@@ -209,25 +219,30 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t m, int s) {
     return __builtin_amdgcn_perm(q, a, (s & 1) ? 0x03070105u : 0x06020400u);
 }
 
+// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h.
+// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h;
+// hi_mask = 0 when the upper 4 groups do not exist (their operand bytes are zero).
 template <int QS, bool kFirst>
-__device__ __forceinline__ void mma_kblock(const uint32_t (&w)[2][2], const long (&A)[QS],
-                                           int s, v4i (&acc)[2][8][QS]) {
-    uint32_t x[2][2];
+__device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4i (&A)[QS],
+                                          uint32_t hi_mask, int s, v4i (&acc)[2][8][QS]) {
 #pragma unroll
     for (int pos = 0; pos < 2; ++pos) {
-        x[pos][0] = quad_byte_transpose(w[0][pos], s);  // planes 0-3, byte s
-        x[pos][1] = quad_byte_transpose(w[1][pos], s);  // planes 4-7, byte s
-    }
+        uint32_t x[2][2];  // [half][planes 0-3 / 4-7]
 #pragma unroll
-    for (int pos = 0; pos < 2; ++pos) {
+        for (int h = 0; h < 2; ++h) {
+            x[h][0] = quad_byte_transpose(w[h][0][pos], s);
+            x[h][1] = quad_byte_transpose(w[h][1][pos], s);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint32_t mask = 0x01010101u << m;
-            const long b = (long)(((uint64_t)(x[pos][1] & mask) << 32) | (x[pos][0] & mask));
+            const uint32_t mhi = mask & hi_mask;
+            const v4i b = {(int)(x[0][0] & mask), (int)(x[0][1] & mask), (int)(x[1][0] & mhi),
+                           (int)(x[1][1] & mhi)};
 #pragma unroll
             for (int set = 0; set < QS; ++set) {
                 const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[pos][m][set];
-                acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[set], b, c, 0, 0, 0);
+                acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[set], b, c, 0, 0, 0);
             }
         }
     }
@@ -271,31 +286,15 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
     }
 }
 
-// Global -> LDS copy of 16 bytes a lane: lane l's bytes land at dst + 16 l (dst is the
-// same for the whole wave).  Written as inline assembly so that the compiler's own wait
-// insertion does not treat every later LDS read as depending on it (it cannot tell the
-// tiles apart); the tile reads wait for it explicitly (wait_vm).
-__device__ __forceinline__ void copy16_to_lds(const uint32_t *src, char *dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+// Global -> LDS copy of 16 bytes a lane: lane l's bytes land at LDS byte address
+// m0 + 16 l (m0 the same for the whole wave).  Written as inline assembly so that the
+// compiler's own wait insertion does not treat every later LDS read as depending on it
+// (it cannot tell the tiles apart); the tile reads wait for it explicitly.
+__device__ __forceinline__ void copy16_to_lds(const uint32_t *src, uint32_t m0) {
     __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                      :
-                     : "v"(src), "s"(m0)
+                     : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
                      : "memory", "m0");
-}
-
-// Wait until at most `later` of this wave's vector memory operations are outstanding.
-__device__ __forceinline__ void wait_vm(int later) {
-    // vmcnt lives in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at "any"
-    switch (later) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    }
 }
 
 // Work split.  The (head, super-step) pairs of a launch are numbered head-major;
@@ -327,10 +326,10 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const char *__restrict__ ws, float *__restrict__ scores) {
     extern __shared__ uint4 lds_u4[];
     char *lds = reinterpret_cast<char *>(lds_u4);
-    // per head slot: MFMA A operands [K-block][lane][QS] (8 bytes), then the word offsets
-    // of the K-block's 32 rows [K-block][32]; then the tile ring
-    const size_t head_bytes = lds_head_bytes<QS>();
-    char *tiles = lds + 2 * head_bytes;
+    constexpr size_t kHeadBytes = lds_head_bytes<QS>();
+    constexpr size_t kRowsOff = (size_t)kMaxKBlocks * 64 * QS * 8;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+    const uint32_t tiles_base = lds_base + 2 * (uint32_t)kHeadBytes;
     const int nss = sp.nss;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     long a, b;  // this workgroup's run of (head, super-step) pairs
@@ -343,12 +342,11 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         b = min(a + (long)sp.run, (long)(h + 1) * nss);
     }
     const int h0 = (int)(a / nss);
-    const int h1 = (int)((b - 1) / nss);          // h0 or h0 + 1
-    const long h1start = (long)(h0 + 1) * nss;    // first super-step of slot 1 (head h1)
+    const int h1 = (int)((b - 1) / nss);  // h0 or h0 + 1
     const ScanMeta *meta0 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h0 * kMetaBytes);
     const ScanMeta *meta1 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h1 * kMetaBytes);
     // clamped so that any workspace content keeps every read inside the head's data
-    const int nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);
+    const int nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);  // 4-group K-blocks
     const int nkb1 = min(max(meta1->n_kblocks, 1), kMaxKBlocks);
     const int tid = threadIdx.x;
 #pragma unroll
@@ -357,9 +355,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         const int hk = k ? h1 : h0, nk = k ? nkb1 : nkb0;
         const uint4 *grec = reinterpret_cast<const uint4 *>(
             ws + (size_t)H * kMetaBytes + (size_t)hk * kMaxKBlocks * 64 * 16 * QS);
-        uint2 *la = reinterpret_cast<uint2 *>(lds + k * head_bytes);
-        uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + k * head_bytes +
-                                                      (size_t)kMaxKBlocks * 64 * QS * 8);
+        uint2 *la = reinterpret_cast<uint2 *>(lds + k * kHeadBytes);
+        uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + k * kHeadBytes + kRowsOff);
         for (int e = tid; e < nk * 64; e += kScanThreads) {
             const uint4 r = grec[(size_t)e * QS];
             la[e * QS] = make_uint2(r.z, r.w);
@@ -380,39 +377,50 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     __syncthreads();
 
     const int lane = tid & 63, wave = tid >> 6;
-    const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4, kbq = lane >> 4;
+    const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
     const size_t head_words = (size_t)kMaxPlanesPerHead * word_stride;
     float C0[QS], S0[QS], C1[QS], S1[QS];
     load_head_consts<QS>(meta0, G, jq, C0, S0);
     load_head_consts<QS>(meta1, G, jq, C1, S1);
     const bool small = max(nkb0, nkb1) < kMaxKBlocks;
-    const long c0 = min(b, h1start) - a;  // super-steps of head h0
-    const int nitems = (int)(c0 * nkb0 + (b - a - c0) * nkb1);
+    const int npr0 = (nkb0 + 1) >> 1, npr1 = (nkb1 + 1) >> 1;  // K-pairs per super-step
+    // super-steps of the run, counted from a: [0, h1rel) in head h0, [h1rel, len) in h1
+    const int len = (int)(b - a);
+    const int h1rel = (int)min((long)len, (long)(h0 + 1) * nss - a);
+    const int ss0 = (int)(a - (long)h0 * nss);  // super-step of head h0 at run start
+    const int nitems = h1rel * npr0 + (len - h1rel) * npr1;
 
-    // copy engine: item fi = (super-step iss, K-block ikb); this lane moves chunk
-    // (lane & 7) ^ (2i & 6) of row i = lane >> 3 of group `wave`
-    long iss = a;
-    int ikb = 0, fi = 0;
-    const int crow = lane >> 3;
-    const int cchunk = (lane & 7) ^ ((2 * crow) & 6);
+    // copy engine: item = (super-step, K-pair); per K-pair half (4 groups) this lane
+    // moves chunk c of row r of the half: r = 8*cgrp + crow, c = cchunk
+    const int cgrp = wave / (kWaves / 4);
+    const int crow = (wave % (kWaves / 4)) * kCopyRows + lane / kRowChunks;
+    const int cchunk = (lane % kRowChunks) ^ (2 * (crow & 3));
+    const uint32_t cdst = (uint32_t)(cgrp * kGroupBytes +
+                                     (wave % (kWaves / 4)) * kCopyRows * kRowChunks * 16);
+    int iss = 0, ipr = 0, fi = 0;
     auto issue = [&]() {
-        const int k = iss >= h1start ? 1 : 0;
+        const int k = iss >= h1rel ? 1 : 0;
         const int hh = k ? h1 : h0;
-        const uint32_t *lrow = reinterpret_cast<const uint32_t *>(
-            lds + k * head_bytes + (size_t)kMaxKBlocks * 64 * QS * 8);
-        uint32_t row = lrow[ikb * 32 + 8 * wave + crow];
-        int word = (int)(iss - (long)hh * nss) * kSuperWords + 4 * cchunk;
-        if (row == kNoRow || word >= word_stride) {  // nothing to read: any valid chunk
-            row = 0;
-            word = 0;
+        const int nk = k ? nkb1 : nkb0;
+        const int word = (k ? iss - h1rel : ss0 + iss) * kSuperWords + 4 * cchunk;
+        const uint32_t *lrow =
+            reinterpret_cast<const uint32_t *>(lds + k * kHeadBytes + kRowsOff);
+        const uint32_t *hbase = planes + (size_t)hh * head_words + word;
+        const uint32_t tile = tiles_base + (uint32_t)((fi % kTiles) * kTileBytes) + cdst;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int kb = 2 * ipr + half;
+            const uint32_t row = kb < nk ? lrow[kb * 32 + 8 * cgrp + crow] : kNoRow;
+            // rows not read and chunks past the row all fetch the store's first 16 bytes
+            const bool live = row != kNoRow && word < word_stride;
+            const uint32_t *src =
+                live ? hbase + (kWide ? (size_t)row * (size_t)word_stride : (size_t)row)
+                     : planes;
+            copy16_to_lds(src, tile + (uint32_t)(half * 4 * kGroupBytes));
         }
-        const uint32_t *src = planes + (size_t)hh * head_words +
-                              (kWide ? (size_t)row * (size_t)word_stride : (size_t)row) + word;
-        char *dst = tiles + (fi % kTiles) * kTileBytes + wave * kTileKbBytes;
-        copy16_to_lds(src, dst);
         ++fi;
-        if (++ikb == (k ? nkb1 : nkb0)) {
-            ikb = 0;
+        if (++ipr == (k ? npr1 : npr0)) {
+            ipr = 0;
             ++iss;
         }
     };
@@ -420,37 +428,57 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         if (fi < nitems) issue();
 
     v4i acc[2][8][QS];
-    long pss = a;
-    int pkb = 0;  // item being used
+    int pss = 0, ppr = 0;  // item being used
     const int rchunk = 2 * wave + (wq >> 1);  // operand chunk and half of this lane
     const int rhalf = 8 * (wq & 1);
+    const int qgrp = lane >> 4;               // operand group q (and q + 4)
     for (int f = 0; f < nitems; ++f) {
-        wait_vm(fi - f - 1);  // this wave's copy of item f has landed
+        // this wave's copies of item f have landed (2 copies per later item in flight)
+        if (fi - f - 1 == kTiles - 2) {
+            if constexpr (kTiles == 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+            if constexpr (kTiles == 3) __builtin_amdgcn_s_waitcnt(0x0F72);
+            if constexpr (kTiles == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+            if constexpr (kTiles == 5) __builtin_amdgcn_s_waitcnt(0x0F76);
+            if constexpr (kTiles == 6) __builtin_amdgcn_s_waitcnt(0x0F78);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // ... and every wave's; tile f-1 is free again
         __asm__ volatile("" ::: "memory");
         if (fi < nitems) issue();
-        const int k = pss >= h1start ? 1 : 0;
-        const char *t = tiles + (f % kTiles) * kTileBytes + kbq * kTileKbBytes;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(t + 16 * tile_slot(s, rchunk) + rhalf);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(t + 16 * tile_slot(s + 4, rchunk) + rhalf);
-        const uint2 *la = reinterpret_cast<const uint2 *>(lds + k * head_bytes) +
-                          (size_t)(pkb * 64 + lane) * QS;
-        long A[QS];
+        const int k = pss >= h1rel ? 1 : 0;
+        const int nk = k ? nkb1 : nkb0;
+        const bool hi = 2 * ppr + 1 < nk;  // upper 4 groups of the K-pair exist
+        const char *t = lds + 2 * kHeadBytes + (f % kTiles) * kTileBytes + qgrp * kGroupBytes;
+        uint32_t w[2][2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const char *tg = t + h * 4 * kGroupBytes;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(tg + 16 * tile_slot(s, rchunk) + rhalf);
+            const uint2 up = *reinterpret_cast<const uint2 *>(tg + 16 * tile_slot(s + 4, rchunk) + rhalf);
+            w[h][0][0] = lo.x;
+            w[h][0][1] = lo.y;
+            w[h][1][0] = up.x;
+            w[h][1][1] = up.y;
+        }
+        const uint2 *la = reinterpret_cast<const uint2 *>(lds + k * kHeadBytes);
+        v4i A[QS];
 #pragma unroll
         for (int set = 0; set < QS; ++set) {
-            const uint2 av = la[set];
-            A[set] = (long)(((uint64_t)av.y << 32) | av.x);
+            const uint2 alo = la[((2 * ppr) * 64 + lane) * QS + set];
+            const uint2 ahi = hi ? la[((2 * ppr + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
+            A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
         }
-        const uint32_t w[2][2] = {{lo.x, lo.y}, {hi.x, hi.y}};
-        if (pkb == 0) mma_kblock<QS, true>(w, A, s, acc);
-        else mma_kblock<QS, false>(w, A, s, acc);
-        if (++pkb == (k ? nkb1 : nkb0)) {
+        const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
+        if (ppr == 0) mma_kpair<QS, true>(w, A, hi_mask, s, acc);
+        else mma_kpair<QS, false>(w, A, hi_mask, s, acc);
+        if (++ppr == (k ? npr1 : npr0)) {
             const int hh = k ? h1 : h0;
-            const int wi = ((int)(pss - (long)hh * nss) * 4 + wave) * 8 + 2 * wq;
+            const int wi = ((k ? pss - h1rel : ss0 + pss) * kWaves + wave) * 8 + 2 * wq;
             combine_store<QS>(acc, k ? C1 : C0, k ? S1 : S0, small, G, jq, s, wi, n,
                               scores + (size_t)hh * G * n);
-            pkb = 0;
+            ppr = 0;
             ++pss;
         }
     }
