@@ -182,7 +182,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "Gkeys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8+fp32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "kv_heads_x_layers": H, "queries_per_kv_head": G,
                    "tokens": n, "d": 128, "budget_bits": B, "k": k, "residency": "hbm",

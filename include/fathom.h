@@ -145,20 +145,21 @@ int fathom_plan_fixed(const fathom_store *st, int n_channels, uint8_t *depth,
  *   fathom_plan_fixed); scores [H][G][n] fp32 out.
  * For token i and query g:  score = sum_c q_gc * (z_c + s_c * m_ic), where m_ic is the
  * middle of the 4-bit codes the t_c planes read allow: p * 2^(4-t) + (2^(4-t) - 1)/2
- * with p the t-plane prefix (t = 0 reads nothing: m = 7.5).  fp32 result; the order of
- * the fp32 additions is the library's (it sums plane groups through lookup tables).
+ * with p the t-plane prefix (t = 0 reads nothing: m = 7.5).  fp32 result: the sum over
+ * planes is taken exactly in integers, with each plane's weight q_gc s_c 2^(3-j) held to
+ * 2^-31 of the head's largest weight, then combined with the constant term in fp32.
  * ws: FATHOM_OP_SCAN bytes.  fathom_scan = fathom_scan_prepare + fathom_scan_prepared.
  */
 int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *depth,
                 float *scores, void *ws, size_t ws_bytes, void *stream);
 
-/* First half of fathom_scan: per-head plane list, constant term and lookup tables
- * into ws (one small kernel). */
+/* First half of fathom_scan: per-head plane list, constant terms and the weights of the
+ * planes in matrix-core operand form, into ws (one small kernel). */
 int fathom_scan_prepare(const fathom_store *st, const float *q, int G,
                         const uint8_t *depth, void *ws, size_t ws_bytes, void *stream);
 
-/* Second half of fathom_scan: the plane-reading kernel, using the tables that
- * fathom_scan_prepare left in ws for the same store and G. */
+/* Second half of fathom_scan: the plane-reading kernel, using what fathom_scan_prepare
+ * left in ws for the same store and G. */
 int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
                          size_t ws_bytes, void *stream);
 
