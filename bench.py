@@ -50,7 +50,10 @@ def parse():
     ap.add_argument("--no-host", action="store_true",
                     help="skip the host-resident 1M-token single-layer step")
     ap.add_argument("--host-only", action="store_true",
-                    help="run only the host-resident 1M-token single-layer step")
+                    help="run only the host-resident lines (1M-token single-layer step, "
+                         "link sweep, full-model host-resident scans)")
+    ap.add_argument("--no-host-models", action="store_true",
+                    help="skip the full-model host-resident scans (n = 256k and 1M)")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --kernel: also run a 1 GiB streaming read and a 256 MiB "
                          "copy, whose byte counts scale the profiler's HBM counters")
@@ -73,7 +76,7 @@ def main():
     from bit_plane_kv_amd import synth
 
     if args.host_only:
-        print(json.dumps(host_resident_step(args)), flush=True)
+        print(json.dumps(host_lines(args)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]
@@ -177,7 +180,7 @@ def main():
     if not args.no_host:
         del K, V, st, ws, scores
         torch.cuda.empty_cache()
-        host = host_resident_step(args)
+        host = host_lines(args)
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "Gkeys/s", "n_gpus": 1,
@@ -195,7 +198,7 @@ def main():
                            "winner_rows": int(H * G * k * 512)},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "parity_before_timing": parity,
-        "host_resident_1m_layer_step": host,
+        "host_resident": host,
     }
     print(json.dumps(result), flush=True)
 
@@ -353,7 +356,176 @@ def link_rate(dev, stream, nbytes=1 << 30):
             "L_GBps": round(max(dma, zc), 2)}
 
 
-def host_resident_step(args):
+def host_lines(args):
+    """All host-resident lines: the link rate and its run-length sweep, the 1M-token
+    single-layer step, and (unless --no-host-models) the full-model scans at 256k and
+    1M tokens with the store in pinned host memory."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    L = link_rate(dev, stream)
+    out = {"link": L}
+    try:
+        out["link_run_sweep"] = link_sweep(dev, stream)
+    except Exception as e:
+        out["link_run_sweep"] = {"error": f"{type(e).__name__}: {e}"}
+    out["layer_1m_step"] = host_resident_step(args, L)
+    if not args.no_host_models:
+        for name in ("qwen3_8b_256k_host", "qwen3_8b_1m_host"):
+            try:
+                out[name] = host_model(args, name, L)
+            except Exception as e:  # report, do not lose the other lines
+                out[name] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.empty_cache()
+    return out
+
+
+def link_sweep(dev, stream, total=1 << 28):
+    """Zero-copy reads of pinned host memory in runs of 256 B .. 1 MiB (every other run
+    skipped, `total` bytes read per point), and one DMA call per run for a few lengths
+    (the blog's "One measurement worth carrying around"), GB/s."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    h = torch.empty(2 * total, dtype=torch.uint8, pin_memory=True)
+    h.fill_(3)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    rows = []
+    for run in [256, 1024, 4096, 16384, 65536, 262144, 1 << 20]:
+        n_runs = total // run
+        ms = timed_ms(lambda: F.fathom_stream_read_runs(h, run, 2 * run, n_runs, sink),
+                      stream, 3)
+        rows.append({"run_bytes": run, "zero_copy_GBps": round(total / (ms * 1e-3) / 1e9, 2)})
+    d = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    for r in rows:
+        run = r["run_bytes"]
+        if run < 4096:
+            continue
+        calls = min(2000, total // run)
+        def per_run():
+            for i in range(calls):
+                d[:run].copy_(h[2 * run * i:2 * run * i + run], non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        per_run()
+        torch.cuda.synchronize()
+        r["dma_call_per_run_GBps_wall"] = round(calls * run / (time.perf_counter() - t0) / 1e9, 3)
+    del h, d
+    return rows
+
+
+def host_model(args, name, L):
+    """Full-model scan + top-k (36 layers x 8 KV heads x 4 queries, k = 512) with the
+    bit-plane store in pinned host memory, read by the GPU over the host link: per budget
+    (and for the 136-bit fixed-depth plan) the GPU time of plan + scan + top-k per step,
+    the scan's plane bytes and their rate as a fraction of the link rate L, and an oracle
+    check of one sampled head (plan exact, scores to 1e-5, top-k exact on the GPU
+    scores)."""
+    import torch
+
+    import oracle
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS[name]
+    H, G, n, k = cfg.H, cfg.G, cfg.n, cfg.k
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    Wst = ((n + 31) // 32 + 3) // 4 * 4
+    planes_h = torch.empty((H, 128, 4, Wst), dtype=torch.int32, pin_memory=True)
+    kw = dict(dtype=torch.float32, device=dev)
+    st_h = F.Store(planes_h, torch.empty((H, 128), **kw), torch.empty((H, 128), **kw),
+                   torch.empty((H, 128), **kw), n)
+    batch = max(1, (8 << 30) // (n * 512))  # about 8 GiB of fp32 keys per batch
+    st_b = F.Store.empty(batch, n, dev)
+    for h0 in range(0, H, batch):
+        h1 = min(H, h0 + batch)
+        keys = synth.keys_torch(args.seed, cfg.cfg_id, range(h0, h1), n, dev)
+        sv = st_b.view_heads(0, h1 - h0)
+        F.fathom_quantize_store(keys, sv)
+        planes_h[h0:h1].copy_(sv.planes)
+        st_h.scale[h0:h1].copy_(sv.scale)
+        st_h.zero[h0:h1].copy_(sv.zero)
+        st_h.var[h0:h1].copy_(sv.var)
+        del keys
+    torch.cuda.synchronize()
+    del st_b
+    torch.cuda.empty_cache()
+    q_np = synth.queries_np(args.seed, cfg.cfg_id, range(H), G)
+    q = torch.from_numpy(q_np).to(dev)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    idx = torch.empty((H, G, k), dtype=torch.int32, device=dev)
+    depth = torch.empty((H, 128), dtype=torch.uint8, device=dev)
+    sws = F.scan_workspace(st_h, G, dev)
+    tneed = F.workspace_size(F.OP_TOPK, H * G, 1, n, k)
+    tws = torch.empty(max(tneed, 1), dtype=torch.uint8, device=dev)
+    log(f"[bench] {name}: pinned store of {planes_h.numel() * 4 / 1e9:.2f} GB ready in "
+        f"{time.time() - t0:.1f}s")
+
+    def plan_for(b):
+        if b == "fixed136":
+            return lambda: F.fathom_plan_fixed(st_h, 34, depth=depth)
+        return lambda: F.fathom_plan(st_h, q, b, depth=depth)
+
+    res = {"workload": name, "kv_heads_x_layers": H, "queries_per_kv_head": G, "tokens": n,
+           "k": k, "residency": "pinned host", "pinned_store_bytes": int(planes_h.numel() * 4),
+           "L_GBps": L["L_GBps"], "budgets": {}}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    reps = 5 if n <= 262144 else 3
+    for b in list(cfg.budgets) + (["fixed136"] if name == "qwen3_8b_1m_host" or
+                                   name == "qwen3_8b_256k_host" else []):
+        plan = plan_for(b)
+        planes_read = 136 if b == "fixed136" else b
+
+        def step():
+            plan()
+            F.fathom_scan(st_h, q, depth, scores=scores, ws=sws)
+            F.fathom_topk(scores, k, idx=idx, ws=tws)
+        step()
+        torch.cuda.synchronize()
+        step_ms = timed_ms(step, stream, reps, flush, sink)
+        F.fathom_scan_prepare(st_h, q, depth, sws)
+        scan_ms = timed_ms(lambda: F.fathom_scan_prepared(st_h, G, scores, sws), stream, reps,
+                           flush, sink)
+        topk_ms = timed_ms(lambda: F.fathom_topk(scores, k, idx=idx, ws=tws), stream, reps,
+                           flush, sink)
+        pb = planes_read / 8 * n * H
+        gbps = pb / (scan_ms * 1e-3) / 1e9
+        res["budgets"][str(b)] = {
+            "step_ms_plan_scan_topk": round(step_ms, 3), "scan_ms": round(scan_ms, 3),
+            "topk_ms": round(topk_ms, 3), "scan_plane_bytes": int(pb),
+            "scan_plane_GBps": round(gbps, 2), "scan_frac_of_link": round(gbps / L["L_GBps"], 4),
+            "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 2),
+            "score_bytes_in_hbm": int(4 * G * n * H)}
+        log(f"[bench] {name} B={b}: step {step_ms:.2f} ms, scan {scan_ms:.2f} ms = "
+            f"{gbps:.1f} GB/s of planes ({gbps / L['L_GBps']:.0%} of L)")
+    del flush
+    if "fixed136" in res["budgets"] and "92" in res["budgets"]:
+        r = res["budgets"]
+        res["speedup_b92_vs_fixed136_step"] = round(r["fixed136"]["step_ms_plan_scan_topk"] /
+                                                     r["92"]["step_ms_plan_scan_topk"], 3)
+    # oracle check of one sampled head at B = 92
+    h = H // 2
+    F.fathom_plan(st_h, q, 92, depth=depth)
+    F.fathom_scan(st_h, q, depth, scores=scores, ws=sws)
+    F.fathom_topk(scores, k, idx=idx, ws=tws)
+    torch.cuda.synchronize()
+    kh = synth.keys_torch(args.seed, cfg.cfg_id, [h], n, dev).cpu().numpy()
+    sh, zh, codes = oracle.quantize(kh)
+    ref_depth = oracle.plan(q_np[h][None], oracle.channel_var(codes, sh), 92)
+    got = scores[h].cpu().numpy()
+    ref = oracle.scores(codes, sh, zh, ref_depth, q_np[h][None])[0]
+    err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+    res["oracle_check"] = {
+        "head": h, "budget_bits": 92,
+        "plan": bool(np.array_equal(depth[h].cpu().numpy(), ref_depth[0])),
+        "score_rel_err": err,
+        "topk": bool(np.array_equal(idx[h].cpu().numpy(), oracle.topk(got, k)))}
+    del planes_h, st_h, scores
+    return res
+
+
+def host_resident_step(args, L):
     """One layer's decode step at n = 1M (8 KV heads x 4 queries, B = 92, k = 512) with
     the bit-plane store and the bf16 K/V rows in pinned host memory (read by the GPU over
     the host link), against the same store mirrored in HBM; plus the measured link rate
@@ -415,21 +587,59 @@ def host_resident_step(args):
     scan136_h = timed_ms(lambda: F.fathom_scan_prepared(st_h, G, scores, sws), stream, 10,
                          flush, sink)
     del flush
-    L = link_rate(dev, stream)
     plane_bytes = B / 8 * n * H
     plane_gbps = plane_bytes / (scan_h * 1e-3) / 1e9
+    oracle_check = layer_oracle_check(args, cfg, q, depth_of(st_d, q, B), idx_d, out_d,
+                                      K_d, V_d, B, k, sm)
     return {
         "workload": cfg.name, "kv_heads": H, "queries_per_kv_head": G, "tokens": n,
-        "budget_bits": B, "k": k, "host_equals_hbm": same,
+        "budget_bits": B, "k": k, "host_equals_hbm": same, "oracle_check": oracle_check,
         "step_ms_host": round(step_h, 3), "step_ms_hbm": round(step_d, 3),
         "scan_ms_host": round(scan_h, 3), "scan_ms_hbm": round(scan_d, 3),
         "scan_fixed136_ms_host": round(scan136_h, 3),
         "scan_plane_bytes": int(plane_bytes),
         "scan_plane_GBps_host": round(plane_gbps, 2),
-        "link": L, "scan_frac_of_link": round(plane_gbps / L["L_GBps"], 4),
+        "L_GBps": L["L_GBps"], "scan_frac_of_link": round(plane_gbps / L["L_GBps"], 4),
         "scan_gkeys_per_s_host": round(H * n / (scan_h * 1e-3) / 1e9, 2),
         "pinned_host_bytes": int(planes_h.numel() * 4 + 2 * K_h.numel() * 2),
     }
+
+
+def depth_of(st, q, B):
+    from bit_plane_kv_amd import fathom as F
+    return F.fathom_plan(st, q, B)
+
+
+def layer_oracle_check(args, cfg, q, depth, idx, out, K, V, B, k, sm):
+    """Oracle check of head 0 of the 1M-token layer: plan exact, scores to 1e-5 of the
+    row maximum, top-k exact on the GPU's scores, attention to 2e-2."""
+    import torch
+
+    import oracle
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    h, n, G = 0, cfg.n, cfg.G
+    st1 = F.Store.empty(1, n, q.device)
+    keys = synth.keys_torch(args.seed, cfg.cfg_id, [h], n, q.device)
+    F.fathom_quantize_store(keys, st1)
+    sc = F.fathom_scan(st1, q[h:h + 1], depth[h:h + 1])
+    torch.cuda.synchronize()
+    kh = keys.cpu().numpy()
+    del keys
+    q_np = q[h:h + 1].cpu().numpy()
+    s, z, codes = oracle.quantize(kh)
+    ref_depth = oracle.plan(q_np, oracle.channel_var(codes, s), B)
+    got = sc[0].cpu().numpy()
+    ref = oracle.scores(codes, s, z, ref_depth, q_np)[0]
+    err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+    gi = idx[h].cpu().numpy()
+    Kh = K[h:h + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+    Vh = V[h:h + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+    att = oracle.attention(q_np, Kh, Vh, gi[None], sm)
+    aerr = float(np.abs(out[h].float().cpu().numpy() - att[0]).max())
+    return {"head": h, "plan": bool(np.array_equal(depth[h].cpu().numpy(), ref_depth[0])),
+            "score_rel_err": err, "topk": bool(np.array_equal(gi, oracle.topk(got, k))),
+            "attn_abs_err": aerr}
 
 
 def cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm, sample_keys):
@@ -459,10 +669,35 @@ def cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm, sample_keys):
         elapsed += time.perf_counter() - t0
         done += len(hs)
         h += len(hs)
+    # single-thread figure on the first head of the last batch
+    cores = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        d1 = oracle.plan(qh[:1], var[:1], B)
+        sc1 = oracle.scores(codes[:1], s[:1], z[:1], d1, qh[:1])
+        idx1 = oracle.topk(sc1.astype(np.float32).reshape(-1, n), k).reshape(1, G, k)
+        oracle.attention(qh[:1], Kh[:1], Vh[:1], idx1, sm)
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
     return {"value": round(done * n / elapsed / 1e9, 6), "unit": "Gkeys/s",
-            "cores": oracle.threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "value_1_thread": round(n / t1 / 1e9, 6),
             "sample": f"{done} of {cfg.H} heads (n={n}, G={G}, B={B}, k={k}): plan + fp64 "
-                      f"scores + top-k + attention, {elapsed:.1f} s wall"}
+                      f"scores + top-k + attention, {elapsed:.1f} s wall on {cores} threads; "
+                      f"1 head on 1 thread in {t1:.2f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -274,6 +274,27 @@ int fathom_stream_read(const void *src, size_t bytes, uint64_t *sink, void *stre
     return hip_status(launch_stream_read(src, bytes, sink, as_stream(stream)));
 }
 
+int fathom_stream_read_runs(const void *src, size_t run_bytes, size_t stride_bytes,
+                            size_t n_runs, uint64_t *sink, void *stream) {
+    if (!src || !sink || run_bytes == 0 || run_bytes % 16 != 0 || n_runs == 0 ||
+        stride_bytes < run_bytes || stride_bytes % 16 != 0 || !aligned(src, 16) ||
+        !aligned(sink, 8))
+        return FATHOM_ERR_INVALID_ARG;
+    if ((run_bytes / 16) * (unsigned __int128)n_runs >= ((unsigned __int128)1 << 32))
+        return FATHOM_ERR_UNSUPPORTED;
+    FATHOM_TRY(check_all({src, sink}));
+    // every byte read must lie inside src's allocation
+    const size_t last = (n_runs - 1) * stride_bytes + run_bytes;  // one past the last byte
+    void *base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(src)) != hipSuccess || !base)
+        return FATHOM_ERR_INVALID_ARG;
+    const size_t off = (size_t)((const char *)src - (const char *)base);
+    if (off > size || last > size - off) return FATHOM_ERR_INVALID_ARG;
+    return hip_status(launch_stream_runs(src, run_bytes, stride_bytes, n_runs, sink,
+                                         as_stream(stream)));
+}
+
 int fathom_host_alloc(size_t bytes, int flags, void **ptr) {
     if (!ptr || bytes == 0 || (flags != 0 && flags != 1)) return FATHOM_ERR_INVALID_ARG;
     *ptr = nullptr;

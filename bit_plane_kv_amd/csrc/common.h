@@ -94,6 +94,8 @@ hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t 
                               uint16_t *out, hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint64_t *sink,
                               hipStream_t s);
+hipError_t launch_stream_runs(const void *src, size_t run_bytes, size_t stride_bytes,
+                              size_t n_runs, uint64_t *sink, hipStream_t s);
 
 // ---------------------------------------------------------------------------------
 // Device helpers

@@ -59,6 +59,7 @@ _SIGS = {
     "fathom_step": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I, ctypes.c_float,
                          _P, _P, _P, _P, _P, _SZ, _P]),
     "fathom_stream_read": (_I, [_P, _SZ, _P, _P]),
+    "fathom_stream_read_runs": (_I, [_P, _SZ, _SZ, _SZ, _P, _P]),
     "fathom_host_alloc": (_I, [_SZ, _I, ctypes.POINTER(ctypes.c_void_p)]),
     "fathom_host_free": (_I, [_P]),
 }
@@ -282,3 +283,10 @@ def fathom_step(store: Store, q, K, V, B: int, k: int, sm_scale: float, out=None
 def fathom_stream_read(src, nbytes: int, sink, stream=None):
     _check(lib().fathom_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)),
            "fathom_stream_read")
+
+
+def fathom_stream_read_runs(src, run_bytes: int, stride_bytes: int, n_runs: int, sink,
+                            stream=None):
+    _check(lib().fathom_stream_read_runs(_ptr(src), int(run_bytes), int(stride_bytes),
+                                         int(n_runs), _ptr(sink), _stream(stream)),
+           "fathom_stream_read_runs")

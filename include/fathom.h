@@ -206,6 +206,18 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K,
 int fathom_stream_read(const void *src, size_t bytes, uint64_t *sink, void *stream);
 
 /*
+ * Run-length sweep of the same measurement (blog, "One measurement worth carrying
+ * around": the link rate depends on the length of the contiguous runs): reads n_runs
+ * runs of run_bytes bytes, the r-th starting at src + r * stride_bytes, with 16-byte
+ * loads, and writes a checksum to *sink.  run_bytes and stride_bytes are multiples of
+ * 16, stride_bytes >= run_bytes, run_bytes/16 * n_runs < 2^32 (else
+ * FATHOM_ERR_UNSUPPORTED).  Every byte read must lie inside the allocation holding src
+ * (checked with hipMemGetAddressRange; FATHOM_ERR_INVALID_ARG otherwise).
+ */
+int fathom_stream_read_runs(const void *src, size_t run_bytes, size_t stride_bytes,
+                            size_t n_runs, uint64_t *sink, void *stream);
+
+/*
  * Pinned host memory the GPU can read directly (hipHostMalloc).  flags: 0 = coherent
  * (fine-grained), 1 = non-coherent (coarse-grained).  fathom_host_free releases it.
  * These are the only calls that allocate; they exist so that callers can place the

@@ -91,6 +91,11 @@ def threads() -> int:
     return int(_load().oracle_threads())
 
 
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count of the batched oracle calls (n >= 1)."""
+    _load().oracle_set_threads(ctypes.c_int(int(n)))
+
+
 def n_words(n: int) -> int:
     return (n + 31) // 32
 

@@ -29,6 +29,7 @@
 
 /* Threads the _batch forms use (OpenMP's default team size). */
 int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 
 /* ------------------------------------------------------------------------------ */
 /* Quantize (blog, "How to read fewer bits per key": 4-bit storage; Glonce: "4-bit  */

@@ -122,6 +122,11 @@ def test_stream_read_and_host_alloc_checks():
     L = F.lib()
     assert L.fathom_stream_read(FAKE, 15, FAKE, None) == F.ERR_INVALID_ARG
     assert L.fathom_stream_read(None, 16, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_stream_read_runs(FAKE, 24, 32, 4, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_stream_read_runs(FAKE, 32, 16, 4, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_stream_read_runs(FAKE, 32, 32, 0, FAKE, None) == F.ERR_INVALID_ARG
+    assert L.fathom_stream_read_runs(FAKE, 1 << 20, 1 << 20, 1 << 20, FAKE,
+                                     None) == F.ERR_UNSUPPORTED
     p = ctypes.c_void_p()
     assert L.fathom_host_alloc(0, 0, ctypes.byref(p)) == F.ERR_INVALID_ARG
     assert L.fathom_host_alloc(16, 2, ctypes.byref(p)) == F.ERR_INVALID_ARG

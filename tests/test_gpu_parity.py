@@ -347,3 +347,24 @@ def test_pageable_host_pointer_is_rejected():
     with pytest.raises(F.FathomError) as e:
         F.fathom_scan(bad, q, depth)
     assert e.value.status == F.ERR_NOT_MAPPED
+
+
+def test_stream_read_runs_stays_in_its_allocation():
+    """The run-length measurement read: runs inside a 1 MiB pinned buffer run; a last
+    run past its end is refused on the host (nothing is launched)."""
+    import ctypes
+    torch = torch_cuda()
+    L = F.lib()
+    p = ctypes.c_void_p()
+    assert L.fathom_host_alloc(1 << 20, 0, ctypes.byref(p)) == F.OK
+    try:
+        sink = torch.zeros(2, dtype=torch.int64, device="cuda")
+        sp = ctypes.c_void_p(sink.data_ptr())
+        assert L.fathom_stream_read_runs(p, 4096, 8192, 128, sp, None) == F.OK   # ends at 1 MiB - 4 KiB
+        assert L.fathom_stream_read_runs(p, 8192, 8192, 128, sp, None) == F.OK   # ends at 1 MiB
+        torch.cuda.synchronize()
+        assert L.fathom_stream_read_runs(p, 4096, 8192, 129, sp, None) == F.ERR_INVALID_ARG
+        off = ctypes.c_void_p(p.value + 16)
+        assert L.fathom_stream_read_runs(off, 8192, 8192, 128, sp, None) == F.ERR_INVALID_ARG
+    finally:
+        assert L.fathom_host_free(p) == F.OK
