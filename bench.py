@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--kernel", default=None,
-                    choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136"],
+                    choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136",
+                             "scan_extract"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--no-host", action="store_true",
@@ -259,6 +260,8 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
         "scan_ms": lambda: F.fathom_scan_prepared(st, G, scores, scan_ws),
         "topk_ms": lambda: F.fathom_topk(scores, k, idx=idx),
         "attn_ms": lambda: F.fathom_sparse_attn(q, K, V, idx, sm, out=out),
+        # comparator: the same scores by per-bit extraction on the integer units
+        "scan_extract_ms": lambda: F.fathom_scan_extract(st, q, depth, scores=scores),
     }
     res = {}
 

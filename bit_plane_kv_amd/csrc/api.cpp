@@ -191,6 +191,16 @@ int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
     return hip_status(launch_scan_main(*st, G, scores, ws, as_stream(stream)));
 }
 
+int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                        float *scores, void *stream) {
+    FATHOM_TRY(check_store(st));
+    FATHOM_TRY(check_g(G));
+    if (!q || !depth || !scores || !aligned(q, 4) || !aligned(scores, 4))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({q, depth, st->planes, st->scale, st->zero, scores}));
+    return hip_status(launch_scan_extract(*st, q, G, depth, scores, as_stream(stream)));
+}
+
 int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *depth,
                 float *scores, void *ws, size_t ws_bytes, void *stream) {
     FATHOM_TRY(scan_common(st, G, ws, ws_bytes));

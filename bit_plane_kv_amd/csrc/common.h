@@ -87,6 +87,8 @@ hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, void *ws, hipStream_t s);
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
                             hipStream_t s);
+hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,
+                               const uint8_t *depth, float *scores, hipStream_t s);
 hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
                        hipStream_t s);
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,

@@ -290,11 +290,16 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
 // m0 + 16 l (m0 the same for the whole wave).  Written as inline assembly so that the
 // compiler's own wait insertion does not treat every later LDS read as depending on it
 // (it cannot tell the tiles apart); the tile reads wait for it explicitly.
+// m0 is a reserved register: it is saved and restored around the copy, so the statement
+// leaves it as it found it.
 __device__ __forceinline__ void copy16_to_lds(const uint32_t *src, uint32_t m0) {
-    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
-                     : "memory", "m0");
+    uint32_t saved;
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
+        : "memory");
 }
 
 // Work split.  The (head, super-step) pairs of a launch are numbered head-major;

@@ -58,6 +58,7 @@ _SIGS = {
     "fathom_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P]),
     "fathom_step": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I, ctypes.c_float,
                          _P, _P, _P, _P, _P, _SZ, _P]),
+    "fathom_scan_extract": (_I, [_P, _P, _I, _P, _P, _P]),
     "fathom_stream_read": (_I, [_P, _SZ, _P, _P]),
     "fathom_stream_read_runs": (_I, [_P, _SZ, _SZ, _SZ, _P, _P]),
     "fathom_host_alloc": (_I, [_SZ, _I, ctypes.POINTER(ctypes.c_void_p)]),
@@ -212,6 +213,18 @@ def fathom_scan(store: Store, q, depth, scores=None, ws=None, stream=None):
     _check(lib().fathom_scan(ctypes.byref(st), _ptr(q), G, _ptr(depth), _ptr(scores),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "fathom_scan")
+    return scores
+
+
+def fathom_scan_extract(store: Store, q, depth, scores=None, stream=None):
+    """Comparator scan (per-bit extraction on the integer units); same result layout."""
+    import torch
+    H, G, _ = q.shape
+    if scores is None:
+        scores = torch.empty((H, G, store.n_tokens), dtype=torch.float32, device=q.device)
+    st = store.descriptor()
+    _check(lib().fathom_scan_extract(ctypes.byref(st), _ptr(q), G, _ptr(depth), _ptr(scores),
+                                     _stream(stream)), "fathom_scan_extract")
     return scores
 
 

@@ -164,6 +164,17 @@ int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
                          size_t ws_bytes, void *stream);
 
 /*
+ * Comparator for measurement: the same scores as fathom_scan, computed the way the blog's
+ * "Where this does not work" section costs the bit-plane scan -- each bit extracted on
+ * the integer units (about 2 operations per bit) to rebuild every channel's t-plane
+ * prefix p, then score = C_g + sum_c A_gc p_c with A_gc = fl32(q_gc s_c) 2^(4 - t_c),
+ * accumulated in fp32 over channels in ascending order.  Same arguments and layouts as
+ * fathom_scan, no workspace.  Slower than fathom_scan by design.
+ */
+int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                        float *scores, void *stream);
+
+/*
  * Top k of each row (blog, "The first fix": take the top k).
  *   scores [R][n] fp32, finite; idx [R][k] int32 out, ascending by token index.
  * Order: score descending, then token index ascending (equal scores go to the lower

@@ -169,6 +169,23 @@ def test_scan_many_small_heads(H, n):
     check_rows(scores.cpu().numpy(), oracle.scores(codes, s, z, depth, q))
 
 
+@pytest.mark.parametrize("H,G,n", [(2, 4, 5000), (1, 1, 4096), (2, 8, 777), (1, 3, 33)])
+@pytest.mark.parametrize("kind", ["plan92", "b512", "random", "b0"])
+def test_scan_extract_matches_oracle(H, G, n, kind):
+    """The per-bit-extraction comparator gives the same scores to the same tolerance."""
+    torch = torch_cuda()
+    print(f"[scan-extract] H={H} G={G} n={n} {kind}", flush=True)
+    keys, q, _, _ = inputs(62, H, G, n)
+    st, _ = store_from_keys(keys)
+    s, z, codes = oracle.quantize(keys)
+    var = oracle.channel_var(codes, s)
+    q_t = to_dev(q)
+    depth = _depths(kind, st, q_t, var, q, np.random.default_rng(n + 1))
+    got = F.fathom_scan_extract(st, q_t, to_dev(depth))
+    torch.cuda.synchronize()
+    check_rows(got.cpu().numpy(), oracle.scores(codes, s, z, depth, q))
+
+
 def test_scan_prepared_equals_scan():
     torch = torch_cuda()
     keys, q, _, _ = inputs(61, 2, 4, 6000)
