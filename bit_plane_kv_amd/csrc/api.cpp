@@ -269,8 +269,7 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const
     uint8_t *depth = depth_out ? depth_out : reinterpret_cast<uint8_t *>(w);
 
     const hipStream_t s = as_stream(stream);
-    FATHOM_TRY(hip_status(launch_plan(*st, q, G, B, depth, s)));
-    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, scan_ws, s)));
+    FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, depth, scan_ws, s)));
     FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
     FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
     return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));

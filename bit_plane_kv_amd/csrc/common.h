@@ -85,6 +85,8 @@ hipError_t launch_plan_fixed(const fathom_store &st, int n_channels, uint8_t *de
                              hipStream_t s);
 hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, void *ws, hipStream_t s);
+hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B,
+                               uint8_t *depth, void *ws, hipStream_t s);
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
                             hipStream_t s);
 hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,

@@ -22,6 +22,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "plan_device.h"
 
 namespace fathom {
 namespace {
@@ -43,24 +44,23 @@ __device__ int weight_digit(long long M, int d) {
     return (int)(((M & 255) ^ 128) - 128);
 }
 
+// Body of the prepare step for head h; tc[c] (LDS, complete) holds the channel depths.
+// 256 threads.
 template <int QS>
-__global__ __launch_bounds__(256) void k_scan_prepare(
-    const float *__restrict__ q, const uint8_t *__restrict__ depth,
-    const float *__restrict__ scale, const float *__restrict__ zero, int H, int G,
-    char *__restrict__ ws) {
+__device__ __forceinline__ void prepare_head(const float *__restrict__ q, const int *tc,
+                                             const float *__restrict__ scale,
+                                             const float *__restrict__ zero, int H, int G,
+                                             char *__restrict__ ws, int h) {
     constexpr int NQ = 4 * QS;
-    __shared__ int tc[kD];
     __shared__ int off[kD + 1];
     __shared__ uint32_t pl[kMaxPlanesPerHead];
     __shared__ double wt[NQ][kMaxPlanesPerHead];
     __shared__ double red[NQ][kD];
     __shared__ double unit[NQ];
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
     ScanMeta *meta = reinterpret_cast<ScanMeta *>(ws + (size_t)h * kMetaBytes);
     uint32_t *rec = reinterpret_cast<uint32_t *>(ws + (size_t)H * kMetaBytes +
                                                  (size_t)h * kMaxKBlocks * 64 * 16 * QS);
-    if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
-    __syncthreads();
     if (tid < 64) {  // one wave: exclusive prefix sum of the depths, 2 channels a lane
         const int a = tc[2 * lane], b = tc[2 * lane + 1];
         int inc = a + b;
@@ -150,6 +150,32 @@ __global__ __launch_bounds__(256) void k_scan_prepare(
         }
         if (QS == 2) dst[6] = dst[7] = 0;
     }
+}
+
+template <int QS>
+__global__ __launch_bounds__(256) void k_scan_prepare(
+    const float *__restrict__ q, const uint8_t *__restrict__ depth,
+    const float *__restrict__ scale, const float *__restrict__ zero, int H, int G,
+    char *__restrict__ ws) {
+    __shared__ int tc[kD];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
+    __syncthreads();
+    prepare_head<QS>(q, tc, scale, zero, H, G, ws, h);
+}
+
+// A decode step's plan and prepare in one kernel: the depths stay in LDS between them
+// (and are also written to `depth`).
+template <int QS>
+__global__ __launch_bounds__(256) void k_plan_prepare(
+    const float *__restrict__ q, const float *__restrict__ var,
+    const float *__restrict__ scale, const float *__restrict__ zero, int H, int G, int B,
+    uint8_t *__restrict__ depth, char *__restrict__ ws) {
+    __shared__ int tc[kD];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    plan_head(q, var, G, B, h, tc);
+    if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];
+    prepare_head<QS>(q, tc, scale, zero, H, G, ws, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -553,6 +579,19 @@ hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
     else
         hipLaunchKernelGGL(k_scan_prepare<2>, grid, block, 0, s, q, depth, st.scale, st.zero,
                            st.n_heads, G, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B,
+                               uint8_t *depth, void *ws, hipStream_t s) {
+    char *w = static_cast<char *>(ws);
+    const dim3 grid(st.n_heads), block(256);
+    if (query_sets(G) == 1)
+        hipLaunchKernelGGL(k_plan_prepare<1>, grid, block, 0, s, q, st.var, st.scale, st.zero,
+                           st.n_heads, G, B, depth, w);
+    else
+        hipLaunchKernelGGL(k_plan_prepare<2>, grid, block, 0, s, q, st.var, st.scale, st.zero,
+                           st.n_heads, G, B, depth, w);
     return hipGetLastError();
 }
 
