@@ -77,7 +77,14 @@ int check_topk_k(int n, int k) {
 size_t step_ws_bytes(int H, int G, int n, int k) {
     return round256(scan_ws_bytes(H, G)) + round256((size_t)H * G * n * sizeof(float)) +
            round256(topk_ws_bytes(H * G, n, k)) + round256((size_t)H * G * k * sizeof(int32_t)) +
-           round256((size_t)H * FATHOM_D);
+           round256((size_t)H * FATHOM_D) + round256(filter_mask_bytes(H, G, n)) +
+           round256(filter_redo_bytes(H, G, n));
+}
+
+size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
+    return round256(scan_ws_bytes(H, G)) + round256((size_t)H * G * n * sizeof(float)) +
+           round256(filter_mask_bytes(H, G, n)) + round256(topk_ws_bytes(H * G, n, k)) +
+           round256(filter_redo_bytes(H, G, n));
 }
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
@@ -133,6 +140,12 @@ int fathom_workspace_size(int op, int H, int G, int n, int k, size_t *bytes) {
         FATHOM_TRY(check_topk_k(n, k));
         *bytes = step_ws_bytes(H, G, n, k);
         return FATHOM_OK;
+    case FATHOM_OP_SCAN_TOPK:
+        if (H < 1) return FATHOM_ERR_INVALID_ARG;
+        FATHOM_TRY(check_g(G));
+        FATHOM_TRY(check_topk_k(n, k));
+        *bytes = scan_topk_ws_bytes(H, G, n, k);
+        return FATHOM_OK;
     default: return FATHOM_ERR_INVALID_ARG;
     }
 }
@@ -180,7 +193,7 @@ int fathom_scan_prepare(const fathom_store *st, const float *q, int G, const uin
     FATHOM_TRY(scan_common(st, G, ws, ws_bytes));
     if (!q || !depth || !aligned(q, 16)) return FATHOM_ERR_INVALID_ARG;
     FATHOM_TRY(check_all({q, depth, st->scale, st->zero, ws}));
-    return hip_status(launch_scan_prepare(*st, q, G, depth, ws, as_stream(stream)));
+    return hip_status(launch_scan_prepare(*st, q, G, depth, 0, ws, as_stream(stream)));
 }
 
 int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
@@ -208,8 +221,40 @@ int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *de
         return FATHOM_ERR_INVALID_ARG;
     FATHOM_TRY(check_all({q, depth, st->planes, st->scale, st->zero, scores, ws}));
     const hipStream_t s = as_stream(stream);
-    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, ws, s)));
+    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, 0, ws, s)));
     return hip_status(launch_scan_main(*st, G, scores, ws, s));
+}
+
+int fathom_scan_topk(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                     int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+    FATHOM_TRY(check_store(st));
+    FATHOM_TRY(check_g(G));
+    if (!q || !depth || !idx || !ws || !aligned(q, 16) || !aligned(idx, 4) || !aligned(ws, 16))
+        return FATHOM_ERR_INVALID_ARG;
+    const int H = st->n_heads, n = st->n_tokens;
+    FATHOM_TRY(check_topk_k(n, k));
+    if (ws_bytes < scan_topk_ws_bytes(H, G, n, k)) return FATHOM_ERR_WORKSPACE;
+    FATHOM_TRY(check_all({q, depth, st->planes, st->scale, st->zero, idx, ws}));
+    char *w = static_cast<char *>(ws);
+    void *scan_ws = w;
+    w += round256(scan_ws_bytes(H, G));
+    float *cand = reinterpret_cast<float *>(w);
+    w += round256((size_t)H * G * n * sizeof(float));
+    uint32_t *masks = reinterpret_cast<uint32_t *>(w);
+    w += round256(filter_mask_bytes(H, G, n));
+    void *topk_ws = w;
+    w += round256(topk_ws_bytes(H * G, n, k));
+    uint32_t *redo = reinterpret_cast<uint32_t *>(w);
+    const hipStream_t s = as_stream(stream);
+    if (sample_rank(n, k) == 0) {  // no threshold possible (k too close to n): scan all
+        FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, 0, scan_ws, s)));
+        FATHOM_TRY(hip_status(launch_scan_main(*st, G, cand, scan_ws, s)));
+        return hip_status(launch_topk(cand, H * G, n, k, idx, topk_ws, s));
+    }
+    FATHOM_TRY(hip_status(launch_scan_prepare(*st, q, G, depth, k, scan_ws, s)));
+    FATHOM_TRY(hip_status(launch_scan_main(*st, G, cand, scan_ws, s, masks)));
+    return hip_status(
+        launch_topk_filtered(*st, G, cand, masks, scan_ws, redo, k, idx, topk_ws, s));
 }
 
 int fathom_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
@@ -267,11 +312,24 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(w);
     w += round256((size_t)H * G * k * sizeof(int32_t));
     uint8_t *depth = depth_out ? depth_out : reinterpret_cast<uint8_t *>(w);
+    w += round256((size_t)H * FATHOM_D);
+    uint32_t *masks = reinterpret_cast<uint32_t *>(w);
+    w += round256(filter_mask_bytes(H, G, n));
+    uint32_t *redo = reinterpret_cast<uint32_t *>(w);
 
     const hipStream_t s = as_stream(stream);
-    FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, depth, scan_ws, s)));
-    FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
-    FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
+    // every score is asked for, or the sample could not give a threshold (k too close
+    // to n): scan all, then select
+    if (scores_out || sample_rank(n, k) == 0) {
+        FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, 0, depth, scan_ws, s)));
+        FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
+        FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
+    } else {  // the filtering scan keeps the candidates only
+        FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, k, depth, scan_ws, s)));
+        FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
+        FATHOM_TRY(hip_status(
+            launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
+    }
     return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -21,8 +22,11 @@ constexpr int kDigits = 4;                   // signed base-256 digits per weigh
 // ---------------------------------------------------------------------------------
 // Scan workspace, per head: a meta block, then per K-block (4 groups of 8 planes) and
 // per wave lane one record of the MFMA operands that lane supplies.
-//   meta: int32 n_planes, n_groups, n_kblocks, pad; float C[8] (constant term of each
-//   query); float S[8] (power-of-two weight unit of each query); uint32 plane[512]
+//   meta: int32 n_planes, n_groups, n_kblocks; uint32 redo (head 0's only: the row
+//   chunks the filtered select hands to the full select); float C[8] (constant term of each
+//   query); float S[8] (power-of-two weight unit of each query); uint32 tkey[8]
+//   (candidate threshold of each query as an order key, 0: keep every key); uint32
+//   cnt[8] (candidates the filtering scan kept per query); uint32 plane[512]
 //   (c*4 + j, channels ascending, planes ascending within a channel).
 //   record (kblock, lane), lane = 16*kb + 4*w + s:  uint32 row of plane s and of plane
 //   s+4 of group 4*kblock + kb (kSkipRow: no plane, load nothing), then for each set of
@@ -35,9 +39,11 @@ struct ScanMeta {
     int32_t n_planes;
     int32_t n_groups;
     int32_t n_kblocks;
-    int32_t pad;
+    uint32_t redo;
     float C[FATHOM_MAX_G];
     float S[FATHOM_MAX_G];
+    uint32_t tkey[FATHOM_MAX_G];
+    uint32_t cnt[FATHOM_MAX_G];
     uint32_t plane[kMaxPlanesPerHead];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
@@ -48,6 +54,47 @@ inline size_t scan_rec_bytes_per_head(int G) {
 }
 inline size_t scan_ws_bytes(int H, int G) {
     return (size_t)H * (kMetaBytes + scan_rec_bytes_per_head(G));
+}
+
+// Candidate filter.  The filtering scan keeps, per row (head, query), the tokens whose
+// score key is >= the row's threshold key: their scores go, in token order, to the
+// front of their 256-token block of a [H][G][n] fp32 buffer, and bit i of word w of a
+// [H][G][ceil(n/32)] uint32 mask marks token 32w + i as kept.  Any threshold is safe
+// once at least k tokens of the row are kept (the k-th largest score is then >= it);
+// the select recomputes a row that kept fewer.
+constexpr int kFilterBlockWords = 8;  // words per compaction block (256 tokens)
+constexpr int kSampleRuns = 8;        // threshold sample: runs of 4 words per head
+constexpr int kSampleRunWords = 4;
+constexpr int kSampleWords = kSampleRuns * kSampleRunWords;  // 32 words: 1024 tokens
+
+// First word of sample run r (0 .. kSampleRuns-1) of a row of W words: every word of a
+// short row, else runs spread evenly over it, 16-byte aligned.
+__host__ __device__ inline int sample_run_word(int r, int W) {
+    return W <= kSampleWords ? kSampleRunWords * r
+                             : kSampleRunWords *
+                                   (int)(((long)r * (W / kSampleRunWords - 1)) / (kSampleRuns - 1));
+}
+// Tokens the sample covers.
+__host__ __device__ inline int sample_tokens(int n) {
+    const int W = (n + 31) / 32;
+    if (W <= kSampleWords) return n;
+    const int end = 32 * (sample_run_word(kSampleRuns - 1, W) + kSampleRunWords);
+    return kSampleWords * 32 - (end > n ? end - n : 0);
+}
+// Rank m of the sampled key kept as the threshold: the least m with
+// n (m - 5 sqrt(m)) / S >= k (S sampled tokens); 0 when it exceeds S (no threshold).
+__host__ __device__ inline int sample_rank(int n, int k) {
+    const int S = sample_tokens(n);
+    const double x = 0.5 * (5.0 + sqrt(25.0 + 4.0 * (double)k * (double)S / (double)n));
+    const double m = ceil(x * x);
+    return m > (double)S ? 0 : (int)m;
+}
+inline size_t filter_mask_bytes(int H, int G, int n) {
+    return (size_t)H * G * (size_t)((n + 31) / 32) * sizeof(uint32_t);
+}
+// the select's list of row chunks for the full select: one uint32 per chunk
+inline size_t filter_redo_bytes(int H, int G, int n) {
+    return (size_t)H * G * (size_t)((n + FATHOM_TOPK_CHUNK - 1) / FATHOM_TOPK_CHUNK) * 4;
 }
 
 // ---------------------------------------------------------------------------------
@@ -83,16 +130,23 @@ hipError_t launch_plan(const fathom_store &st, const float *q, int G, int B,
                        uint8_t *depth, hipStream_t s);
 hipError_t launch_plan_fixed(const fathom_store &st, int n_channels, uint8_t *depth,
                              hipStream_t s);
+// k > 0: also sample the candidate thresholds for a top-k of k (0: no filtering)
 hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
-                               const uint8_t *depth, void *ws, hipStream_t s);
-hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B,
+                               const uint8_t *depth, int k, void *ws, hipStream_t s);
+hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B, int k,
                                uint8_t *depth, void *ws, hipStream_t s);
+// masks == nullptr: every score to `scores`; else the candidate filter (see above)
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
-                            hipStream_t s);
+                            hipStream_t s, uint32_t *masks = nullptr);
 hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, float *scores, hipStream_t s);
 hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
                        hipStream_t s);
+// top-k of the filtering scan's candidates (rows = H*G); rows that kept fewer than k
+// are rescored from the store and the prepared scan workspace
+hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand,
+                                const uint32_t *masks, void *scan_ws, uint32_t *redo_list,
+                                int k, int32_t *idx, void *ws, hipStream_t s);
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s);
@@ -114,6 +168,14 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
         return (uint16_t)((u >> 16) | 0x0040u);
     u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
     return (uint16_t)(u >> 16);
+}
+
+// Order-preserving 32-bit key of a score (-0 ranks as +0); key 0 is below every
+// non-NaN value.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Map launch block b of nb onto a logical block so that logical blocks

@@ -44,12 +44,123 @@ __device__ int weight_digit(long long M, int d) {
     return (int)(((M & 255) ^ 128) - 128);
 }
 
+// Candidate thresholds of one head (256 threads).  A guess of each query's score
+// quantile from a sample of the head's tokens (sample_run_word), scored in fp32 from the
+// fp64 weights -- not the scan's arithmetic: only the count of kept tokens decides
+// correctness, and the select checks it.  The sample_rank-th largest sampled key is the
+// threshold: about five standard deviations of the sample quantile above the k the
+// select needs.  The sampled words of up to 128 planes at a time are staged in LDS,
+// one 16-byte load per (plane, run), all in flight together; thread t then scores byte
+// (t & 3) of sampled word (t & 127) >> 2 for the two queries 2 (t >> 7) + {0, 1} of
+// each set of 4.
+constexpr int kSamplePlanes = 128;
+template <int QS>
+__device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ planes, int n,
+                                                  int word_stride, int k, int h,
+                                                  int nplanes, const uint32_t *pl,
+                                                  const double (*wt)[kMaxPlanesPerHead],
+                                                  const double (*red)[kD], ScanMeta *meta) {
+    constexpr int kST = kSampleWords * 32;  // sampled tokens per query
+    // the staged words and, once they are used, the sampled keys share one buffer
+    __shared__ __align__(16) uint32_t sbuf[kSamplePlanes * kSampleWords];
+    static_assert(kSamplePlanes * kSampleWords >= 4 * kST, "sample keys");
+    uint32_t(*sw)[kSampleWords] = reinterpret_cast<uint32_t(*)[kSampleWords]>(sbuf);
+    uint32_t(*skey)[kST] = reinterpret_cast<uint32_t(*)[kST]>(sbuf);
+    __shared__ float wf[4][kSamplePlanes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int W = (n + 31) >> 5;
+    const int qh = tid >> 7, rest = tid & 127;
+    const int i = rest >> 2, sb = rest & 3;  // byte sb of sampled word i
+    const int word = sample_run_word(i / kSampleRunWords, W) + i % kSampleRunWords;
+    const bool ok = word < W;
+    const uint32_t m = (uint32_t)sample_rank(n, k);
+    const uint32_t *hp = planes + (size_t)h * kMaxPlanesPerHead * word_stride;
+#pragma unroll
+    for (int set = 0; set < QS; ++set) {
+        float acc[2][8];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) acc[gg][mm] = (float)red[4 * set + 2 * qh + gg][0];
+        for (int p0 = 0; p0 < nplanes; p0 += kSamplePlanes) {
+            const int np = min(kSamplePlanes, nplanes - p0);
+            __syncthreads();  // the previous batch is no longer read
+            {   // every (plane, run) of the batch: at most 4 per thread, loads first
+                constexpr int kPer = kSamplePlanes * kSampleRuns / 256;
+                uint4 v[kPer];
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int e = tid + 256 * u;
+                    const int p = e / kSampleRuns, r = e % kSampleRuns;
+                    const int w0 = sample_run_word(r, W);
+                    v[u] = make_uint4(0u, 0u, 0u, 0u);
+                    // a run starts below W and the row holds word_stride >= 4 * ceil(W / 4)
+                    // words, so the 16 bytes lie in the row
+                    if (p < np && w0 < W)
+                        v[u] = *reinterpret_cast<const uint4 *>(
+                            hp + (size_t)pl[p0 + p] * word_stride + w0);
+                }
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int e = tid + 256 * u;
+                    const int p = e / kSampleRuns, r = e % kSampleRuns;
+                    if (p < np) *reinterpret_cast<uint4 *>(&sw[p][kSampleRunWords * r]) = v[u];
+                }
+            }
+            for (int e = tid; e < 4 * np; e += 256)
+                wf[e / np][e % np] = (float)wt[4 * set + e / np][p0 + e % np];
+            __syncthreads();
+            for (int p = 0; p < np; ++p) {
+                const uint32_t bits = sw[p][i] >> (8 * sb);
+                const float w0 = wf[2 * qh][p], w1 = wf[2 * qh + 1][p];
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm) {
+                    const float b = (float)((bits >> mm) & 1u);  // 0 or 1: the fma is exact
+                    acc[0][mm] = fmaf(b, w0, acc[0][mm]);
+                    acc[1][mm] = fmaf(b, w1, acc[1][mm]);
+                }
+            }
+        }
+        __syncthreads();  // the staged words are no longer read
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) {
+                const bool valid = ok && 32 * word + 8 * sb + mm < n;
+                skey[2 * qh + gg][8 * rest + mm] = valid ? order_key(acc[gg][mm]) : 0u;
+            }
+        __syncthreads();
+        {   // wave gq: the m-th largest sampled key of query 4*set + gq, bit by bit
+            const int gq = tid >> 6;
+            constexpr int kPerLane = kST / 64;
+            uint32_t kk[kPerLane];
+#pragma unroll
+            for (int e = 0; e < kPerLane; ++e) kk[e] = skey[gq][lane + 64 * e];
+            uint32_t T = 0u;  // the top 20 bits of the key suffice for a guess
+            if (m > 0u) {
+                for (int b = 31; b >= 12; --b) {
+                    const uint32_t cand = T | (1u << b);
+                    uint32_t c = 0u;
+#pragma unroll
+                    for (int e = 0; e < kPerLane; ++e)
+                        c += (uint32_t)__popcll(__ballot(kk[e] >= cand));
+                    if (c >= m) T = cand;
+                }
+            }
+            if (lane == 0) meta->tkey[4 * set + gq] = T;
+        }
+        __syncthreads();  // skey is reused by the next set
+    }
+}
+
 // Body of the prepare step for head h; tc[c] (LDS, complete) holds the channel depths.
 // 256 threads.
 template <int QS>
 __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const int *tc,
                                              const float *__restrict__ scale,
                                              const float *__restrict__ zero, int H, int G,
+                                             const uint32_t *__restrict__ planes, int n,
+                                             int word_stride, int k,
                                              char *__restrict__ ws, int h) {
     constexpr int NQ = 4 * QS;
     __shared__ int off[kD + 1];
@@ -122,7 +233,7 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
         meta->n_planes = nplanes;
         meta->n_groups = ngroups;
         meta->n_kblocks = nkb;
-        meta->pad = 0;
+        meta->redo = 0u;
     }
     // operand records: lane ln of K-block kbl serves group 4*kbl + (ln >> 4)
     for (int e = tid; e < nkb * 64; e += 256) {
@@ -150,18 +261,25 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
         }
         if (QS == 2) dst[6] = dst[7] = 0;
     }
+    if (tid < FATHOM_MAX_G) meta->cnt[tid] = 0u;
+    if (k <= 0) {
+        if (tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
+        return;
+    }
+    sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, pl, wt, red, meta);
 }
 
 template <int QS>
 __global__ __launch_bounds__(256) void k_scan_prepare(
     const float *__restrict__ q, const uint8_t *__restrict__ depth,
     const float *__restrict__ scale, const float *__restrict__ zero, int H, int G,
+    const uint32_t *__restrict__ planes, int n, int word_stride, int k,
     char *__restrict__ ws) {
     __shared__ int tc[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
     if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
     __syncthreads();
-    prepare_head<QS>(q, tc, scale, zero, H, G, ws, h);
+    prepare_head<QS>(q, tc, scale, zero, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // A decode step's plan and prepare in one kernel: the depths stay in LDS between them
@@ -170,12 +288,13 @@ template <int QS>
 __global__ __launch_bounds__(256) void k_plan_prepare(
     const float *__restrict__ q, const float *__restrict__ var,
     const float *__restrict__ scale, const float *__restrict__ zero, int H, int G, int B,
+    const uint32_t *__restrict__ planes, int n, int word_stride, int k,
     uint8_t *__restrict__ depth, char *__restrict__ ws) {
     __shared__ int tc[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
     plan_head(q, var, G, B, h, tc);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];
-    prepare_head<QS>(q, tc, scale, zero, H, G, ws, h);
+    prepare_head<QS>(q, tc, scale, zero, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -312,6 +431,73 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
     }
 }
 
+// The filtering form of the combine: the same scores, of which only those whose key is
+// >= the row's threshold key are written to the front of the wave's 256-token block
+// (words wb .. wb+7) of the row, with the block's 8 mask words; the row's count of kept
+// tokens grows by the block's.  Within a block the kept scores are ordered by word in
+// the order wb, wb+2, wb+4, wb+6, wb+1, wb+3, wb+5, wb+7 (pos, then w: lane 4w + s of a
+// query's 16 holds byte s of words wb + 2w + pos), and by token within a word.
+template <int QS>
+__device__ __forceinline__ float combined_score(const v4i &d, int m, float C, float S,
+                                                bool small) {
+    const float lo = small ? (float)(d[0] + d[1] * 256) : fmaf((float)d[1], 256.0f, (float)d[0]);
+    const float hi = (float)(d[2] + d[3] * 256);
+    const float f = fmaf(hi, 65536.0f, lo);
+    const float mult = m < 7 ? S * (1.0f / (float)(1 << m)) : S * (-1.0f / 128.0f);
+    return fmaf(f, mult, C);
+}
+
+template <int QS>
+__device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const float (&Cq)[QS],
+                                               const float (&Sq)[QS], const float (&Tq)[QS],
+                                               bool small, int G, int jq, int s, int wq,
+                                               int lane, int wi, int n, float *hcand,
+                                               uint32_t *hmask, uint32_t *hcnt) {
+    const int W = (n + 31) >> 5;
+    const int wb = wi - 2 * wq;   // first word of the block
+#pragma unroll
+    for (int set = 0; set < QS; ++set) {
+        const int g = 4 * set + jq;
+        const bool live = g < G;  // the same for a query's 16 lanes
+        float *blk = hcand + (size_t)g * n + (size_t)wb * 32;
+        uint32_t base = 0u;       // kept tokens of the block's earlier words
+#pragma unroll
+        for (int pos = 0; pos < 2; ++pos) {
+            const int left = live ? n - ((wi + pos) * 32 + 8 * s) : 0;  // tokens < n
+            float v[8];
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                v[m] = combined_score<QS>(acc[pos][m][set], m, Cq[set], Sq[set], small);
+                bits |= (uint32_t)(m < left && v[m] >= Tq[set]) << m;
+            }
+            // the quad's 4 bytes make the mask word; the bytes below this lane's come
+            // first
+            uint32_t x = bits << (8 * s);
+            x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+            x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+            const uint32_t t = (uint32_t)__popc(x);  // this quad's word
+            // inclusive prefix over the 4 quads of the query's 16 lanes (one DPP row):
+            // row_shr 4 and 8, lanes shifted in from outside the row read 0
+            uint32_t inc = t + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x114, 0xF, 0xF, true);
+            inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x118, 0xF, 0xF, true);
+            // and the inclusive suffix (row_shl 4 and 8): together the row's total
+            uint32_t suf = t + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x104, 0xF, 0xF, true);
+            suf += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)suf, 0x108, 0xF, 0xF, true);
+            const uint32_t tot = inc + suf - t;
+            uint32_t r = base + inc - t + (uint32_t)__popc(x & ((1u << (8 * s)) - 1u));
+            base += tot;
+            if (live) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if ((bits >> m) & 1u) blk[r++] = v[m];
+                if (s == 0 && wi + pos < W) hmask[(size_t)g * W + wi + pos] = x;
+            }
+        }
+        if (live && (lane & 15) == 0 && base) atomicAdd(hcnt + g, base);
+    }
+}
+
 // Global -> LDS copy of 16 bytes a lane: lane l's bytes land at LDS byte address
 // m0 + 16 l (m0 the same for the whole wave).  Written as inline assembly so that the
 // compiler's own wait insertion does not treat every later LDS read as depending on it
@@ -341,20 +527,26 @@ struct ScanSplit {
 
 template <int QS>
 __device__ __forceinline__ void load_head_consts(const ScanMeta *meta, int G, int jq,
-                                                 float (&C)[QS], float (&S)[QS]) {
+                                                 float (&C)[QS], float (&S)[QS],
+                                                 float (&T)[QS]) {
 #pragma unroll
     for (int set = 0; set < QS; ++set) {
         const int g = 4 * set + jq;
         C[set] = g < G ? meta->C[g] : 0.0f;
         S[set] = g < G ? meta->S[g] : 0.0f;
+        // the threshold key as a float: for non-NaN scores v, order_key(v) >= key
+        // exactly when v >= this value (-0 and +0 compare equal); key 0 keeps all
+        const uint32_t key = g < G ? meta->tkey[g] : 0u;
+        T[set] = key == 0u ? -INFINITY
+                           : __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
     }
 }
 
-template <int QS, bool kWide>
+template <int QS, bool kWide, bool kFilter>
 __global__ __launch_bounds__(kScanThreads)
 __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) void k_scan_main(
     const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H, ScanSplit sp,
-    const char *__restrict__ ws, float *__restrict__ scores) {
+    const char *__restrict__ ws, float *__restrict__ scores, uint32_t *__restrict__ masks) {
     extern __shared__ uint4 lds_u4[];
     char *lds = reinterpret_cast<char *>(lds_u4);
     constexpr size_t kHeadBytes = lds_head_bytes<QS>();
@@ -411,8 +603,9 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
     const size_t head_words = (size_t)kMaxPlanesPerHead * word_stride;
     float C0[QS], S0[QS], C1[QS], S1[QS];
-    load_head_consts<QS>(meta0, G, jq, C0, S0);
-    load_head_consts<QS>(meta1, G, jq, C1, S1);
+    float T0[QS], T1[QS];
+    load_head_consts<QS>(meta0, G, jq, C0, S0, T0);
+    load_head_consts<QS>(meta1, G, jq, C1, S1, T1);
     const bool small = max(nkb0, nkb1) < kMaxKBlocks;
     const int npr0 = (nkb0 + 1) >> 1, npr1 = (nkb1 + 1) >> 1;  // K-pairs per super-step
     // super-steps of the run, counted from a: [0, h1rel) in head h0, [h1rel, len) in h1
@@ -507,8 +700,16 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         if (++ppr == (k ? npr1 : npr0)) {
             const int hh = k ? h1 : h0;
             const int wi = ((k ? pss - h1rel : ss0 + pss) * kWaves + wave) * 8 + 2 * wq;
-            combine_store<QS>(acc, k ? C1 : C0, k ? S1 : S0, small, G, jq, s, wi, n,
-                              scores + (size_t)hh * G * n);
+            if constexpr (kFilter) {
+                ScanMeta *mh = reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) +
+                                                            (size_t)hh * kMetaBytes);
+                combine_filter<QS>(acc, k ? C1 : C0, k ? S1 : S0, k ? T1 : T0, small, G, jq,
+                                   s, wq, lane, wi, n, scores + (size_t)hh * G * n,
+                                   masks + (size_t)hh * G * ((n + 31) >> 5), mh->cnt);
+            } else {
+                combine_store<QS>(acc, k ? C1 : C0, k ? S1 : S0, small, G, jq, s, wi, n,
+                                  scores + (size_t)hh * G * n);
+            }
             ppr = 0;
             ++pss;
         }
@@ -516,7 +717,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
 }
 
 // Resident workgroups of a kernel instance over the device (asked once per device).
-template <int QS, bool kWide>
+template <int QS, bool kWide, bool kFilter>
 int resident_slots() {
     static std::mutex mu;
     static int slots[64] = {0};
@@ -525,7 +726,8 @@ int resident_slots() {
     std::lock_guard<std::mutex> lock(mu);
     if (!slots[dev]) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_scan_main<QS, kWide>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
+                                                         k_scan_main<QS, kWide, kFilter>,
                                                          kScanThreads,
                                                          scan_lds_bytes<QS>()) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -536,14 +738,14 @@ int resident_slots() {
     return slots[dev];
 }
 
-template <int QS, bool kWide>
+template <int QS, bool kWide, bool kFilter>
 hipError_t launch_main_qs(const fathom_store &st, int G, float *scores, const char *ws,
-                          hipStream_t s) {
+                          uint32_t *masks, hipStream_t s) {
     const int W = (st.n_tokens + 31) >> 5;
     ScanSplit sp;
     sp.nss = (W + kSuperWords - 1) / kSuperWords;
     const long total = (long)st.n_heads * sp.nss;
-    int slots = resident_slots<QS, kWide>();
+    int slots = resident_slots<QS, kWide, kFilter>();
     if (slots <= 0) slots = 1024;
     slots *= FATHOM_SCAN_ROUNDS;
     sp.run = (int)std::max(1L, (total + slots - 1) / slots);
@@ -552,54 +754,59 @@ hipError_t launch_main_qs(const fathom_store &st, int G, float *scores, const ch
     sp.wgs_per_head = (sp.nss + sp.run - 1) / sp.run;
     const long nblocks = sp.flat ? (total + sp.run - 1) / sp.run
                                  : (long)st.n_heads * sp.wgs_per_head;
-    hipLaunchKernelGGL((k_scan_main<QS, kWide>), dim3((unsigned)nblocks), dim3(kScanThreads),
-                       scan_lds_bytes<QS>(), s, st.planes, st.n_tokens, st.word_stride, G,
-                       st.n_heads, sp, ws, scores);
+    hipLaunchKernelGGL((k_scan_main<QS, kWide, kFilter>), dim3((unsigned)nblocks),
+                       dim3(kScanThreads), scan_lds_bytes<QS>(), s, st.planes, st.n_tokens,
+                       st.word_stride, G, st.n_heads, sp, ws, scores, masks);
     return hipGetLastError();
 }
 
 template <int QS>
 hipError_t launch_main_q(const fathom_store &st, int G, float *scores, const char *ws,
-                         hipStream_t s) {
+                         uint32_t *masks, hipStream_t s) {
     // word offsets of a head's 512 rows fit 32 bits (below the no-row marker)?
     const bool wide = (uint64_t)kMaxPlanesPerHead * (uint64_t)st.word_stride >= 0xFFFFFFFFull;
-    return wide ? launch_main_qs<QS, true>(st, G, scores, ws, s)
-                : launch_main_qs<QS, false>(st, G, scores, ws, s);
+    if (masks)
+        return wide ? launch_main_qs<QS, true, true>(st, G, scores, ws, masks, s)
+                    : launch_main_qs<QS, false, true>(st, G, scores, ws, masks, s);
+    return wide ? launch_main_qs<QS, true, false>(st, G, scores, ws, nullptr, s)
+                : launch_main_qs<QS, false, false>(st, G, scores, ws, nullptr, s);
 }
 
 }  // namespace
 
 hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
-                               const uint8_t *depth, void *ws, hipStream_t s) {
+                               const uint8_t *depth, int k, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     const dim3 grid(st.n_heads), block(256);
     if (query_sets(G) == 1)
         hipLaunchKernelGGL(k_scan_prepare<1>, grid, block, 0, s, q, depth, st.scale, st.zero,
-                           st.n_heads, G, w);
+                           st.n_heads, G, st.planes, st.n_tokens, st.word_stride, k, w);
     else
         hipLaunchKernelGGL(k_scan_prepare<2>, grid, block, 0, s, q, depth, st.scale, st.zero,
-                           st.n_heads, G, w);
+                           st.n_heads, G, st.planes, st.n_tokens, st.word_stride, k, w);
     return hipGetLastError();
 }
 
-hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B,
+hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B, int k,
                                uint8_t *depth, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     const dim3 grid(st.n_heads), block(256);
     if (query_sets(G) == 1)
         hipLaunchKernelGGL(k_plan_prepare<1>, grid, block, 0, s, q, st.var, st.scale, st.zero,
-                           st.n_heads, G, B, depth, w);
+                           st.n_heads, G, B, st.planes, st.n_tokens, st.word_stride, k,
+                           depth, w);
     else
         hipLaunchKernelGGL(k_plan_prepare<2>, grid, block, 0, s, q, st.var, st.scale, st.zero,
-                           st.n_heads, G, B, depth, w);
+                           st.n_heads, G, B, st.planes, st.n_tokens, st.word_stride, k,
+                           depth, w);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
-                            hipStream_t s) {
+                            hipStream_t s, uint32_t *masks) {
     const char *w = static_cast<const char *>(ws);
-    return query_sets(G) == 1 ? launch_main_q<1>(st, G, scores, w, s)
-                              : launch_main_q<2>(st, G, scores, w, s);
+    return query_sets(G) == 1 ? launch_main_q<1>(st, G, scores, w, masks, s)
+                              : launch_main_q<2>(st, G, scores, w, masks, s);
 }
 
 }  // namespace fathom

@@ -48,12 +48,6 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kEPT = kTopkChunk / kThreads;  // 32
 
-__device__ __forceinline__ uint32_t order_key(float v) {
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
 }
@@ -119,32 +113,160 @@ __device__ __forceinline__ void find_bin(uint32_t *hist, uint32_t *scan_sh, uint
 
 constexpr int kCandCap = 4096;  // threshold-bin entries refined in LDS
 
+// What the first level of a filtered select reads besides the candidates.
+struct FilterArgs {
+    const uint32_t *masks;    // [R][W] kept-token masks
+    const char *scan_ws;      // the prepared scan workspace (meta blocks, records)
+    const uint32_t *planes;   // the store, for rows that are rescored
+    int word_stride, W, G, H, qs;
+};
+
+// Filler candidates for slots [from, to) of a chunk's output: value with key 0 (below
+// every score) and an index past any row.  They fill the slots of a chunk that kept
+// fewer than k candidates; the rows they belong to kept at least k in total, so the
+// later levels never select them.
+__device__ __forceinline__ void fill_slots(float *out_val, int32_t *out_idx, int64_t base,
+                                           int from, int to) {
+    for (int o = from + (int)threadIdx.x; o < to; o += (int)blockDim.x) {
+        out_val[base + o] = __uint_as_float(0xFFFFFFFFu);
+        out_idx[base + o] = 0x7FFFFFFF;
+    }
+}
+
+// Kept-candidate keys of this thread's word (tokens 32*word .. +31): the block's kept
+// scores lie at the front of its 256-token region, words in the order 0,2,4,6,1,3,5,7
+// of the block, tokens ascending within a word.  Returns the mask.
+__device__ __forceinline__ uint32_t load_kept(const float *row_cand, const uint32_t *row_mask,
+                                              int word, int W, uint32_t lenmask,
+                                              uint32_t (&key)[kEPT]) {
+    const uint32_t mk = (word < W ? row_mask[word] : 0u) & lenmask;
+    const uint32_t c = (uint32_t)__popc(mk);
+    const int j = threadIdx.x & 7;  // word within the block (blocks are 8 threads)
+    const int oj = (j & 1) * 4 + (j >> 1);
+    uint32_t pre = 0u;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {  // words stored before this one
+        const uint32_t co = (uint32_t)__shfl((int)c, 2 * (o & 3) + (o >> 2), 8);
+        if (o < oj) pre += co;
+    }
+    const float *src = row_cand + (size_t)(word & ~7) * 32 + pre;
+    uint32_t r = 0u;
+#pragma unroll
+    for (int e = 0; e < kEPT; ++e) {
+        key[e] = 0u;
+        if ((mk >> e) & 1u) key[e] = order_key(src[r++]);
+    }
+    return mk;
+}
+
+// Scores of this thread's word of row (h, g), recomputed from the store and the
+// prepared records with the scan's own arithmetic, so they equal its scores bit for
+// bit: per token the exact integer sums L = sum bit * (d0 + 256 d1) and
+// Hs = sum bit * (d2 + 256 d3) over the head's planes (d the weight's base-256 digits),
+// f = fl(fl(Hs) 65536 + fl(L)), and with m the token's bit within its byte the scan's
+// final step fl(f 2^m * fl(S 2^-m) + C) (-128 in place of 2^7).  tab: 3*512 words of LDS.
+// Kept out of line: it runs only for rows whose threshold guess failed, and inlined it
+// makes the compiler duplicate the select around it.
+__device__ __noinline__ void rescore_word(const FilterArgs &fa, int h, int g, int word,
+                                             uint32_t lenmask, uint32_t *tab,
+                                             uint32_t (&key)[kEPT]) {
+    const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
+    const int np = min(max(meta->n_planes, 0), kMaxPlanesPerHead);
+    const uint32_t *rec = reinterpret_cast<const uint32_t *>(
+        fa.scan_ws + (size_t)fa.H * kMetaBytes + (size_t)h * kMaxKBlocks * 64 * 16 * fa.qs);
+    int *tl = reinterpret_cast<int *>(tab), *th = tl + kMaxPlanesPerHead;
+    uint32_t *tp = tab + 2 * kMaxPlanesPerHead;
+    for (int p = threadIdx.x; p < np; p += kThreads) {
+        const int grp = p >> 3, i = p & 7, kbl = grp >> 2;
+        int dg[kDigits];
+#pragma unroll
+        for (int d = 0; d < kDigits; ++d) {
+            const int ln = 16 * (grp & 3) + 4 * (g & 3) + d;
+            const uint32_t wv =
+                rec[(size_t)(kbl * 64 + ln) * 4 * fa.qs + 2 + 2 * (g >> 2) + (i >> 2)];
+            dg[d] = (int)(int8_t)(uint8_t)(wv >> (8 * (i & 3)));
+        }
+        tl[p] = dg[0] + 256 * dg[1];
+        th[p] = dg[2] + 256 * dg[3];
+        tp[p] = meta->plane[p];
+    }
+    __syncthreads();
+    const float C = meta->C[g], S = meta->S[g];
+    const uint32_t *hp = fa.planes + (size_t)h * kMaxPlanesPerHead * fa.word_stride + word;
+    const bool inrow = word < fa.W;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {  // 4 tokens a pass: 8*(b/2) + 4*(b%2) + m4
+        int la[4], ha[4];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) la[m4] = ha[m4] = 0;
+        if (inrow) {
+            for (int p = 0; p < np; ++p) {
+                const uint32_t x = hp[(size_t)tp[p] * fa.word_stride] >> (4 * b);
+                const int l = tl[p], hh = th[p];
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) {
+                    const int on = -(int)((x >> m4) & 1u);
+                    la[m4] += l & on;
+                    ha[m4] += hh & on;
+                }
+            }
+        }
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const int m = 4 * (b & 1) + m4;  // bit within the byte
+            const float f = fmaf((float)ha[m4], 65536.0f, (float)la[m4]);
+            const float fm = m < 7 ? f * (float)(1 << m) : f * -128.0f;
+            const float mult = m < 7 ? S * (1.0f / (float)(1 << m)) : S * (-1.0f / 128.0f);
+            const int e = 4 * b + m4;
+            key[e] = ((lenmask >> e) & 1u) ? order_key(fmaf(fm, mult, C)) : 0u;
+        }
+    }
+    __syncthreads();  // the tables are no longer read
+}
+
+
 // kExplicit: input entries carry their own int32 index (candidate levels); otherwise
 // the index is the position in the row.  kCandOut: write (value, index) candidates
 // (at column chunk*kk of the output row) instead of final indices.
-template <bool kExplicit, bool kCandOut>
-__global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
-    const float *__restrict__ vals, const int32_t *__restrict__ in_idx, int64_t row_len,
-    int64_t in_stride, int row0, int k, float *__restrict__ out_val,
-    int32_t *__restrict__ out_idx, int64_t out_stride) {
+template <bool kExplicit, bool kCandOut, bool kMasked>
+__device__ __forceinline__ void select_chunk(
+    int64_t row, int chunk, const float *__restrict__ vals, const int32_t *__restrict__ in_idx,
+    int64_t row_len, int64_t in_stride, int k, float *__restrict__ out_val,
+    int32_t *__restrict__ out_idx, int64_t out_stride, const FilterArgs &fa) {
     __shared__ uint32_t hist[4096];
     __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t scan_sh[17];
     __shared__ uint32_t pick[3];
     __shared__ uint32_t ncand;
     const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
-    const int64_t row = (int64_t)row0 + blockIdx.y;
     const int64_t start = (int64_t)chunk * kTopkChunk;
     const int len = (int)min((int64_t)kTopkChunk, row_len - start);
-    const int kr = min(k, len);
     const float *v = vals + row * in_stride + start;
     const int p0 = tid * kEPT;  // this thread's positions p0 .. p0+31
     const int nvalid = max(0, min(kEPT, len - p0));
-    const uint32_t vmask = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
+    uint32_t vmask = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
 
     uint32_t key[kEPT];
-    if (((((uintptr_t)(v + p0)) & 15u) == 0) && nvalid == kEPT) {
+    int kr = min(k, len);
+    if constexpr (kMasked) {
+        // Candidates of the filtering scan.  A row that kept fewer than k tokens is
+        // rescored in full here (its threshold guess was too high).
+        const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
+        const ScanMeta *meta =
+            reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
+        const int word = chunk * kThreads + tid;
+        if (meta->cnt[g] < (uint32_t)k) {
+            rescore_word(fa, h, g, word, vmask, hist, key);
+        } else {
+            vmask = load_kept(vals + row * in_stride, fa.masks + row * fa.W, word, fa.W, vmask,
+                              key);
+            if (kCandOut) {  // this chunk may hold fewer than k candidates
+                uint32_t total;
+                block_excl_scan((uint32_t)__popc(vmask), scan_sh, &total);
+                kr = min(kr, (int)total);
+            }
+        }
+    } else if (((((uintptr_t)(v + p0)) & 15u) == 0) && nvalid == kEPT) {
 #pragma unroll
         for (int e = 0; e < kEPT; e += 4) {
             const float4 f = *reinterpret_cast<const float4 *>(v + p0 + e);
@@ -162,13 +284,18 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
     for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
     if (tid == 0) ncand = 0u;
     __syncthreads();
-    if (nvalid == kEPT) {
+    if (kCandOut && kMasked && kr == 0) {  // a chunk without candidates: all filler
+        fill_slots(out_val, out_idx, row * out_stride + (int64_t)chunk * min(k, kTopkChunk), 0,
+                   min(k, len));
+        return;
+    }
+    if (vmask == 0xFFFFFFFFu) {
 #pragma unroll
         for (int e = 0; e < kEPT; ++e) atomicAdd(&hist[key[e] >> 20], 1u);
     } else {
 #pragma unroll
         for (int e = 0; e < kEPT; ++e)
-            if (e < nvalid) atomicAdd(&hist[key[e] >> 20], 1u);
+            if ((vmask >> e) & 1u) atomicAdd(&hist[key[e] >> 20], 1u);
     }
     __syncthreads();
     find_bin(hist, scan_sh, pick, 4096, (uint32_t)kr);
@@ -266,6 +393,249 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
         }
         ++slot;
     }
+    if (kCandOut && kMasked)  // slots past this chunk's candidates: filler
+        fill_slots(out_val, out_idx, row * out_stride + (int64_t)chunk * min(k, kTopkChunk), kr,
+                   min(k, len));
+}
+
+template <bool kExplicit, bool kCandOut, bool kMasked>
+__global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
+    const float *__restrict__ vals, const int32_t *__restrict__ in_idx, int64_t row_len,
+    int64_t in_stride, int row0, int k, float *__restrict__ out_val,
+    int32_t *__restrict__ out_idx, int64_t out_stride, FilterArgs fa) {
+    select_chunk<kExplicit, kCandOut, kMasked>((int64_t)row0 + blockIdx.y, blockIdx.x, vals,
+                                               in_idx, row_len, in_stride, k, out_val, out_idx,
+                                               out_stride, fa);
+}
+
+// The row chunks the filtered select handed over (listed as row * nch + chunk; their
+// count is the head-0 meta block's redo field), a grid-stride loop over the list: a
+// small grid, as the list is usually empty.
+constexpr int kRedoGrid = 64;
+template <bool kCandOut>
+__global__ __launch_bounds__(kThreads, 8) void k_topk_redo(
+    const float *__restrict__ vals, int64_t row_len, int k, float *__restrict__ out_val,
+    int32_t *__restrict__ out_idx, int64_t out_stride, FilterArgs fa,
+    const uint32_t *__restrict__ list, int nch) {
+    const uint32_t total = reinterpret_cast<const ScanMeta *>(fa.scan_ws)->redo;
+    for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
+        const uint32_t item = list[it];
+        select_chunk<false, kCandOut, true>((int64_t)(item / (uint32_t)nch),
+                                            (int)(item % (uint32_t)nch), vals, nullptr, row_len,
+                                            row_len, k, out_val, out_idx, out_stride, fa);
+        __syncthreads();  // LDS is reused by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Filtered select: one 256-thread workgroup per row chunk ranks the chunk's kept
+// candidates in LDS (up to kSelCap of them), so that every row of a decode step runs
+// at once.  A chunk with more candidates, or of a row that kept fewer than k tokens in
+// total, is appended to the redo list for the full select above.
+// ---------------------------------------------------------------------------------
+constexpr int kSelThreads = 256;
+constexpr int kSelCap = 3840;  // with 8 KB of histogram: 5 workgroups per CU
+constexpr int kSelWords = kTopkChunk / 32 / kSelThreads;  // mask words per thread: 4
+static_assert(kSelWords == 4, "two threads per 8-word block");
+
+// Exclusive prefix over the 256 threads with one barrier: each thread adds the totals
+// of the waves before its own.  sh (4 words) must not be rewritten before every thread
+// has read it: callers alternate between two.
+__device__ __forceinline__ uint32_t block256_prefix(uint32_t v, uint32_t *sh, uint32_t *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t inc = wave_incl_scan(v, lane);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    const uint32_t a = sh[0], b = sh[1], c = sh[2], d = sh[3];
+    *total = a + b + c + d;
+    return inc - v + (wave > 0 ? a : 0u) + (wave > 1 ? b : 0u) + (wave > 2 ? c : 0u);
+}
+
+constexpr int kSelBins = 2048;  // 11-bit digits: passes over bits 31-21, 20-10, 9-0
+
+template <bool kCandOut>
+__global__ __launch_bounds__(kSelThreads) void k_select_kept(
+    const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
+    uint32_t *__restrict__ list, float *__restrict__ out_val, int32_t *__restrict__ out_idx,
+    int64_t out_stride) {
+    __shared__ uint32_t skey[kSelCap];
+    __shared__ uint16_t soff[kSelCap];
+    __shared__ uint32_t hist[kSelBins];
+    __shared__ uint32_t sh[2][4];
+    __shared__ uint32_t pick[2][3];
+    const int tid = threadIdx.x, chunk = blockIdx.x, nch = gridDim.x;
+    const int64_t row = (int64_t)row0 + blockIdx.y;
+    const int64_t start = (int64_t)chunk * kTopkChunk;
+    const int len = (int)min((int64_t)kTopkChunk, n - start);
+    const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
+    ScanMeta *meta0 = reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws));
+    const ScanMeta *meta =
+        reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
+    // this thread's 4 mask words: chunk words 4 tid .. 4 tid + 3
+    const int wl = kSelWords * tid;
+    const int64_t wg = (int64_t)chunk * (kTopkChunk / 32) + wl;
+    uint32_t mk[kSelWords], c[kSelWords];
+#pragma unroll
+    for (int j = 0; j < kSelWords; ++j) {
+        const int t0 = 32 * (wl + j);  // first chunk token of the word
+        const uint32_t lm = t0 >= len ? 0u : (len - t0 >= 32 ? 0xFFFFFFFFu : (1u << (len - t0)) - 1u);
+        mk[j] = wg + j < fa.W ? fa.masks[row * fa.W + wg + j] & lm : 0u;
+    }
+    const bool full = meta->cnt[g] < (uint32_t)k;  // the row is rescored by the full select
+#pragma unroll
+    for (int j = 0; j < kSelWords; ++j) {
+        if (full) mk[j] = 0u;
+        c[j] = (uint32_t)__popc(mk[j]);
+    }
+    for (int b = tid; b < kSelBins; b += kSelThreads) hist[b] = 0u;
+    uint32_t C;
+    const uint32_t pos0 = block256_prefix(c[0] + c[1] + c[2] + c[3], sh[0], &C);
+    if (full || C > (uint32_t)kSelCap) {
+        if (tid == 0) list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
+        return;
+    }
+    // Stored order of a block's kept scores: words 0,2,4,6,1,3,5,7.  Thread 2b holds
+    // words 0-3 of block b, thread 2b+1 words 4-7.
+    {
+        const uint32_t E = c[0] + c[2], O = c[1] + c[3];
+        const uint32_t pE = (uint32_t)__shfl_xor((int)E, 1, 64);
+        const uint32_t pO = (uint32_t)__shfl_xor((int)O, 1, 64);
+        const bool odd = tid & 1;
+        const uint32_t eb = odd ? pE : 0u, ob = odd ? pO : 0u, te = E + pE;
+        uint32_t off[kSelWords];
+        off[0] = eb;
+        off[2] = eb + c[0];
+        off[1] = te + ob;
+        off[3] = te + ob + c[1];
+        // first the row offset of each kept score, in token order ...
+        const uint32_t blk = (uint32_t)(start + 32 * (int64_t)(wl & ~7));
+        uint32_t pos = pos0;
+#pragma unroll
+        for (int j = 0; j < kSelWords; ++j) {
+            uint32_t m = mk[j], r = blk + off[j];
+            while (m) {
+                const int b = __ffs(m) - 1;
+                m &= m - 1u;
+                skey[pos] = r++;
+                soff[pos] = (uint16_t)(32 * (wl + j) + b);
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+    {   // ... then all the loads at once, each thread up to kSelCap / 256 of them, and the
+        // first histogram (top 11 bits) on the way
+        constexpr int kPer = kSelCap / kSelThreads;
+        const float *crow = cand + row * n;
+        float v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = tid + kSelThreads * u;
+            v[u] = e < (int)C ? crow[skey[e]] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = tid + kSelThreads * u;
+            if (e < (int)C) {
+                const uint32_t key = order_key(v[u]);
+                skey[e] = key;
+                atomicAdd(&hist[key >> 21], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    const int kk = min(k, kTopkChunk);
+    const int64_t obase = row * out_stride + (int64_t)chunk * kk;
+    const int kr = min(min(k, len), (int)C);
+    if (kCandOut && kr == 0) {
+        fill_slots(out_val, out_idx, obase, 0, min(k, len));
+        return;
+    }
+    // radix select of the kr-th largest key: 11, 11 and 10 bit digits
+    uint32_t prefix = 0u, need = (uint32_t)kr;
+    int shift = 32;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sd = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        if (pass > 0) {  // histogram of the keys under the prefix (pass 0's is built)
+            for (int i = tid; i < (int)C; i += kSelThreads) {
+                const uint32_t key = skey[i];
+                if ((key >> shift) == prefix) atomicAdd(&hist[(key >> sd) & (nb - 1)], 1u);
+            }
+            __syncthreads();
+        }
+        // thread t owns bins nb-1-8t .. nb-8-8t (largest first)
+        uint32_t c8[8], local = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int bin = nb - 1 - (8 * tid + e);
+            c8[e] = bin >= 0 ? hist[bin] : 0u;
+            local += c8[e];
+        }
+        uint32_t tot;
+        const uint32_t above = block256_prefix(local, sh[(pass + 1) & 1], &tot);
+        if (above < need && need <= above + local) {
+            uint32_t cum = above;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (cum < need && need <= cum + c8[e]) {
+                    pick[pass & 1][0] = (uint32_t)(nb - 1 - (8 * tid + e));
+                    pick[pass & 1][1] = cum;
+                    pick[pass & 1][2] = c8[e];
+                }
+                cum += c8[e];
+            }
+        }
+        // every thread has read hist: clear it for the next pass
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int bin = nb - 1 - (8 * tid + e);
+            if (bin >= 0) hist[bin] = 0u;
+        }
+        __syncthreads();
+        prefix = pass == 0 ? pick[0][0] : ((prefix << (pass == 1 ? 11 : 10)) | pick[pass & 1][0]);
+        need -= pick[pass & 1][1];
+        const uint32_t in_bin = pick[pass & 1][2];
+        shift = sd;
+        if (in_bin == need) break;
+    }
+    // ordered output: greater keys all win; of the keys equal to the prefix, the `need`
+    // first in token order
+    const int seg = ((int)C + kSelThreads - 1) / kSelThreads;
+    const int b0 = min((int)C, tid * seg), b1 = min((int)C, b0 + seg);
+    uint32_t gt = 0u, eq = 0u;
+    for (int i = b0; i < b1; ++i) {
+        const uint32_t kv = skey[i] >> shift;
+        gt += kv > prefix;
+        eq += kv == prefix;
+    }
+    uint32_t tot;
+    const uint32_t before = block256_prefix(gt | (eq << 16), sh[1], &tot);
+    const uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
+    const uint32_t eq_won_before = min(eqb, need);
+    uint32_t take = min(need - eq_won_before, eq);
+    int slot = (int)(gtb + eq_won_before);
+    for (int i = b0; i < b1; ++i) {
+        const uint32_t kv = skey[i] >> shift;
+        bool win = kv > prefix;
+        if (kv == prefix && take > 0u) {
+            win = true;
+            --take;
+        }
+        if (win) {
+            if (slot < kr) {
+                const int32_t index = (int32_t)(start + soff[i]);
+                if (kCandOut) {
+                    out_val[obase + slot] = key_value(skey[i]);
+                    out_idx[obase + slot] = index;
+                } else {
+                    out_idx[row * (int64_t)k + slot] = index;
+                }
+            }
+            ++slot;
+        }
+    }
+    if (kCandOut) fill_slots(out_val, out_idx, obase, kr, min(k, len));
 }
 
 template <bool kExplicit, bool kCandOut>
@@ -275,19 +645,39 @@ void launch_level(const float *vals, const int32_t *in_idx, int64_t len, int64_t
     const int nch = (int)((len + kTopkChunk - 1) / kTopkChunk);
     for (int r0 = 0; r0 < R; r0 += 65535) {
         const int rows = std::min(65535, R - r0);
-        hipLaunchKernelGGL((k_topk_chunk<kExplicit, kCandOut>), dim3(nch, rows),
+        hipLaunchKernelGGL((k_topk_chunk<kExplicit, kCandOut, false>), dim3(nch, rows),
                            dim3(kThreads), 0, s, vals, in_idx, len, in_stride, r0, k,
-                           out_val, out_idx, out_stride);
+                           out_val, out_idx, out_stride, FilterArgs{});
     }
 }
 
-}  // namespace
+// Level 0 of the filtered select: the lean select over every row chunk, then the full
+// select over the chunks it handed over.
+template <bool kCandOut>
+void launch_filtered_level(const float *cand, int64_t n, int R, int k, const FilterArgs &fa,
+                           uint32_t *list, float *out_val, int32_t *out_idx, int64_t out_stride,
+                           hipStream_t s) {
+    const int nch = (int)((n + kTopkChunk - 1) / kTopkChunk);
+    for (int r0 = 0; r0 < R; r0 += 65535) {
+        const int rows = std::min(65535, R - r0);
+        hipLaunchKernelGGL(k_select_kept<kCandOut>, dim3(nch, rows), dim3(kSelThreads), 0, s,
+                           cand, n, r0, k, fa, list, out_val, out_idx, out_stride);
+    }
+    const int grid = (int)std::min<int64_t>((int64_t)R * nch, kRedoGrid);
+    hipLaunchKernelGGL(k_topk_redo<kCandOut>, dim3(grid), dim3(kThreads), 0, s, cand, n, k,
+                       out_val, out_idx, out_stride, fa, list, nch);
+}
 
-hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
-                       hipStream_t s) {
+// Levels over R rows of n entries; the first reads either plain scores or (with a redo
+// list) the filtering scan's candidates.
+hipError_t run_levels(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
+                      hipStream_t s, const FilterArgs &fa, uint32_t *list) {
     const TopkLevels L = topk_levels(n, k);
     if (L.n_levels == 0) {
-        launch_level<false, false>(scores, nullptr, n, n, R, k, nullptr, idx, 0, s);
+        if (list)
+            launch_filtered_level<false>(scores, n, R, k, fa, list, nullptr, idx, 0, s);
+        else
+            launch_level<false, false>(scores, nullptr, n, n, R, k, nullptr, idx, 0, s);
         return hipGetLastError();
     }
     const size_t one = topk_ws_bytes(R, n, k) / (L.n_levels >= 2 ? 2 : 1);
@@ -299,7 +689,9 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
         const int64_t os = level_stride(cin, k);
         float *ov = reinterpret_cast<float *>(buf[l & 1]);
         int32_t *oi = reinterpret_cast<int32_t *>(buf[l & 1] + (size_t)R * os * 4);
-        if (l == 0)
+        if (l == 0 && list)
+            launch_filtered_level<true>(in_val, cin, R, k, fa, list, ov, oi, os, s);
+        else if (l == 0)
             launch_level<false, true>(in_val, nullptr, cin, in_stride, R, k, ov, oi, os, s);
         else
             launch_level<true, true>(in_val, in_i, cin, in_stride, R, k, ov, oi, os, s);
@@ -310,6 +702,28 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
     }
     launch_level<true, false>(in_val, in_i, cin, in_stride, R, k, nullptr, idx, 0, s);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
+                       hipStream_t s) {
+    return run_levels(scores, R, n, k, idx, ws, s, FilterArgs{}, nullptr);
+}
+
+hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand,
+                                const uint32_t *masks, void *scan_ws, uint32_t *redo_list,
+                                int k, int32_t *idx, void *ws, hipStream_t s) {
+    FilterArgs fa;
+    fa.masks = masks;
+    fa.scan_ws = static_cast<const char *>(scan_ws);
+    fa.planes = st.planes;
+    fa.word_stride = st.word_stride;
+    fa.W = (st.n_tokens + 31) / 32;
+    fa.G = G;
+    fa.H = st.n_heads;
+    fa.qs = query_sets(G);
+    return run_levels(cand, st.n_heads * G, st.n_tokens, k, idx, ws, s, fa, redo_list);
 }
 
 }  // namespace fathom

@@ -23,7 +23,7 @@ TOPK_CHUNK = 32768
 
 OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_MAPPED, ERR_HIP = \
     range(7)
-OP_QUANTIZE, OP_SCAN, OP_TOPK, OP_STEP = range(4)
+OP_QUANTIZE, OP_SCAN, OP_TOPK, OP_STEP, OP_SCAN_TOPK = range(5)
 
 
 class FathomError(RuntimeError):
@@ -54,6 +54,7 @@ _SIGS = {
     "fathom_scan": (_I, [ctypes.POINTER(fathom_store), _P, _I, _P, _P, _P, _SZ, _P]),
     "fathom_scan_prepare": (_I, [ctypes.POINTER(fathom_store), _P, _I, _P, _P, _SZ, _P]),
     "fathom_scan_prepared": (_I, [ctypes.POINTER(fathom_store), _I, _P, _P, _SZ, _P]),
+    "fathom_scan_topk": (_I, [ctypes.POINTER(fathom_store), _P, _I, _P, _I, _P, _P, _SZ, _P]),
     "fathom_topk": (_I, [_P, _I, _I, _I, _P, _P, _SZ, _P]),
     "fathom_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P]),
     "fathom_step": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I, ctypes.c_float,
@@ -242,6 +243,24 @@ def fathom_scan_prepared(store: Store, G: int, scores, ws, stream=None):
                                       ws.numel() * ws.element_size(), _stream(stream)),
            "fathom_scan_prepared")
     return scores
+
+
+def scan_topk_workspace(store: Store, G: int, k: int, device):
+    return _workspace(workspace_size(OP_SCAN_TOPK, store.n_heads, G, store.n_tokens, k), device)
+
+
+def fathom_scan_topk(store: Store, q, depth, k: int, idx=None, ws=None, stream=None):
+    """Scan + top-k without writing every score -> idx [H][G][k] int32."""
+    import torch
+    H, G, _ = q.shape
+    if idx is None:
+        idx = torch.empty((H, G, k), dtype=torch.int32, device=q.device)
+    ws = scan_topk_workspace(store, G, k, q.device) if ws is None else ws
+    st = store.descriptor()
+    _check(lib().fathom_scan_topk(ctypes.byref(st), _ptr(q), G, _ptr(depth), int(k), _ptr(idx),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "fathom_scan_topk")
+    return idx
 
 
 def fathom_topk(scores, k: int, idx=None, ws=None, stream=None):

@@ -87,7 +87,8 @@ enum fathom_op {
     FATHOM_OP_QUANTIZE = 0, /* fathom_quantize_store: uses H, n */
     FATHOM_OP_SCAN = 1,     /* fathom_scan / fathom_scan_prepare(d): uses H, G */
     FATHOM_OP_TOPK = 2,     /* fathom_topk: uses H as the row count R, n, k */
-    FATHOM_OP_STEP = 3      /* fathom_step: uses H, G, n, k */
+    FATHOM_OP_STEP = 3,     /* fathom_step: uses H, G, n, k */
+    FATHOM_OP_SCAN_TOPK = 4 /* fathom_scan_topk: uses H, G, n, k */
 };
 
 /* Bytes of workspace `op` needs for the given sizes (0 is possible).  Status only. */
@@ -175,6 +176,23 @@ int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uin
                         float *scores, void *stream);
 
 /*
+ * Scan and top-k in one call, without writing every score (blog, "The first fix":
+ * score every key, keep the top k; "That is the whole method": the scan feeds the
+ * select).  Same inputs as fathom_scan; idx [H][G][k] int32 out, exactly what
+ * fathom_scan followed by fathom_topk gives (same order and tie rule).
+ * How: the prepare step guesses, per query, a score threshold from a sample of the
+ * head's tokens; the scan writes only the scores whose key clears it, compacted, with a
+ * bit mask of the kept tokens and a per-query count; the select reads only those.  A
+ * threshold is safe whenever at least k tokens of the row clear it (every winner then
+ * clears it); a row that kept fewer is rescored in full inside the select, from the
+ * store, with the scan's own integer arithmetic, so the result never depends on the
+ * guess.  1 <= k <= n, with fathom_topk's limits.  ws: FATHOM_OP_SCAN_TOPK bytes (the
+ * prepared scan workspace comes first).
+ */
+int fathom_scan_topk(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                     int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Top k of each row (blog, "The first fix": take the top k).
  *   scores [R][n] fp32, finite; idx [R][k] int32 out, ascending by token index.
  * Order: score descending, then token index ascending (equal scores go to the lower
@@ -201,7 +219,9 @@ int fathom_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int
  * all enqueued on `stream` with no host synchronization (blog, "That is the whole
  * method"; Rootconf: sync-free accounting).  Same arguments as the calls above.
  * depth_out [H][d], scores_out [H][G][n] and idx_out [H][G][k] are optional (NULL: the
- * intermediate lives in ws).  ws: FATHOM_OP_STEP bytes.
+ * intermediate lives in ws).  Without scores_out the scan and the select run as in
+ * fathom_scan_topk (only candidate scores are written); with it every score is written
+ * and selected from.  The winners are the same either way.  ws: FATHOM_OP_STEP bytes.
  */
 int fathom_step(const fathom_store *st, const float *q, const uint16_t *K,
                 const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,

@@ -88,6 +88,19 @@ def test_scan_checks():
                                  None) == F.ERR_INVALID_ARG
 
 
+def test_scan_topk_checks():
+    L = F.lib()
+    st = _st()
+    need = F.workspace_size(F.OP_SCAN_TOPK, 2, 4, 100, 10)
+    args = lambda G, k, ws, ws_bytes: (ctypes.byref(st), FAKE, G, FAKE, k, FAKE, ws, ws_bytes,
+                                       None)
+    assert L.fathom_scan_topk(*args(4, 10, FAKE, need - 1)) == F.ERR_WORKSPACE
+    assert L.fathom_scan_topk(*args(4, 101, FAKE, need)) == F.ERR_INVALID_ARG
+    assert L.fathom_scan_topk(*args(4, 0, FAKE, need)) == F.ERR_INVALID_ARG
+    assert L.fathom_scan_topk(*args(9, 10, FAKE, need)) == F.ERR_UNSUPPORTED
+    assert L.fathom_scan_topk(*args(4, 10, None, need)) == F.ERR_INVALID_ARG
+
+
 def test_topk_checks():
     L = F.lib()
     assert L.fathom_topk(FAKE, 4, 100, 0, FAKE, None, 0, None) == F.ERR_INVALID_ARG
@@ -141,6 +154,16 @@ def test_workspace_formulas():
     assert F.workspace_size(F.OP_TOPK, 1152, 1, 32768, 512) == 0
     # 1M tokens: 32 chunks x 512 candidates x (4 + 4) bytes per row, one level
     assert F.workspace_size(F.OP_TOPK, 32, 1, 1 << 20, 512) == 32 * 32 * 512 * 8
+    # scan + top-k: scan workspace, candidate buffer (4 bytes per score), kept-token
+    # masks (4 bytes per 32 tokens), the top-k levels and the redo list (4 bytes per row
+    # chunk), each rounded up to 256 bytes
+    r256 = lambda x: (x + 255) // 256 * 256
+    for H, G, n, k in [(2, 4, 100, 10), (288, 4, 32768, 512), (3, 8, 70000, 512)]:
+        want = (r256(F.workspace_size(F.OP_SCAN, H, G)) + r256(H * G * n * 4) +
+                r256(H * G * ((n + 31) // 32) * 4) +
+                r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
+                r256(H * G * ((n + 32767) // 32768) * 4))
+        assert F.workspace_size(F.OP_SCAN_TOPK, H, G, n, k) == want
     # quantize: min/max partials + integer sums
     q = F.workspace_size(F.OP_QUANTIZE, 2, 1, 4096, 1)
     assert q == 2 * 2 * 2 * 128 * 4 + 2 * 128 * 16

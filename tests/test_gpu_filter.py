@@ -1,0 +1,162 @@
+"""The candidate-filtering scan + select (fathom_scan_topk, and fathom_step without
+scores_out) against the full scan + top-k.
+
+Bar: the index sets are bit-exact with the oracle's top-k of the full scan's scores (the
+full scan itself is held to the oracle's scores in test_gpu_parity).  The filter's
+threshold is a guess; the cases below also force the guess to fail (rows keep fewer than
+k tokens), which the select must repair by rescoring, and check through the workspace's
+per-query counts that both the filtering and the repair actually ran.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_plane_kv_amd import fathom as F
+
+from gpu_util import bf16_to_f32, inputs, store_from_keys, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+META_BYTES = 4096
+CNT_OFFSET = 16 + 3 * 32   # int32 x4, then C[8], S[8], tkey[8]; cnt[8] follows
+
+
+def _kept_counts(ws, H, G):
+    """Per-(head, query) kept-token counts from the prepared scan workspace."""
+    raw = ws[:H * META_BYTES].cpu().numpy().view(np.uint8).reshape(H, META_BYTES)
+    return raw[:, CNT_OFFSET:CNT_OFFSET + 32].copy().view(np.uint32)[:, :G]
+
+
+def _depth(kind, st, q_t, H, n):
+    torch = torch_cuda()
+    if kind == "plan92":
+        return F.fathom_plan(st, q_t, 92)
+    if kind == "b0":
+        return torch.zeros((H, 128), dtype=torch.uint8, device="cuda")
+    if kind == "b512":
+        return torch.full((H, 128), 4, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(n)
+    return to_dev(rng.integers(0, 5, (H, 128)).astype(np.uint8))
+
+
+def _sample_words(W):
+    """Words the threshold sample reads: every word of a short row, else 8 runs of 4
+    words at 4 * floor(r (W // 4 - 1) / 7)."""
+    if W <= 32:
+        return np.arange(W)
+    return np.concatenate([4 * (r * (W // 4 - 1) // 7) + np.arange(4) for r in range(8)])
+
+
+def _filters(n, k):
+    """Whether the sample yields a threshold: its rank m (least m with
+    n (m - 5 sqrt(m)) / S >= k) must not exceed the S sampled tokens."""
+    W = (n + 31) // 32
+    toks = (_sample_words(W)[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    S = int((toks < n).sum())
+    x = 0.5 * (5.0 + np.sqrt(25.0 + 4.0 * k * S / n))
+    return np.ceil(x * x) <= S
+
+
+def _run(keys, q, k, kind):
+    torch = torch_cuda()
+    H, G, _ = q.shape
+    n = keys.shape[1]
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    depth = _depth(kind, st, q_t, H, n)
+    full = F.fathom_scan(st, q_t, depth)
+    ws = F.scan_topk_workspace(st, G, k, "cuda")
+    idx = F.fathom_scan_topk(st, q_t, depth, k, ws=ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().reshape(H * G, k)
+    ref = oracle.topk(full.cpu().numpy().reshape(H * G, n), k)
+    assert np.array_equal(got, ref)
+    return _kept_counts(ws, H, G)
+
+
+@pytest.mark.parametrize("H,G,n,k,kind", [
+    (3, 4, 5000, 64, "plan92"),       # sampled runs (more than 64 words)
+    (2, 8, 4096, 100, "random"),      # two query sets
+    (1, 3, 33, 5, "plan92"),          # every word sampled
+    (2, 1, 32768, 512, "plan92"),     # the Qwen3-8B row length
+    (1, 2, 70000, 512, "plan92"),     # several chunks: candidate levels with filler
+    (2, 4, 12345, 1, "random"),       # k = 1
+    (1, 4, 2000, 2000, "plan92"),     # k = n: no threshold
+    (2, 4, 3000, 50, "b0"),           # every score equal: ties to the lower index
+    (2, 4, 9000, 300, "b512"),
+    (1, 5, 40000, 16384, "plan92"),   # the largest k with several chunks
+])
+def test_scan_topk_matches_full_scan(H, G, n, k, kind):
+    print(f"[scan_topk] H={H} G={G} n={n} k={k} {kind}", flush=True)
+    keys, q, _, _ = inputs(100, H, G, n)
+    cnt = _run(keys, q, k, kind)
+    if not _filters(n, k):   # k too close to n: the call scans everything
+        return
+    assert (cnt >= k).all() or kind == "random"   # a random depth may need the repair
+    if n == 32768 and kind == "plan92":   # the filter keeps a small share of the row
+        assert cnt.max() <= n // 8
+
+
+def _boost_sampled_tokens(keys, q):
+    """Make the tokens the threshold sample reads the best of their rows, so that the
+    sampled quantile sits far above the row's k-th score and few tokens clear it."""
+    H, n, _ = keys.shape
+    W = (n + 31) // 32
+    toks = (_sample_words(W)[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    toks = toks[toks < n]
+    out = keys.copy()
+    for h in range(H):
+        d = q[h].sum(axis=0)
+        out[h, toks, :] += 6.0 * d / np.linalg.norm(d) * np.abs(keys[h]).max()
+    return out
+
+
+@pytest.mark.parametrize("H,G,n,k", [(2, 4, 32768, 512), (1, 2, 70000, 512),
+                                     (1, 8, 9000, 300)])
+def test_scan_topk_repairs_rows_that_kept_too_few(H, G, n, k):
+    print(f"[scan_topk repair] H={H} G={G} n={n} k={k}", flush=True)
+    keys, q, _, _ = inputs(101, H, G, n)
+    keys = _boost_sampled_tokens(keys, q)
+    cnt = _run(keys, q, k, "plan92")
+    assert (cnt < k).any()   # the repair ran on at least one row
+
+
+def test_step_filtered_equals_step_full():
+    torch = torch_cuda()
+    H, G, n, B, k = 4, 4, 20000, 92, 256
+    print(f"[step filtered] H={H} G={G} n={n} B={B} k={k}", flush=True)
+    keys, q, K, V = inputs(102, H, G, n)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    scores = torch.empty((H, G, n), dtype=torch.float32, device="cuda")
+    i1 = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    o1 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, scores_out=scores, idx_out=i1)
+    o2 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
+    got = i2.cpu().numpy().reshape(H * G, k)
+    assert np.array_equal(got, oracle.topk(scores.cpu().numpy().reshape(H * G, n), k))
+    ref_out = oracle.attention(q, K, V, i2.cpu().numpy(), sm)
+    assert np.abs(bf16_to_f32(o2) - ref_out).max() <= 2e-2
+
+
+def test_scan_topk_host_resident_store():
+    torch = torch_cuda()
+    H, G, n, k = 2, 4, 20000, 128
+    print(f"[scan_topk host] H={H} G={G} n={n} k={k}", flush=True)
+    keys, q, _, _ = inputs(103, H, G, n)
+    st_d, _ = store_from_keys(keys)
+    W = ((n + 31) // 32 + 3) // 4 * 4
+    pinned = torch.empty((H, 128, 4, W), dtype=torch.int32, pin_memory=True)
+    st_h, _ = store_from_keys(keys, planes=pinned)
+    q_t = to_dev(q)
+    depth = F.fathom_plan(st_d, q_t, 92)
+    a = F.fathom_scan_topk(st_d, q_t, depth, k)
+    b = F.fathom_scan_topk(st_h, q_t, depth, k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
