@@ -12,8 +12,10 @@ timing starts.  Before timing, sampled heads are checked against the CPU oracle.
 
 Prints ONE JSON line: value = keys ranked per second over the whole step (Gkeys/s);
 roofline = the scan kernel's algorithmic bytes (planes read + fp32 scores written) per
-launch / its mean launch time, against 8 TB/s; cpu_baseline = the oracle on the host
-cores over a bounded sample of heads.
+launch / its mean launch time, against 8 TB/s (the scan in its full-score form,
+fathom_scan; the step itself runs the fused form, which writes only the candidate scores
+that clear a sampled threshold, and is checked to give the same winners); cpu_baseline =
+the oracle on the host cores over a bounded sample of heads.
 """
 from __future__ import annotations
 
@@ -45,7 +47,7 @@ def parse():
                     help="target wall time of the oracle sample")
     ap.add_argument("--kernel", default=None,
                     choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136",
-                             "scan_extract"],
+                             "scan_extract", "scan_topk"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--no-host", action="store_true",
@@ -139,6 +141,17 @@ def main():
     torch.cuda.synchronize()
     parity = check_sample(st, q_np, K, V, depth, scores, idx, out, sample_keys, B, k,
                           sm_scale)
+    # the timed step runs the fused scan -> select: its winners and output must be those
+    # of the full scan + top-k just checked, for every head
+    idx_f = torch.empty_like(idx)
+    out_f = torch.empty_like(out)
+    F.fathom_step(st, q, K, V, B, k, sm_scale, out=out_f, idx_out=idx_f, ws=ws)
+    torch.cuda.synchronize()
+    parity["fused_equals_full"] = bool(torch.equal(idx_f, idx) and torch.equal(out_f, out))
+    parity["ok"] = bool(parity["ok"] and parity["fused_equals_full"])
+    kept = ws[:H * 4096].view(torch.int32).view(H, 1024)[:, 28:28 + G].float()
+    parity["kept_per_row_mean"] = round(float(kept.mean()), 1)
+    parity["kept_per_row_max"] = int(kept.max())
     log(f"[bench] parity on heads {sample_heads}: {parity}")
 
     # ---------------- timed region: K whole steps ----------------
@@ -169,7 +182,7 @@ def main():
     traffic = load_traffic(scan_bytes)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "k_scan_main<1,false>",
+                "traffic": traffic, "kernel": "k_scan_main<1,false,false>",
                 "algorithmic_bytes_per_launch": int(scan_bytes)}
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
@@ -195,7 +208,10 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
         "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
-        "bytes_per_step": {"planes": int(plane_bytes), "scores_written": int(score_bytes),
+        "bytes_per_step": {"planes": int(plane_bytes),
+                           "candidate_scores_written": int(4 * H * G * parity["kept_per_row_mean"]),
+                           "kept_masks_written": int(H * G * ((n + 31) // 32) * 4),
+                           "scores_written_by_full_scan": int(score_bytes),
                            "winner_rows": int(H * G * k * 512)},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "parity_before_timing": parity,
@@ -254,11 +270,15 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     F.fathom_scan_prepare(st, q, depth, scan_ws)
     F.fathom_scan_prepared(st, G, scores, scan_ws)
     F.fathom_topk(scores, k, idx=idx)
+    stk_ws = F.scan_topk_workspace(st, G, k, dev)
+    idx2 = torch.empty_like(idx)
     calls = {
         "plan_ms": lambda: F.fathom_plan(st, q, B, depth=depth),
         "scan_prepare_ms": lambda: F.fathom_scan_prepare(st, q, depth, scan_ws),
         "scan_ms": lambda: F.fathom_scan_prepared(st, G, scores, scan_ws),
         "topk_ms": lambda: F.fathom_topk(scores, k, idx=idx),
+        # the fused form: prepare with thresholds, filtering scan, select of candidates
+        "scan_topk_ms": lambda: F.fathom_scan_topk(st, q, depth, k, idx=idx2, ws=stk_ws),
         "attn_ms": lambda: F.fathom_sparse_attn(q, K, V, idx, sm, out=out),
         # comparator: the same scores by per-bit extraction on the integer units
         "scan_extract_ms": lambda: F.fathom_scan_extract(st, q, depth, scores=scores),
@@ -461,6 +481,7 @@ def host_model(args, name, L):
     sws = F.scan_workspace(st_h, G, dev)
     tneed = F.workspace_size(F.OP_TOPK, H * G, 1, n, k)
     tws = torch.empty(max(tneed, 1), dtype=torch.uint8, device=dev)
+    stk_ws = F.scan_topk_workspace(st_h, G, k, dev)
     log(f"[bench] {name}: pinned store of {planes_h.numel() * 4 / 1e9:.2f} GB ready in "
         f"{time.time() - t0:.1f}s")
 
@@ -487,6 +508,13 @@ def host_model(args, name, L):
         step()
         torch.cuda.synchronize()
         step_ms = timed_ms(step, stream, reps, flush, sink)
+
+        def step_fused():
+            plan()
+            F.fathom_scan_topk(st_h, q, depth, k, idx=idx, ws=stk_ws)
+        step_fused()
+        torch.cuda.synchronize()
+        fused_ms = timed_ms(step_fused, stream, reps, flush, sink)
         F.fathom_scan_prepare(st_h, q, depth, sws)
         scan_ms = timed_ms(lambda: F.fathom_scan_prepared(st_h, G, scores, sws), stream, reps,
                            flush, sink)
@@ -495,16 +523,21 @@ def host_model(args, name, L):
         pb = planes_read / 8 * n * H
         gbps = pb / (scan_ms * 1e-3) / 1e9
         res["budgets"][str(b)] = {
-            "step_ms_plan_scan_topk": round(step_ms, 3), "scan_ms": round(scan_ms, 3),
+            "step_ms_plan_scan_topk": round(step_ms, 3),
+            "step_ms_plan_fused_scan_topk": round(fused_ms, 3), "scan_ms": round(scan_ms, 3),
             "topk_ms": round(topk_ms, 3), "scan_plane_bytes": int(pb),
             "scan_plane_GBps": round(gbps, 2), "scan_frac_of_link": round(gbps / L["L_GBps"], 4),
             "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 2),
             "score_bytes_in_hbm": int(4 * G * n * H)}
-        log(f"[bench] {name} B={b}: step {step_ms:.2f} ms, scan {scan_ms:.2f} ms = "
+        log(f"[bench] {name} B={b}: step {step_ms:.2f} ms (fused {fused_ms:.2f} ms), "
+            f"scan {scan_ms:.2f} ms = "
             f"{gbps:.1f} GB/s of planes ({gbps / L['L_GBps']:.0%} of L)")
     del flush
     if "fixed136" in res["budgets"] and "92" in res["budgets"]:
         r = res["budgets"]
+        res["speedup_b92_vs_fixed136_fused_step"] = round(
+            r["fixed136"]["step_ms_plan_fused_scan_topk"] /
+            r["92"]["step_ms_plan_fused_scan_topk"], 3)
         res["speedup_b92_vs_fixed136_step"] = round(r["fixed136"]["step_ms_plan_scan_topk"] /
                                                      r["92"]["step_ms_plan_scan_topk"], 3)
     # oracle check of one sampled head at B = 92
