@@ -54,6 +54,7 @@ def _load():
     sig = {
         "oracle_quantize_batch": (None, [P, I, I, I, P, P, P]),
         "oracle_pack_planes_batch": (None, [P, I, I, I, I, P]),
+        "oracle_pack_nibbles_batch": (None, [P, I, I, I, P]),
         "oracle_var_batch": (None, [P, P, I, I, I, P]),
         "oracle_plan_batch": (I, [P, P, I, I, I, I, P]),
         "oracle_plan_fixed": (I, [P, I, I, P]),
@@ -130,6 +131,18 @@ def pack_planes(codes, W: int | None = None):
     planes = np.empty((H, d, PLANES, W), np.uint32)
     _load().oracle_pack_planes_batch(_p(cd), H, n, d, W, _p(planes))
     return planes[0] if squeeze else planes
+
+
+def pack_nibbles(codes):
+    """codes u8 [H][n][d] -> token-major nibbles u8 [H][n][d/2] (channel 2j low, 2j+1 high)."""
+    cd = _c(codes, np.uint8)
+    squeeze = cd.ndim == 2
+    if squeeze:
+        cd = cd[None]
+    H, n, d = cd.shape
+    nib = np.empty((H, n, d // 2), np.uint8)
+    _load().oracle_pack_nibbles_batch(_p(cd), H, n, d, _p(nib))
+    return nib[0] if squeeze else nib
 
 
 def plane_prefix(planes_head, c: int, t: int, i: int) -> int:

@@ -87,6 +87,21 @@ void oracle_pack_planes(const uint8_t *codes, int n, int d, int W, uint32_t *pla
             }
 }
 
+/* The ordinary layout the pages compare against (blog, "Where this does not work":  */
+/* a plain 4-bit scan reads each 4-bit number whole).  Token-major, two channels a   */
+/* byte: byte j of token i holds the code of channel 2j in its low four bits and     */
+/* that of channel 2j+1 in its high four bits (the order within the byte is not      */
+/* stated; this one is the plainest).  Layout [i][d/2], d even.                      */
+void oracle_pack_nibbles(const uint8_t *codes, int n, int d, uint8_t *nib)
+{
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < d / 2; ++j) {
+            const uint8_t lo = codes[(size_t)i * d + 2 * j] & 15u;
+            const uint8_t hi = codes[(size_t)i * d + 2 * j + 1] & 15u;
+            nib[(size_t)i * (d / 2) + j] = (uint8_t)(lo | (hi << 4));
+        }
+}
+
 /* Inverse of the packing, for one channel at read depth t (0..4): the t-plane      */
 /* prefix p of token i, i.e. the integer whose bits are planes 0..t-1 (blog, "Bit   */
 /* planes": reading planes 0 and 1 gives every number rounded to 2 bits).           */
@@ -363,6 +378,13 @@ void oracle_pack_planes_batch(const uint8_t *codes, int H, int n, int d, int W,
     for (int h = 0; h < H; ++h)
         oracle_pack_planes(codes + (size_t)h * n * d, n, d, W,
                            planes + (size_t)h * d * ORACLE_PLANES * W);
+}
+
+void oracle_pack_nibbles_batch(const uint8_t *codes, int H, int n, int d, uint8_t *nib)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h)
+        oracle_pack_nibbles(codes + (size_t)h * n * d, n, d, nib + (size_t)h * n * (d / 2));
 }
 
 void oracle_var_batch(const uint8_t *codes, const float *scale, int H, int n, int d,

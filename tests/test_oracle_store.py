@@ -153,3 +153,28 @@ def test_batched_quantize_equals_per_head():
     for h in range(3):
         s1, z1, c1 = oracle.quantize(x[h])
         assert (s1 == s[h]).all() and (z1 == z[h]).all() and (c1 == codes[h]).all()
+
+
+@settings(max_examples=15, deadline=None)
+@given(n=st.integers(1, 200), seed=st.integers(0, 2**31 - 1))
+def test_nibbles_hold_the_four_plane_prefix(n, seed):
+    """The ordinary token-major layout (blog, "Where this does not work": the plain 4-bit
+    scan reads each number whole) holds, for every token and channel, the same number the
+    bit planes give when all four are read: checked against the plane packing and its
+    prefix, which the pages' diagram pins."""
+    d = 6
+    x = _keys(n, d, seed)
+    _, _, codes = oracle.quantize(x)
+    nib = oracle.pack_nibbles(codes)
+    planes = oracle.pack_planes(codes)
+    assert nib.shape == (n, d // 2) and nib.dtype == np.uint8
+    for i in range(n):
+        for c in range(d):
+            byte = int(nib[i, c // 2])
+            number = (byte >> 4) if c % 2 else (byte & 15)
+            assert number == oracle.plane_prefix(planes, c, 4, i), (i, c)
+
+
+def test_nibble_store_is_64_bytes_per_token_at_d128():
+    codes = np.zeros((3, 128), np.uint8)
+    assert oracle.pack_nibbles(codes).nbytes == 3 * 64
