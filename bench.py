@@ -47,7 +47,7 @@ def parse():
                     help="target wall time of the oracle sample")
     ap.add_argument("--kernel", default=None,
                     choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136",
-                             "scan_extract", "scan_topk"],
+                             "scan_extract", "scan_topk", "scan_nibble", "scan_b512"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--no-host", action="store_true",
@@ -272,6 +272,7 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     F.fathom_topk(scores, k, idx=idx)
     stk_ws = F.scan_topk_workspace(st, G, k, dev)
     idx2 = torch.empty_like(idx)
+    nib = F.fathom_pack_nibbles(st)  # the ordinary 4-bit layout, 64 B per token
     calls = {
         "plan_ms": lambda: F.fathom_plan(st, q, B, depth=depth),
         "scan_prepare_ms": lambda: F.fathom_scan_prepare(st, q, depth, scan_ws),
@@ -282,6 +283,9 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
         "attn_ms": lambda: F.fathom_sparse_attn(q, K, V, idx, sm, out=out),
         # comparator: the same scores by per-bit extraction on the integer units
         "scan_extract_ms": lambda: F.fathom_scan_extract(st, q, depth, scores=scores),
+        # comparator: the plain 4-bit scan over the ordinary layout (every channel whole)
+        "scan_nibble_ms": lambda: F.fathom_scan_nibble(nib, st.scale, st.zero, q,
+                                                        scores=scores),
     }
     res = {}
 
@@ -297,6 +301,10 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
             tot += a.elapsed_time(b)
         return tot / reps
 
+    if only == "scan_b512":
+        full = torch.full((H, 128), 4, dtype=torch.uint8, device=dev)
+        F.fathom_scan_prepare(st, q, full, scan_ws)
+        return {"scan_b512_ms": timed(lambda: F.fathom_scan_prepared(st, G, scores, scan_ws))}
     if only == "scan_fixed136":
         fixed = F.fathom_plan_fixed(st, 34)
         F.fathom_scan_prepare(st, q, fixed, scan_ws)
@@ -313,6 +321,10 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     fixed = F.fathom_plan_fixed(st, 34)
     F.fathom_scan_prepare(st, q, fixed, scan_ws)
     res["scan_fixed136_ms"] = timed(lambda: F.fathom_scan_prepared(st, G, scores, scan_ws))
+    # every plane of every channel: the same numbers the nibble scan computes
+    full = torch.full((H, 128), 4, dtype=torch.uint8, device=dev)
+    F.fathom_scan_prepare(st, q, full, scan_ws)
+    res["scan_b512_ms"] = timed(lambda: F.fathom_scan_prepared(st, G, scores, scan_ws))
     # HBM streaming-read rate of this device (1 GiB, warm launch) for context
     F.fathom_stream_read(flush, flush.numel(), sink)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

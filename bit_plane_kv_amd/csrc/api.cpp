@@ -214,6 +214,24 @@ int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uin
     return hip_status(launch_scan_extract(*st, q, G, depth, scores, as_stream(stream)));
 }
 
+int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream) {
+    FATHOM_TRY(check_store(st));
+    if (!nib || !aligned(nib, 16)) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({st->planes, nib}));
+    return hip_status(launch_pack_nibbles(*st, nib, as_stream(stream)));
+}
+
+int fathom_scan_nibble(const uint8_t *nib, const float *scale, const float *zero, int H, int n,
+                       const float *q, int G, float *scores, void *stream) {
+    if (!nib || !scale || !zero || !q || !scores || H < 1 || n < 1) return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_g(G));
+    if (!aligned(nib, 16) || !aligned(q, 4) || !aligned(scores, 4) || !aligned(scale, 4) ||
+        !aligned(zero, 4))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({nib, scale, zero, q, scores}));
+    return hip_status(launch_scan_nibble(nib, scale, zero, H, n, q, G, scores, as_stream(stream)));
+}
+
 int fathom_scan(const fathom_store *st, const float *q, int G, const uint8_t *depth,
                 float *scores, void *ws, size_t ws_bytes, void *stream) {
     FATHOM_TRY(scan_common(st, G, ws, ws_bytes));

@@ -140,6 +140,9 @@ hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *
                             hipStream_t s, uint32_t *masks = nullptr);
 hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, float *scores, hipStream_t s);
+hipError_t launch_pack_nibbles(const fathom_store &st, uint8_t *nib, hipStream_t s);
+hipError_t launch_scan_nibble(const uint8_t *nib, const float *scale, const float *zero, int H,
+                              int n, const float *q, int G, float *scores, hipStream_t s);
 hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
                        hipStream_t s);
 // top-k of the filtering scan's candidates (rows = H*G); rows that kept fewer than k

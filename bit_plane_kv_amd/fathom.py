@@ -60,6 +60,8 @@ _SIGS = {
     "fathom_step": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I, ctypes.c_float,
                          _P, _P, _P, _P, _P, _SZ, _P]),
     "fathom_scan_extract": (_I, [_P, _P, _I, _P, _P, _P]),
+    "fathom_pack_nibbles": (_I, [ctypes.POINTER(fathom_store), _P, _P]),
+    "fathom_scan_nibble": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P]),
     "fathom_stream_read": (_I, [_P, _SZ, _P, _P]),
     "fathom_stream_read_runs": (_I, [_P, _SZ, _SZ, _SZ, _P, _P]),
     "fathom_host_alloc": (_I, [_SZ, _I, ctypes.POINTER(ctypes.c_void_p)]),
@@ -226,6 +228,30 @@ def fathom_scan_extract(store: Store, q, depth, scores=None, stream=None):
     st = store.descriptor()
     _check(lib().fathom_scan_extract(ctypes.byref(st), _ptr(q), G, _ptr(depth), _ptr(scores),
                                      _stream(stream)), "fathom_scan_extract")
+    return scores
+
+
+def fathom_pack_nibbles(store: Store, nib=None, stream=None):
+    """The store's codes in the ordinary token-major layout: uint8 [H][n][64]."""
+    import torch
+    if nib is None:
+        nib = torch.empty((store.n_heads, store.n_tokens, D // 2), dtype=torch.uint8,
+                          device=store.var.device)
+    st = store.descriptor()
+    _check(lib().fathom_pack_nibbles(ctypes.byref(st), _ptr(nib), _stream(stream)),
+           "fathom_pack_nibbles")
+    return nib
+
+
+def fathom_scan_nibble(nib, scale, zero, q, scores=None, stream=None):
+    """Plain 4-bit scan of nibble-packed codes [H][n][64] -> scores [H][G][n] fp32."""
+    import torch
+    H, n, _ = nib.shape
+    G = q.shape[1]
+    if scores is None:
+        scores = torch.empty((H, G, n), dtype=torch.float32, device=q.device)
+    _check(lib().fathom_scan_nibble(_ptr(nib), _ptr(scale), _ptr(zero), H, n, _ptr(q), G,
+                                    _ptr(scores), _stream(stream)), "fathom_scan_nibble")
     return scores
 
 

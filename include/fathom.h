@@ -176,6 +176,27 @@ int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uin
                         float *scores, void *stream);
 
 /*
+ * The ordinary 4-bit layout the pages compare the bit planes against (blog, "Where this
+ * does not work": a plain 4-bit scan reads each number whole).  Writes the store's codes
+ * token-major, two channels a byte: nib [H][n][d/2] uint8, byte j of token i = code of
+ * channel 2j | code of channel 2j+1 << 4 (64 bytes per token at d = 128).  The codes are
+ * read from st->planes (all four planes), so both layouts hold the same numbers.
+ * nib: device memory, 16-byte aligned, caller-owned.
+ */
+int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream);
+
+/*
+ * The plain 4-bit scan over that layout (the comparator of "Where this does not work"):
+ * every channel read in full, score_g(i) = C_g + sum_c fl32(q_gc s_c) code_c(i), with
+ * C_g = sum_c q_gc z_c in fp64 (fixed tree order, rounded once) and the channel sum in
+ * fp32, ascending.  The same numbers as fathom_scan at depth 4 on every channel, up to
+ * fp32 rounding.  nib [H][n][d/2] as written by fathom_pack_nibbles (16-byte aligned);
+ * scale, zero [H][d] fp32 (the store's); q [H][G][d] fp32; scores [H][G][n] fp32 out.
+ */
+int fathom_scan_nibble(const uint8_t *nib, const float *scale, const float *zero, int H,
+                       int n, const float *q, int G, float *scores, void *stream);
+
+/*
  * Scan and top-k in one call, without writing every score (blog, "The first fix":
  * score every key, keep the top k; "That is the whole method": the scan feeds the
  * select).  Same inputs as fathom_scan; idx [H][G][k] int32 out, exactly what
