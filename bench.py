@@ -57,6 +57,10 @@ def parse():
                          "link sweep, full-model host-resident scans)")
     ap.add_argument("--no-host-models", action="store_true",
                     help="skip the full-model host-resident scans (n = 256k and 1M)")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the synthetic accuracy-per-byte sweep")
+    ap.add_argument("--accuracy-only", action="store_true",
+                    help="run only the synthetic accuracy-per-byte sweep")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --kernel: also run a 1 GiB streaming read and a 256 MiB "
                          "copy, whose byte counts scale the profiler's HBM counters")
@@ -80,6 +84,9 @@ def main():
 
     if args.host_only:
         print(json.dumps(host_lines(args)), flush=True)
+        return
+    if args.accuracy_only:
+        print(json.dumps(accuracy_sweep(args)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]
@@ -191,9 +198,13 @@ def main():
         cpu = cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm_scale, sample_keys)
 
     host = None
-    if not args.no_host:
+    acc = None
+    if not args.no_host or not args.no_accuracy:
         del K, V, st, ws, scores
         torch.cuda.empty_cache()
+    if not args.no_accuracy:
+        acc = accuracy_sweep(args)
+    if not args.no_host:
         host = host_lines(args)
 
     result = {
@@ -216,6 +227,7 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "parity_before_timing": parity,
         "host_resident": host,
+        "accuracy_per_byte": acc,
     }
     print(json.dumps(result), flush=True)
 
@@ -389,6 +401,76 @@ def link_rate(dev, stream, nbytes=1 << 30):
     del h, d
     return {"dma_h2d_GBps": round(dma, 2), "zero_copy_read_GBps": round(zc, 2),
             "L_GBps": round(max(dma, zc), 2)}
+
+
+ACC_BUDGETS = (16, 24, 32, 40, 48, 56, 64, 72, 80, 92, 104, 120, 136, 168, 200, 256, 512)
+
+
+def accuracy_sweep(args):
+    """Attention error against budget on a synthetic cache (blog, "Accuracy per byte": the
+    bits per token the per-query plan needs to match the attention error of the 136-bit
+    fixed-depth scans).  Four layers of the Qwen3-8B-shaped cache (32 KV heads x 4
+    queries, n = 32768, k = 512).  Error of a row = ||o - o_dense|| / ||o_dense||, o_dense =
+    softmax attention over all n tokens (fp32 arithmetic on the bf16 K/V rows).  For every
+    budget B the Fathom plan runs through fathom_step; the comparators are the 136-bit
+    fixed-depth scan (34 channels of largest variance, all four planes) and the exact
+    top-k (the k largest exact logits).  Synthetic keys and queries stand in for the
+    pages' five models, so this is a proxy for their 46-74-bit finding, not a check of it."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS["qwen3_8b_32k_hbm"]
+    heads = list(range(32))
+    H, G, n, k = len(heads), cfg.G, cfg.n, cfg.k
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    keys = synth.keys_torch(args.seed, cfg.cfg_id, heads, n, dev)
+    st = F.Store.empty(H, n, dev)
+    F.fathom_quantize_store(keys, st)
+    K = keys.to(torch.bfloat16)
+    del keys
+    V = synth.values_torch(args.seed, cfg.cfg_id, heads, n, dev)
+    sm = float(np.float32(1.0 / np.sqrt(128)))
+    fixed = F.fathom_plan_fixed(st, 34)
+    res = {"workload": "qwen3_8b_32k_hbm, layers 0-3 (32 KV heads x 4 queries)", "k": k,
+           "error": "mean over rows of ||o - o_dense|| / ||o_dense||"}
+    regimes = {"iid_queries": synth.queries_np(args.seed, cfg.cfg_id, heads, G),
+               "heavy_tailed_queries": synth.queries_heavy_np(args.seed, cfg.cfg_id, heads, G)}
+    for name, q_np in regimes.items():
+        q = torch.from_numpy(q_np).to(dev)
+        # dense reference, fp32 arithmetic, head by head
+        logits = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+        dense = torch.empty((H, G, 128), dtype=torch.float32, device=dev)
+        for h in range(H):
+            logits[h] = torch.matmul(q[h], K[h].float().t().contiguous()) * sm
+            dense[h] = torch.matmul(torch.softmax(logits[h], -1), V[h].float())
+        dn = dense.norm(dim=-1)
+
+        def err(out):
+            e = (out.float() - dense).norm(dim=-1) / dn
+            return {"mean": round(float(e.mean()), 5), "max": round(float(e.max()), 5)}
+
+        r = {"fathom": {}}
+        out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
+        for B in ACC_BUDGETS:
+            F.fathom_step(st, q, K, V, B, k, sm, out=out)
+            r["fathom"][str(B)] = err(out)
+        idx = F.fathom_topk(F.fathom_scan(st, q, fixed), k)
+        r["fixed136"] = err(F.fathom_sparse_attn(q, K, V, idx, sm))
+        top = torch.topk(logits, k, dim=-1).indices.sort(dim=-1).values.to(torch.int32)
+        r["exact_topk"] = err(F.fathom_sparse_attn(q, K, V, top.contiguous(), sm))
+        match = [B for B in ACC_BUDGETS
+                 if r["fathom"][str(B)]["mean"] <= r["fixed136"]["mean"]]
+        r["bits_to_match_fixed136"] = match[0] if match else None
+        r["bytes_ratio_vs_fixed136"] = round(136 / match[0], 2) if match else None
+        res[name] = r
+        log(f"[bench] accuracy ({name}): fixed-136 {r['fixed136']}, exact top-k "
+            f"{r['exact_topk']}, bits to match {r['bits_to_match_fixed136']}")
+        del logits, dense
+    log(f"[bench] accuracy sweep in {time.time() - t0:.1f}s")
+    del K, V, st
+    torch.cuda.empty_cache()
+    return res
 
 
 def host_lines(args):

@@ -27,7 +27,7 @@ D = 128          # channels per KV head (Qwen3-8B)
 LAYERS = 36
 KV_HEADS = 8
 
-ROLE_SPREAD, ROLE_KEYS, ROLE_QUERY, ROLE_VALUE = 0, 1, 2, 3
+ROLE_SPREAD, ROLE_KEYS, ROLE_QUERY, ROLE_VALUE, ROLE_QGAIN = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -98,6 +98,20 @@ def queries_np(seed: int, cfg_id: int, heads, G: int, d: int = D) -> np.ndarray:
     out = np.empty((len(heads), G, d), np.float32)
     for a, h in enumerate(heads):
         out[a] = _rng(seed, cfg_id, h, ROLE_QUERY).standard_normal((G, d), dtype=np.float32)
+    return out
+
+
+def queries_heavy_np(seed: int, cfg_id: int, heads, G: int, d: int = D,
+                     sigma: float = 1.5) -> np.ndarray:
+    """Queries whose channel magnitudes are heavy-tailed: N(0, 1) times a per-(KV head,
+    channel) gain exp(sigma N(0, 1)) shared by the head's G queries, so that a few
+    channels dominate each head's scores (the regime a per-query plan is for)."""
+    heads = list(heads)
+    out = np.empty((len(heads), G, d), np.float32)
+    for a, h in enumerate(heads):
+        gain = np.exp(sigma * _rng(seed, cfg_id, h, ROLE_QGAIN).standard_normal(d))
+        z = _rng(seed, cfg_id, h, ROLE_QUERY).standard_normal((G, d), dtype=np.float32)
+        out[a] = (z * gain[None, :]).astype(np.float32)
     return out
 
 
