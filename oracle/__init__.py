@@ -55,6 +55,11 @@ def _load():
         "oracle_quantize_batch": (None, [P, I, I, I, P, P, P]),
         "oracle_pack_planes_batch": (None, [P, I, I, I, I, P]),
         "oracle_pack_nibbles_batch": (None, [P, I, I, I, P]),
+        "oracle_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+        "oracle_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "oracle_quantize_grouped_batch": (None, [P, I, I, I, I, P, P, P]),
+        "oracle_var_grouped_batch": (None, [P, P, P, I, I, I, I, P]),
+        "oracle_scores_grouped_batch": (None, [P, P, P, P, P, I, I, I, I, I, P]),
         "oracle_var_batch": (None, [P, P, I, I, I, P]),
         "oracle_plan_batch": (I, [P, P, I, I, I, I, P]),
         "oracle_plan_fixed": (I, [P, I, I, P]),
@@ -143,6 +148,64 @@ def pack_nibbles(codes):
     nib = np.empty((H, n, d // 2), np.uint8)
     _load().oracle_pack_nibbles_batch(_p(cd), H, n, d, _p(nib))
     return nib[0] if squeeze else nib
+
+
+GROUP = 128  # tokens per scale/zero group of the grouped store
+
+
+def f32_to_f16_bits(x: float) -> int:
+    return int(_load().oracle_f32_to_f16(float(x)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(_load().oracle_f16_to_f32(int(h)))
+
+
+def quantize_grouped(keys, group: int = GROUP):
+    """keys fp32 [H][n][d] -> (s16, z16 fp16 bits u16 [H][d][ceil(n/group)], codes u8 [H][n][d])."""
+    x = _c(keys, np.float32)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[None]
+    H, n, d = x.shape
+    ng = (n + group - 1) // group
+    s16 = np.empty((H, d, ng), np.uint16)
+    z16 = np.empty((H, d, ng), np.uint16)
+    codes = np.empty((H, n, d), np.uint8)
+    _load().oracle_quantize_grouped_batch(_p(x), H, n, d, int(group), _p(s16), _p(z16),
+                                          _p(codes))
+    if squeeze:
+        return s16[0], z16[0], codes[0]
+    return s16, z16, codes
+
+
+def var_grouped(codes, s16, z16, group: int = GROUP):
+    """fp32 [H][d] variance of the group-dequantized channels."""
+    cd = _c(codes, np.uint8)
+    sh, zh = _c(s16, np.uint16), _c(z16, np.uint16)
+    squeeze = cd.ndim == 2
+    if squeeze:
+        cd, sh, zh = cd[None], sh[None], zh[None]
+    H, n, d = cd.shape
+    var = np.empty((H, d), np.float32)
+    _load().oracle_var_grouped_batch(_p(cd), _p(sh), _p(zh), H, n, d, int(group), _p(var))
+    return var[0] if squeeze else var
+
+
+def scores_grouped(codes, s16, z16, depth, q, group: int = GROUP):
+    """fp64 approximate scores [H][G][n] over a grouped store."""
+    cd = _c(codes, np.uint8)
+    sh, zh = _c(s16, np.uint16), _c(z16, np.uint16)
+    dp, qq = _c(depth, np.uint8), _c(q, np.float32)
+    squeeze = cd.ndim == 2
+    if squeeze:
+        cd, sh, zh, dp, qq = cd[None], sh[None], zh[None], dp[None], qq[None]
+    H, n, d = cd.shape
+    G = qq.shape[1]
+    out = np.empty((H, G, n), np.float64)
+    _load().oracle_scores_grouped_batch(_p(cd), _p(sh), _p(zh), _p(dp), _p(qq), H, n, d, G,
+                                        int(group), _p(out))
+    return out[0] if squeeze else out
 
 
 def plane_prefix(planes_head, c: int, t: int, i: int) -> int:

@@ -205,6 +205,130 @@ int oracle_plan_fixed(const float *var, int d, int n_channels, uint8_t *depth)
 }
 
 /* ------------------------------------------------------------------------------ */
+/* IEEE 754 binary16 (fp16), round to nearest, ties to even, from the format's       */
+/* definition: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; values below */
+/* 2^-14 are multiples of 2^-24; at or above 65520 the value rounds to infinity.     */
+/* ------------------------------------------------------------------------------ */
+uint16_t oracle_f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u) return sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u);
+    const double v = fabs((double)x);
+    if (v >= 65520.0) return sign | 0x7C00u;
+    if (v < 6.103515625e-05) {               /* below 2^-14: steps of 2^-24 */
+        const double r = nearbyint(v * 16777216.0);
+        return sign | (uint16_t)r;           /* r = 1024 is the smallest normal */
+    }
+    int e;
+    const double f = frexp(v, &e);           /* v = f 2^e, f in [0.5, 1) */
+    double r = nearbyint(ldexp(f, 11));      /* 11 significant bits */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    const int E = e - 1 + 15;
+    if (E >= 31) return sign | 0x7C00u;
+    return sign | (uint16_t)((E << 10) | ((uint32_t)r - 1024u));
+}
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    const int E = (h >> 10) & 31, F = h & 1023;
+    double v;
+    if (E == 31) v = F ? NAN : INFINITY;
+    else if (E == 0) v = ldexp((double)F, -24);
+    else v = ldexp((double)(1024 + F), E - 25);
+    return (float)((h & 0x8000u) ? -v : v);
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Grouped scale and zero.  A reading of the blog's "Where this does not work": the  */
+/* index costs 68 bytes per token per KV head, 4 more than 128 channels of 4-bit     */
+/* codes; one fp16 scale and one fp16 zero per channel per group of 128 tokens are   */
+/* exactly those 4 bytes.  Per channel, per group of `group` consecutive tokens (the */
+/* last may be shorter): s = (max - min)/15 and z = min in fp32 as in               */
+/* oracle_quantize, each rounded to fp16; the codes use the fp16 values:            */
+/*   code = clamp(floor((x - zf)/sf + 0.5), 0, 15), every step one fp32 operation,   */
+/* sf == 0 gives code 0.  s16, z16: fp16 bits [d][ceil(n/group)].                   */
+/* ------------------------------------------------------------------------------ */
+void oracle_quantize_grouped(const float *x, int n, int d, int group, uint16_t *s16,
+                             uint16_t *z16, uint8_t *codes)
+{
+    const int ng = (n + group - 1) / group;
+    for (int c = 0; c < d; ++c)
+        for (int gi = 0; gi < ng; ++gi) {
+            const int i0 = gi * group, i1 = i0 + group < n ? i0 + group : n;
+            float mn = x[(size_t)i0 * d + c], mx = mn;
+            for (int i = i0 + 1; i < i1; ++i) {
+                const float v = x[(size_t)i * d + c];
+                if (v < mn) mn = v;
+                if (v > mx) mx = v;
+            }
+            const float range = mx - mn;
+            const uint16_t sh = oracle_f32_to_f16(range / 15.0f);
+            const uint16_t zh = oracle_f32_to_f16(mn);
+            s16[(size_t)c * ng + gi] = sh;
+            z16[(size_t)c * ng + gi] = zh;
+            const float sf = oracle_f16_to_f32(sh), zf = oracle_f16_to_f32(zh);
+            for (int i = i0; i < i1; ++i) {
+                uint8_t code = 0;
+                if (sf != 0.0f) {
+                    float diff = x[(size_t)i * d + c] - zf;
+                    float u = diff / sf;
+                    float r = u + 0.5f;
+                    float f = floorf(r);
+                    if (f < 0.0f) f = 0.0f;
+                    if (f > 15.0f) f = 15.0f;
+                    code = (uint8_t)f;
+                }
+                codes[(size_t)i * d + c] = code;
+            }
+        }
+}
+
+/* Variance of the dequantized channel zf + sf*code over all n tokens (the importance  */
+/* of "How each query picks its own depth"), from per-group integer code sums S1, S2: */
+/*   S = sum_G (n_G zf + sf S1),  Q = sum_G (n_G zf^2 + 2 zf sf S1 + sf^2 S2),         */
+/* each product exact in fp64, each term added in that order, groups ascending; then  */
+/* var = (n Q - S^2) / n^2 in fp64, rounded once to fp32.                            */
+void oracle_var_grouped(const uint8_t *codes, const uint16_t *s16, const uint16_t *z16,
+                        int n, int d, int group, float *var)
+{
+    const int ng = (n + group - 1) / group;
+    for (int c = 0; c < d; ++c) {
+        double S = 0.0, Q = 0.0;
+        for (int gi = 0; gi < ng; ++gi) {
+            const int i0 = gi * group, i1 = i0 + group < n ? i0 + group : n;
+            int64_t s1 = 0, s2 = 0;
+            for (int i = i0; i < i1; ++i) {
+                const int64_t k = codes[(size_t)i * d + c];
+                s1 += k;
+                s2 += k * k;
+            }
+            const double zf = oracle_f16_to_f32(z16[(size_t)c * ng + gi]);
+            const double sf = oracle_f16_to_f32(s16[(size_t)c * ng + gi]);
+            const double nG = (double)(i1 - i0);
+            S = S + nG * zf;
+            S = S + sf * (double)s1;
+            Q = Q + nG * (zf * zf);
+            Q = Q + 2.0 * zf * sf * (double)s1;
+            Q = Q + (sf * sf) * (double)s2;
+        }
+        const double nn = (double)n;
+        var[c] = (float)((nn * Q - S * S) / (nn * nn));
+    }
+}
+
+/* Approximate scores over a grouped store: as oracle_scores, each token dequantized */
+/* with its group's fp16 scale and zero.  fp64.                                       */
+void oracle_scores_grouped(const uint8_t *codes, const uint16_t *s16, const uint16_t *z16,
+                           const uint8_t *depth, const float *q, int n, int d, int G,
+                           int group, double *scores);
+
+/* ------------------------------------------------------------------------------ */
 /* Reconstruction at the bin midpoint.  A t-plane prefix p pins the 4-bit code to   */
 /* the 2^(4-t) codes p*2^(4-t) .. p*2^(4-t) + 2^(4-t) - 1; the channel is            */
 /* reconstructed at the middle of that run: m = p*2^(4-t) + (2^(4-t) - 1)/2,         */
@@ -237,6 +361,25 @@ void oracle_scores(const uint8_t *codes, const float *scale, const float *zero,
                 double m = oracle_midpoint_level(codes[(size_t)i * d + c], depth[c]);
                 double khat = (double)zero[c] + (double)scale[c] * m;
                 acc += (double)q[(size_t)g * d + c] * khat;
+            }
+            scores[(size_t)g * n + i] = acc;
+        }
+}
+
+void oracle_scores_grouped(const uint8_t *codes, const uint16_t *s16, const uint16_t *z16,
+                           const uint8_t *depth, const float *q, int n, int d, int G,
+                           int group, double *scores)
+{
+    const int ng = (n + group - 1) / group;
+    for (int g = 0; g < G; ++g)
+        for (int i = 0; i < n; ++i) {
+            const int gi = i / group;
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) {
+                const double m = oracle_midpoint_level(codes[(size_t)i * d + c], depth[c]);
+                const double zf = oracle_f16_to_f32(z16[(size_t)c * ng + gi]);
+                const double sf = oracle_f16_to_f32(s16[(size_t)c * ng + gi]);
+                acc += (double)q[(size_t)g * d + c] * (zf + sf * m);
             }
             scores[(size_t)g * n + i] = acc;
         }
@@ -385,6 +528,39 @@ void oracle_pack_nibbles_batch(const uint8_t *codes, int H, int n, int d, uint8_
 #pragma omp parallel for schedule(dynamic, 1)
     for (int h = 0; h < H; ++h)
         oracle_pack_nibbles(codes + (size_t)h * n * d, n, d, nib + (size_t)h * n * (d / 2));
+}
+
+void oracle_quantize_grouped_batch(const float *x, int H, int n, int d, int group,
+                                   uint16_t *s16, uint16_t *z16, uint8_t *codes)
+{
+    const int ng = (n + group - 1) / group;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h)
+        oracle_quantize_grouped(x + (size_t)h * n * d, n, d, group, s16 + (size_t)h * d * ng,
+                                z16 + (size_t)h * d * ng, codes + (size_t)h * n * d);
+}
+
+void oracle_var_grouped_batch(const uint8_t *codes, const uint16_t *s16, const uint16_t *z16,
+                              int H, int n, int d, int group, float *var)
+{
+    const int ng = (n + group - 1) / group;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h)
+        oracle_var_grouped(codes + (size_t)h * n * d, s16 + (size_t)h * d * ng,
+                           z16 + (size_t)h * d * ng, n, d, group, var + (size_t)h * d);
+}
+
+void oracle_scores_grouped_batch(const uint8_t *codes, const uint16_t *s16,
+                                 const uint16_t *z16, const uint8_t *depth, const float *q,
+                                 int H, int n, int d, int G, int group, double *scores)
+{
+    const int ng = (n + group - 1) / group;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h)
+        oracle_scores_grouped(codes + (size_t)h * n * d, s16 + (size_t)h * d * ng,
+                              z16 + (size_t)h * d * ng, depth + (size_t)h * d,
+                              q + (size_t)h * G * d, n, d, G, group,
+                              scores + (size_t)h * G * n);
 }
 
 void oracle_var_batch(const uint8_t *codes, const float *scale, int H, int n, int d,
