@@ -199,9 +199,9 @@ def main():
 
     host = None
     acc = None
-    if not args.no_host or not args.no_accuracy:
-        del K, V, st, ws, scores
-        torch.cuda.empty_cache()
+    del K, V, st, ws, scores
+    torch.cuda.empty_cache()
+    grouped = grouped_lines(args, kern)
     if not args.no_accuracy:
         acc = accuracy_sweep(args)
     if not args.no_host:
@@ -228,6 +228,7 @@ def main():
         "parity_before_timing": parity,
         "host_resident": host,
         "accuracy_per_byte": acc,
+        "grouped_store": grouped,
     }
     print(json.dumps(result), flush=True)
 
@@ -401,6 +402,60 @@ def link_rate(dev, stream, nbytes=1 << 30):
     del h, d
     return {"dma_h2d_GBps": round(dma, 2), "zero_copy_read_GBps": round(zc, 2),
             "L_GBps": round(max(dma, zc), 2)}
+
+
+def grouped_lines(args, kern):
+    """The grouped store (fp16 scale and zero per 128-token group: 68 B per token per KV
+    head, the index size of the blog's "Where this does not work") on the bench workload:
+    its build, a decode-time append of one token to every head (the last group
+    re-quantized and every variance recomputed), and its scan at the bench budget, with
+    one sampled head checked against the oracle."""
+    import torch
+    import oracle
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS[args.config]
+    H, G, n, B = cfg.H, cfg.G, cfg.n, args.budget
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    keys = synth.keys_torch(args.seed, cfg.cfg_id, range(H), n, dev)
+    q = torch.from_numpy(synth.queries_np(args.seed, cfg.cfg_id, range(H), G)).to(dev)
+    ng = (n + 127) // 128
+    gs = F.GStore.empty(H, n + 128, dev, n=n - 1)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    build_ms = timed_ms(lambda: F.fathom_quantize_groups(keys[:, :n - 1], gs, 0, ng),
+                        stream, 3, flush, sink)
+    gs.n_tokens = n   # append token n-1: its group is re-quantized
+    g = (n - 1) // 128
+    append_ms = timed_ms(lambda: F.fathom_quantize_groups(keys[:, 128 * g:n], gs, g, g + 1),
+                         stream, 10, flush, sink)
+    depth = F.fathom_plan_grouped(gs, q, B)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    scan_ms = timed_ms(lambda: F.fathom_scan_grouped(gs, q, depth, scores=scores), stream, 10,
+                       flush, sink)
+    torch.cuda.synchronize()
+    h = H // 2
+    kh = keys[h:h + 1].cpu().numpy()
+    s16, z16, codes = oracle.quantize_grouped(kh)
+    ref_depth = oracle.plan(q[h:h + 1].cpu().numpy(), oracle.var_grouped(codes, s16, z16), B)
+    ref = oracle.scores_grouped(codes, s16, z16, ref_depth, q[h:h + 1].cpu().numpy())
+    got = scores[h:h + 1].cpu().numpy()
+    rel = float((np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+    ok = bool(np.array_equal(gs.scale16[h:h + 1, :, :ng].cpu().numpy().view(np.uint16), s16)
+              and np.array_equal(depth[h:h + 1].cpu().numpy(), ref_depth) and rel <= 1e-5)
+    res = {"bytes_per_token_per_kv_head": 64 + 4, "group_tokens": 128,
+           "build_ms": round(build_ms, 3), "append_one_token_ms": round(append_ms, 4),
+           "scan_ms": round(scan_ms, 4),
+           "scan_ms_per_channel_store_matrix_cores": round(kern["scan_ms"], 4),
+           "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
+           "oracle_check_head": h, "score_rel_err": rel, "ok": ok}
+    log(f"[bench] grouped store: build {build_ms:.2f} ms, append {append_ms * 1e3:.1f} us, "
+        f"scan {scan_ms * 1e3:.1f} us (per-channel matrix-core scan "
+        f"{kern['scan_ms'] * 1e3:.1f} us), check {ok}")
+    del keys, gs, scores, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 ACC_BUDGETS = (16, 24, 32, 40, 48, 56, 64, 72, 80, 92, 104, 120, 136, 168, 200, 256, 512)

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "fathom")
 LIB = os.path.join(PKG, "libfathom.so")
 
-SOURCES = ["api.cpp", "store.hip", "plan.hip", "scan.hip", "scan_extract.hip", "nibble.hip", "topk.hip",
+SOURCES = ["api.cpp", "store.hip", "plan.hip", "scan.hip", "scan_extract.hip", "nibble.hip", "grouped.hip", "topk.hip",
            "attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

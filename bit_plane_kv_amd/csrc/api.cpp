@@ -214,6 +214,64 @@ int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uin
     return hip_status(launch_scan_extract(*st, q, G, depth, scores, as_stream(stream)));
 }
 
+static int check_gstore(const fathom_gstore *gs) {
+    if (!gs || gs->n_heads < 1 || gs->n_tokens < 1 || !gs->planes || !gs->scale16 ||
+        !gs->zero16 || !gs->sums || !gs->var || !gs->prefix || !gs->prefix_groups ||
+        gs->pad != 0)
+        return FATHOM_ERR_INVALID_ARG;
+    if (gs->d != FATHOM_D) return FATHOM_ERR_UNSUPPORTED;
+    const int ng = (gs->n_tokens + FATHOM_GROUP - 1) / FATHOM_GROUP;
+    if (gs->word_stride < 4 * ng || (gs->word_stride & 3) || gs->group_stride < ng)
+        return FATHOM_ERR_INVALID_ARG;
+    if (!aligned(gs->planes, 16) || !aligned(gs->scale16, 2) || !aligned(gs->zero16, 2) ||
+        !aligned(gs->sums, 8) || !aligned(gs->var, 4) || !aligned(gs->prefix, 16) ||
+        !aligned(gs->prefix_groups, 4))
+        return FATHOM_ERR_INVALID_ARG;
+    return check_all({gs->planes, gs->scale16, gs->zero16, gs->sums, gs->var, gs->prefix,
+                      gs->prefix_groups});
+}
+
+int fathom_quantize_groups(const float *keys, int64_t keys_head_stride, const fathom_gstore *gs,
+                           int g0, int g1, void *stream) {
+    FATHOM_TRY(check_gstore(gs));
+    const int n = gs->n_tokens, ng = (n + FATHOM_GROUP - 1) / FATHOM_GROUP;
+    if (!keys || !aligned(keys, 16) || g0 < 0 || g1 <= g0 || g1 > ng)
+        return FATHOM_ERR_INVALID_ARG;
+    const int64_t m = (int64_t)std::min(n, FATHOM_GROUP * g1) - (int64_t)FATHOM_GROUP * g0;
+    if (keys_head_stride % 4 != 0 || (gs->n_heads > 1 && keys_head_stride < m * FATHOM_D))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({keys}));
+    return hip_status(launch_quantize_groups(keys, keys_head_stride, *gs, g0, g1,
+                                             as_stream(stream)));
+}
+
+int fathom_plan_grouped(const fathom_gstore *gs, const float *q, int G, int B, uint8_t *depth,
+                        void *stream) {
+    FATHOM_TRY(check_gstore(gs));
+    FATHOM_TRY(check_g(G));
+    if (!q || !depth || !aligned(q, 4)) return FATHOM_ERR_INVALID_ARG;
+    if (B < 0 || B > FATHOM_D * FATHOM_PLANES) return FATHOM_ERR_BUDGET;
+    FATHOM_TRY(check_all({q, depth}));
+    fathom_store view{};
+    view.n_heads = gs->n_heads;
+    view.n_tokens = gs->n_tokens;
+    view.d = gs->d;
+    view.word_stride = gs->word_stride;
+    view.planes = gs->planes;
+    view.var = gs->var;
+    return hip_status(launch_plan(view, q, G, B, depth, as_stream(stream)));
+}
+
+int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const uint8_t *depth,
+                        float *scores, void *stream) {
+    FATHOM_TRY(check_gstore(gs));
+    FATHOM_TRY(check_g(G));
+    if (!q || !depth || !scores || !aligned(q, 4) || !aligned(scores, 4))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_all({q, depth, scores}));
+    return hip_status(launch_scan_grouped(*gs, q, depth, G, scores, as_stream(stream)));
+}
+
 int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream) {
     FATHOM_TRY(check_store(st));
     if (!nib || !aligned(nib, 16)) return FATHOM_ERR_INVALID_ARG;

@@ -39,6 +39,16 @@ class fathom_store(ctypes.Structure):
                 ("zero", ctypes.c_void_p), ("var", ctypes.c_void_p)]
 
 
+class fathom_gstore(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("word_stride", ctypes.c_int32),
+                ("group_stride", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("planes", ctypes.c_void_p), ("scale16", ctypes.c_void_p),
+                ("zero16", ctypes.c_void_p), ("sums", ctypes.c_void_p),
+                ("var", ctypes.c_void_p), ("prefix", ctypes.c_void_p),
+                ("prefix_groups", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -61,6 +71,10 @@ _SIGS = {
                          _P, _P, _P, _P, _P, _SZ, _P]),
     "fathom_scan_extract": (_I, [_P, _P, _I, _P, _P, _P]),
     "fathom_pack_nibbles": (_I, [ctypes.POINTER(fathom_store), _P, _P]),
+    "fathom_quantize_groups": (_I, [_P, ctypes.c_int64, ctypes.POINTER(fathom_gstore), _I, _I,
+                                    _P]),
+    "fathom_plan_grouped": (_I, [ctypes.POINTER(fathom_gstore), _P, _I, _I, _P, _P]),
+    "fathom_scan_grouped": (_I, [ctypes.POINTER(fathom_gstore), _P, _I, _P, _P, _P]),
     "fathom_scan_nibble": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P]),
     "fathom_stream_read": (_I, [_P, _SZ, _P, _P]),
     "fathom_stream_read_runs": (_I, [_P, _SZ, _SZ, _SZ, _P, _P]),
@@ -165,6 +179,75 @@ class Store:
     def view_heads(self, h0: int, h1: int) -> "Store":
         return Store(self.planes[h0:h1], self.scale[h0:h1], self.zero[h0:h1],
                      self.var[h0:h1], self.n_tokens)
+
+
+GROUP = 128  # tokens per scale/zero group of the grouped store
+
+
+@dataclass
+class GStore:
+    """Grouped store: planes as in Store, fp16 scale/zero and int32 code sums per
+    (channel, 128-token group), fp32 var.  Capacity: n_max tokens."""
+    planes: object        # int32 [H][d][4][word_stride]
+    scale16: object       # int16 (fp16 bits) [H][d][group_stride]
+    zero16: object
+    sums: object          # int32 [H][d][group_stride][2]
+    var: object           # fp32 [H][d]
+    prefix: object        # fp64 [H][d][2], zeroed
+    prefix_groups: object  # int32 [H][d], zeroed
+    n_tokens: int
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.planes.shape[0])
+
+    def descriptor(self) -> fathom_gstore:
+        return fathom_gstore(self.n_heads, self.n_tokens, D, int(self.planes.shape[-1]),
+                             int(self.scale16.shape[-1]), 0, _ptr(self.planes),
+                             _ptr(self.scale16), _ptr(self.zero16), _ptr(self.sums),
+                             _ptr(self.var), _ptr(self.prefix), _ptr(self.prefix_groups))
+
+    @staticmethod
+    def empty(H: int, n_max: int, device, n: int = 0) -> "GStore":
+        import torch
+        ng = (n_max + GROUP - 1) // GROUP
+        i32 = dict(dtype=torch.int32, device=device)
+        return GStore(torch.zeros((H, D, PLANES, 4 * ng), **i32),
+                      torch.zeros((H, D, ng), dtype=torch.int16, device=device),
+                      torch.zeros((H, D, ng), dtype=torch.int16, device=device),
+                      torch.zeros((H, D, ng, 2), **i32),
+                      torch.zeros((H, D), dtype=torch.float32, device=device),
+                      torch.zeros((H, D, 2), dtype=torch.float64, device=device),
+                      torch.zeros((H, D), **i32), n)
+
+
+def fathom_quantize_groups(keys, gstore: GStore, g0: int, g1: int, stream=None):
+    """keys fp32 [H][m][d] (m = min(n, 128 g1) - 128 g0; any head stride) -> groups g0..g1-1."""
+    gs = gstore.descriptor()
+    _check(lib().fathom_quantize_groups(_ptr(keys), int(keys.stride(0)), ctypes.byref(gs),
+                                        int(g0), int(g1), _stream(stream)),
+           "fathom_quantize_groups")
+
+
+def fathom_plan_grouped(gstore: GStore, q, B: int, depth=None, stream=None):
+    import torch
+    if depth is None:
+        depth = torch.empty((gstore.n_heads, D), dtype=torch.uint8, device=q.device)
+    gs = gstore.descriptor()
+    _check(lib().fathom_plan_grouped(ctypes.byref(gs), _ptr(q), q.shape[1], int(B),
+                                     _ptr(depth), _stream(stream)), "fathom_plan_grouped")
+    return depth
+
+
+def fathom_scan_grouped(gstore: GStore, q, depth, scores=None, stream=None):
+    import torch
+    H, G, _ = q.shape
+    if scores is None:
+        scores = torch.empty((H, G, gstore.n_tokens), dtype=torch.float32, device=q.device)
+    gs = gstore.descriptor()
+    _check(lib().fathom_scan_grouped(ctypes.byref(gs), _ptr(q), G, _ptr(depth), _ptr(scores),
+                                     _stream(stream)), "fathom_scan_grouped")
+    return scores
 
 
 # ---------------------------------------------------------------------------------

@@ -82,6 +82,38 @@ typedef struct fathom_store {
     float *var;
 } fathom_store;
 
+#define FATHOM_GROUP 128      /* tokens per scale/zero group of the grouped store */
+
+/*
+ * The grouped store (a reading of the blog's "Where this does not work": the index is
+ * 68 bytes per token per KV head, i.e. 4-bit codes plus 4 bytes, which one fp16 scale
+ * and one fp16 zero per channel per 128-token group give).  Caller-owned buffers:
+ *   planes [H][d][4][word_stride] uint32, as in fathom_store; word_stride >=
+ *          4*ceil(n/128) and a multiple of 4 (whole groups of 4 words).
+ *   scale16, zero16 [H][d][group_stride] fp16 bits: group G of channel c of head h.
+ *   sums [H][d][group_stride][2] int32: the group's sum of codes and of squared codes.
+ *   var [H][d] fp32: variance of the group-dequantized channel over all n tokens.
+ *   prefix [H][d][2] fp64 and prefix_groups [H][d] int32: the variance's running sums
+ *          (S, Q below) over the first prefix_groups groups, kept so that an append
+ *          adds only the groups it changed.  Zero them before the first call.
+ * group_stride >= ceil(n/128).  All device memory except planes (HBM or pinned host).
+ */
+typedef struct fathom_gstore {
+    int32_t n_heads;      /* H */
+    int32_t n_tokens;     /* n, >= 1 */
+    int32_t d;            /* must be FATHOM_D */
+    int32_t word_stride;  /* see above */
+    int32_t group_stride; /* see above */
+    int32_t pad;          /* 0 */
+    uint32_t *planes;
+    uint16_t *scale16;
+    uint16_t *zero16;
+    int32_t *sums;
+    float *var;
+    double *prefix;
+    int32_t *prefix_groups;
+} fathom_gstore;
+
 /* Operations for fathom_workspace_size. */
 enum fathom_op {
     FATHOM_OP_QUANTIZE = 0, /* fathom_quantize_store: uses H, n */
@@ -173,6 +205,45 @@ int fathom_scan_prepared(const fathom_store *st, int G, float *scores, void *ws,
  * fathom_scan, no workspace.  Slower than fathom_scan by design.
  */
 int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uint8_t *depth,
+                        float *scores, void *stream);
+
+/*
+ * Build and decode-time append of the grouped store (SURVEY's reading of the pages'
+ * 68-byte index; blog, "Bit planes" for the layout): (re)quantize groups g0 .. g1-1 of
+ * every head from keys, then recompute var from all groups' sums.
+ *   keys: fp32, head h's tokens 128*g0 .. min(n, 128*g1) - 1 at keys + h*keys_head_stride,
+ *         d floats per token (keys 16-byte aligned; keys_head_stride in floats, a
+ *         multiple of 4, >= (min(n,128*g1) - 128*g0)*d).
+ * Per group and channel: s = (max - min)/15 and z = min in fp32, each rounded to fp16
+ * (nearest, ties to even); code = clamp(floor((x - zf)/sf + 0.5), 0, 15) with zf, sf the
+ * fp16 values as fp32, every step one fp32 operation (sf = 0: code 0).  A group's 4 words
+ * per plane are rewritten whole (bits of tokens >= n zero).  var is recomputed as
+ * (n Q - S^2)/n^2 in fp64 from S = sum_G (n_G zf + sf S1_G) and Q = sum_G (n_G zf^2 +
+ * 2 zf sf S1_G + sf^2 S2_G), term by term, groups ascending, rounded once; the running
+ * sums over the groups before g0 are reused from prefix when it covers no group >= g0,
+ * which gives the same fp64 values as summing from group 0.
+ * Build: g0 = 0, g1 = ceil(n/128).  Append one token: set n to the new count, g0 = g1 - 1
+ * = (n-1)/128, keys = that group's tokens.  0 <= g0 < g1 <= ceil(n/128).
+ */
+int fathom_quantize_groups(const float *keys, int64_t keys_head_stride,
+                           const fathom_gstore *gs, int g0, int g1, void *stream);
+
+/*
+ * Plan for the grouped store: fathom_plan with gs->var (same rule and arithmetic).
+ */
+int fathom_plan_grouped(const fathom_gstore *gs, const float *q, int G, int B,
+                        uint8_t *depth, void *stream);
+
+/*
+ * Scan of the grouped store (blog, "Bit planes"; "How each query picks its own depth"):
+ * each channel read to its depth, reconstructed at the bin midpoint with its token's
+ * group scale and zero:  score_g(i) = C_gG + sum_c fl32(q_gc sf_cG) * P_c(i), P the
+ * t-plane prefix times 2^(4-t), C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64 rounded
+ * once, the channel sum in fp32 ascending.  Bits are extracted on the vector units (the
+ * matrix-core scan needs weights shared by 16 consecutive token columns, which straddle
+ * groups).  q [H][G][d] fp32, depth [H][d], scores [H][G][n] fp32 out.
+ */
+int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const uint8_t *depth,
                         float *scores, void *stream);
 
 /*
