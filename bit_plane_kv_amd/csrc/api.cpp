@@ -394,9 +394,9 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const
     uint32_t *redo = reinterpret_cast<uint32_t *>(w);
 
     const hipStream_t s = as_stream(stream);
-    // every score is asked for, or the sample could not give a threshold (k too close
-    // to n): scan all, then select
-    if (scores_out || sample_rank(n, k) == 0) {
+    // every score is asked for, or no threshold can help (k too close to n for the
+    // sample, or B = 0: every score of a row is the same): scan all, then select
+    if (scores_out || sample_rank(n, k) == 0 || B == 0) {
         FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, 0, depth, scan_ws, s)));
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
         FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));

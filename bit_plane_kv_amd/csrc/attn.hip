@@ -54,31 +54,51 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     const int32_t *ix = idx + (size_t)hg * k;
     const uint16_t *Kh = K + (size_t)h * n * kD + sub * 16;
     const uint16_t *Vh = V + (size_t)h * n * kD + sub * 16;
-    for (int r = slot; r < k; r += kSlots) {
-        const int row = ix[r];
-        if ((unsigned)row >= (unsigned)n) continue;  // out-of-range index: skipped
-        const uint4 *kp = reinterpret_cast<const uint4 *>(Kh + (size_t)row * kD);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(Vh + (size_t)row * kD);
-        const uint4 ka = kp[0], kb = kp[1], va = vp[0], vb = vp[1];
-        float kf[16], vf[16];
-        unpack8(ka, kf);
-        unpack8(kb, kf + 8);
-        unpack8(va, vf);
-        unpack8(vb, vf + 8);
-        float dot = 0.0f;
+    // four rows a slot at a time: their indices, then their K and V pieces, are loaded
+    // together, so that each batch waits for two memory latencies instead of each row
+    for (int r0 = slot; r0 < k; r0 += 4 * kSlots) {
+        int row[4];
+        bool ok[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], kf[i], dot);
-        dot += __shfl_xor(dot, 1, 64);
-        dot += __shfl_xor(dot, 2, 64);
-        dot += __shfl_xor(dot, 4, 64);
-        const float s = dot * sm_scale;
-        const float mn = fmaxf(m, s);
-        const float a = expf(m - mn);  // 0 while m is still -inf
-        const float b = expf(s - mn);
-        l = l * a + b;
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + u * kSlots;
+            row[u] = r < k ? ix[r] : -1;
+            ok[u] = (unsigned)row[u] < (unsigned)n;  // out-of-range index: skipped
+        }
+        uint4 kk[4][2], vv[4][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] = o[i] * a + b * vf[i];
-        m = mn;
+        for (int u = 0; u < 4; ++u) {
+            if (!ok[u]) continue;
+            const uint4 *kp = reinterpret_cast<const uint4 *>(Kh + (size_t)row[u] * kD);
+            const uint4 *vp = reinterpret_cast<const uint4 *>(Vh + (size_t)row[u] * kD);
+            kk[u][0] = kp[0];
+            kk[u][1] = kp[1];
+            vv[u][0] = vp[0];
+            vv[u][1] = vp[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (!ok[u]) continue;
+            float kf[16], vf[16];
+            unpack8(kk[u][0], kf);
+            unpack8(kk[u][1], kf + 8);
+            unpack8(vv[u][0], vf);
+            unpack8(vv[u][1], vf + 8);
+            float dot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], kf[i], dot);
+            dot += __shfl_xor(dot, 1, 64);
+            dot += __shfl_xor(dot, 2, 64);
+            dot += __shfl_xor(dot, 4, 64);
+            const float s = dot * sm_scale;
+            const float mn = fmaxf(m, s);
+            const float a = expf(m - mn);  // 0 while m is still -inf
+            const float b = expf(s - mn);
+            l = l * a + b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] = o[i] * a + b * vf[i];
+            m = mn;
+        }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) so[slot][sub * 16 + i] = o[i];

@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
 // The row chunks the filtered select handed over (listed as row * nch + chunk; their
 // count is the head-0 meta block's redo field), a grid-stride loop over the list: a
 // small grid, as the list is usually empty.
-constexpr int kRedoGrid = 64;
+constexpr int kRedoGrid = 16;
 template <bool kCandOut>
 __global__ __launch_bounds__(kThreads, 8) void k_topk_redo(
     const float *__restrict__ vals, int64_t row_len, int k, float *__restrict__ out_val,
