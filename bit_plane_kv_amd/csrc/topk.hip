@@ -463,6 +463,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     __shared__ uint32_t hist[kSelBins];
     __shared__ uint32_t sh[2][4];
     __shared__ uint32_t pick[2][3];
+    __shared__ uint32_t smm[2][4];  // per-wave min and max key
     const int tid = threadIdx.x, chunk = blockIdx.x, nch = gridDim.x;
     const int64_t row = (int64_t)row0 + blockIdx.y;
     const int64_t start = (int64_t)chunk * kTopkChunk;
@@ -536,11 +537,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = tid + kSelThreads * u;
-            if (e < (int)C) {
-                const uint32_t key = order_key(v[u]);
-                skey[e] = key;
-                atomicAdd(&hist[key >> 21], 1u);
-            }
+            if (e < (int)C) skey[e] = order_key(v[u]);
         }
     }
     __syncthreads();
@@ -551,19 +548,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         fill_slots(out_val, out_idx, obase, 0, min(k, len));
         return;
     }
-    // radix select of the kr-th largest key: 11, 11 and 10 bit digits
-    uint32_t prefix = 0u, need = (uint32_t)kr;
-    int shift = 32;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int sd = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nb = pass == 2 ? 1024 : 2048;
-        if (pass > 0) {  // histogram of the keys under the prefix (pass 0's is built)
-            for (int i = tid; i < (int)C; i += kSelThreads) {
-                const uint32_t key = skey[i];
-                if ((key >> shift) == prefix) atomicAdd(&hist[(key >> sd) & (nb - 1)], 1u);
-            }
-            __syncthreads();
+    // The kept keys are the top few percent of the row and share their top bits; the
+    // radix select starts below the bits all of them share (from their min and max), so
+    // that its first histogram spreads them over many bins instead of a few contended
+    // ones.  Digits of up to 11 bits.
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int i = tid; i < (int)C; i += kSelThreads) {
+        const uint32_t key = skey[i];
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    if ((tid & 63) == 0) {
+        smm[0][tid >> 6] = kmin;
+        smm[1][tid >> 6] = kmax;
+    }
+    __syncthreads();
+    kmin = min(min(smm[0][0], smm[0][1]), min(smm[0][2], smm[0][3]));
+    kmax = max(max(smm[1][0], smm[1][1]), max(smm[1][2], smm[1][3]));
+    const uint32_t diff = kmin ^ kmax;
+    int shift = diff == 0u ? 0 : 32 - __clz(diff);  // bits >= shift: the same in every key
+    uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift), need = (uint32_t)kr;
+    for (int pass = 0; shift > 0; ++pass) {
+        const int sd = max(0, shift - 11), width = shift - sd, nb = 1 << width;
+        for (int i = tid; i < (int)C; i += kSelThreads) {
+            const uint32_t key = skey[i];
+            if (((uint64_t)key >> shift) == prefix) atomicAdd(&hist[(key >> sd) & (nb - 1)], 1u);
         }
+        __syncthreads();
         // thread t owns bins nb-1-8t .. nb-8-8t (largest first)
         uint32_t c8[8], local = 0u;
 #pragma unroll
@@ -593,7 +609,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
             if (bin >= 0) hist[bin] = 0u;
         }
         __syncthreads();
-        prefix = pass == 0 ? pick[0][0] : ((prefix << (pass == 1 ? 11 : 10)) | pick[pass & 1][0]);
+        prefix = (prefix << width) | pick[pass & 1][0];
         need -= pick[pass & 1][1];
         const uint32_t in_bin = pick[pass & 1][2];
         shift = sd;
@@ -605,7 +621,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     const int b0 = min((int)C, tid * seg), b1 = min((int)C, b0 + seg);
     uint32_t gt = 0u, eq = 0u;
     for (int i = b0; i < b1; ++i) {
-        const uint32_t kv = skey[i] >> shift;
+        const uint32_t kv = (uint32_t)((uint64_t)skey[i] >> shift);
         gt += kv > prefix;
         eq += kv == prefix;
     }
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     uint32_t take = min(need - eq_won_before, eq);
     int slot = (int)(gtb + eq_won_before);
     for (int i = b0; i < b1; ++i) {
-        const uint32_t kv = skey[i] >> shift;
+        const uint32_t kv = (uint32_t)((uint64_t)skey[i] >> shift);
         bool win = kv > prefix;
         if (kv == prefix && take > 0u) {
             win = true;
