@@ -59,6 +59,8 @@ def parse():
                     help="skip the full-model host-resident scans (n = 256k and 1M)")
     ap.add_argument("--no-accuracy", action="store_true",
                     help="skip the synthetic accuracy-per-byte sweep")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="skip the grouped-store lines (build, append, scan)")
     ap.add_argument("--accuracy-only", action="store_true",
                     help="run only the synthetic accuracy-per-byte sweep")
     ap.add_argument("--calibrate", action="store_true",
@@ -201,7 +203,7 @@ def main():
     acc = None
     del K, V, st, ws, scores
     torch.cuda.empty_cache()
-    grouped = grouped_lines(args, kern)
+    grouped = None if args.no_grouped else grouped_lines(args, kern)
     if not args.no_accuracy:
         acc = accuracy_sweep(args)
     if not args.no_host:
