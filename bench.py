@@ -177,6 +177,18 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = H * n / (ms_per_step * 1e-3) / 1e9
+    # per-step GPU times of 30 more steps, each bracketed by its own events
+    per_step = []
+    for _ in range(30):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, ws=ws)
+        b.record(stream)
+        b.synchronize()
+        per_step.append(a.elapsed_time(b))
+    pct = {"median": round(float(np.median(per_step)), 4),
+           "p10": round(float(np.percentile(per_step, 10)), 4),
+           "p90": round(float(np.percentile(per_step, 90)), 4), "n": len(per_step)}
     log(f"[bench] step {ms_per_step:.3f} ms (GPU time), wall {wall / args.steps * 1e3:.3f} ms"
         f" -> {value:.1f} Gkeys/s")
 
@@ -227,6 +239,7 @@ def main():
                            "scores_written_by_full_scan": int(score_bytes),
                            "winner_rows": int(H * G * k * 512)},
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "step_ms_single_launch": pct,
         "parity_before_timing": parity,
         "host_resident": host,
         "accuracy_per_byte": acc,
