@@ -145,6 +145,32 @@ def test_step_filtered_equals_step_full():
     assert np.abs(bf16_to_f32(o2) - ref_out).max() <= 2e-2
 
 
+@pytest.mark.parametrize("B,n,k", [(0, 9000, 100), (92, 3000, 2900), (92, 40000, 16384),
+                                   (512, 33000, 512)])
+def test_step_without_scores_out_equals_step_with(B, n, k):
+    """The step's own choice of path (filter, or the full scan at B = 0 and when k is
+    too close to n for a threshold) gives the winners and outputs of the full path."""
+    torch = torch_cuda()
+    H, G = 2, 4
+    print(f"[step paths] B={B} n={n} k={k}", flush=True)
+    keys, q, K, V = inputs(104, H, G, n)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    scores = torch.empty((H, G, n), dtype=torch.float32, device="cuda")
+    i1 = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    o1 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, scores_out=scores, idx_out=i1)
+    o2 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
+    assert np.array_equal(i1.cpu().numpy().reshape(H * G, k),
+                          oracle.topk(scores.cpu().numpy().reshape(H * G, n), k))
+
+
 def test_scan_topk_host_resident_store():
     torch = torch_cuda()
     H, G, n, k = 2, 4, 20000, 128
