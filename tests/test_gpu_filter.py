@@ -186,3 +186,42 @@ def test_scan_topk_host_resident_store():
     b = F.fathom_scan_topk(st_h, q_t, depth, k)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def _random_cases(count, seed=7):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        H = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 9))
+        n = int(rng.choice([rng.integers(1, 300), rng.integers(300, 40000),
+                            rng.integers(40000, 90000)]))
+        B = int(rng.choice([0, 4, 37, 92, 136, 300, 512]))
+        kmax = n if n <= 32768 else 16384
+        k = int(min(kmax, rng.choice([1, 7, 64, 512, 2000, n])))
+        cases.append((H, G, n, B, k, int(rng.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("H,G,n,B,k,seed", _random_cases(20))
+def test_step_paths_agree_on_random_shapes(H, G, n, B, k, seed):
+    """Seeded random shapes, budgets and k: the step's fused path (or its fallback) gives
+    exactly the winners and outputs of the full path."""
+    torch = torch_cuda()
+    print(f"[step random] H={H} G={G} n={n} B={B} k={k} seed={seed}", flush=True)
+    keys, q, K, V = inputs(105, H, G, n, seed=seed % 1000)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    scores = torch.empty((H, G, n), dtype=torch.float32, device="cuda")
+    i1 = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    o1 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, scores_out=scores, idx_out=i1)
+    o2 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
+    assert np.array_equal(i1.cpu().numpy().reshape(H * G, k),
+                          oracle.topk(scores.cpu().numpy().reshape(H * G, n), k))
