@@ -11,11 +11,12 @@ log-uniform s_c in [0.1, 10], queries N(0,1), V N(0,1) in bf16), resident in HBM
 timing starts.  Before timing, sampled heads are checked against the CPU oracle.
 
 Prints ONE JSON line: value = keys ranked per second over the whole step (Gkeys/s);
-roofline = the scan kernel's algorithmic bytes (planes read + fp32 scores written) per
-launch / its mean launch time, against 8 TB/s (the scan in its full-score form,
-fathom_scan; the step itself runs the fused form, which writes only the candidate scores
-that clear a sampled threshold, and is checked to give the same winners); cpu_baseline =
-the oracle on the host cores over a bounded sample of heads.
+roofline = the step's longest kernel (the filtering scan or the attention), its
+algorithmic bytes per launch / its mean launch time over a pass of K more steps timed
+phase by phase (fathom_step_timed: events on the launch stream between the kernels),
+against 8 TB/s; roofline_full_scan = the same for the scan in its full-score form
+(fathom_scan, planes read + every fp32 score written), timed alone with cold caches;
+cpu_baseline = the oracle on the host cores over a bounded sample of heads.
 """
 from __future__ import annotations
 
@@ -191,6 +192,11 @@ def main():
            "p90": round(float(np.percentile(per_step, 90)), 4), "n": len(per_step)}
     log(f"[bench] step {ms_per_step:.3f} ms (GPU time), wall {wall / args.steps * 1e3:.3f} ms"
         f" -> {value:.1f} Gkeys/s")
+    # each kernel of the step, live: K more steps through fathom_step_timed, whose events
+    # on the launch stream bracket the step's phases
+    phases = step_phases(F, st, q, K, V, B, k, sm_scale, out, ws, stream, args.steps)
+    kept_total = float(ws[:H * 4096].view(torch.int32).view(H, 1024)[:, 28:28 + G].sum())
+    log(f"[bench] phases over {args.steps} steps (ms): {phases}")
 
     # ---------------- per-kernel times (cold caches between launches) ----------------
     kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
@@ -200,11 +206,31 @@ def main():
     scan_bytes = plane_bytes + score_bytes
     scan_ms = kern["scan_ms"]
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = load_traffic(scan_bytes)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "k_scan_main<1,false,false>",
-                "algorithmic_bytes_per_launch": int(scan_bytes)}
+    roofline_full = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("scan_full"), "kernel": "k_scan_main<1,false,false>",
+                     "algorithmic_bytes_per_launch": int(scan_bytes),
+                     "timing": "fathom_scan alone, cold caches, mean of its own timed launches"}
+    # the step's own kernels, timed live in the phase pass: the scan (filtering form) and
+    # the attention; the roofline is the longer one's
+    W = (n + 31) // 32
+    live = {
+        "scan": ("k_scan_main<1,false,true>", "scan_filter",
+                 plane_bytes + 4 * kept_total + 4 * W * G * H),
+        "attention": ("k_sparse_attn", "attn", H * G * (k * (2 * 128 * 2 + 4) + 128 * 4 + 128 * 2)),
+    }
+    phase_rooflines = {}
+    for name, (kname, tkey, nbytes) in live.items():
+        gbs = nbytes / (phases[name] * 1e-3) / 1e9
+        phase_rooflines[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": load_traffic(tkey), "kernel": kname,
+                                 "algorithmic_bytes_per_launch": int(nbytes),
+                                 "ms_per_launch": phases[name]}
+    dominant = max(live, key=lambda nm: phases[nm])
+    roofline = dict(phase_rooflines[dominant])
+    roofline["timing"] = (f"the step's longest kernel ({dominant}), mean over the "
+                          f"{args.steps} steps of the phase pass, events on the launch stream")
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None
@@ -230,6 +256,9 @@ def main():
                    "tokens": n, "d": 128, "budget_bits": B, "k": k, "residency": "hbm",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "roofline_full_scan": roofline_full,
+        "step_phases_ms": phases,
+        "step_phase_rooflines": phase_rooflines,
         "cpu_baseline": cpu,
         "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
         "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
@@ -366,22 +395,49 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     return res
 
 
-def load_traffic(algorithmic_bytes):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
-    taken on the current scan kernel source; else None."""
+TRAFFIC_FILES = {  # kernel -> (counter summary under profiles/, the source it was taken on)
+    "scan_full": ("scan_traffic.json", "scan.hip"),
+    "scan_filter": ("scan_filter_traffic.json", "scan.hip"),
+    "attn": ("attn_traffic.json", "attn.hip"),
+}
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter summary, if
+    the summary was taken on the current source of that kernel; else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "scan_traffic.json")
-    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", "scan.hip")
+    name, srcname = TRAFFIC_FILES[kernel]
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", srcname)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("scan_hip_sha256") != digest:
+        if rec.get("source_sha256", rec.get("scan_hip_sha256")) != digest:
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:
         return None
+
+
+PHASES = ("plan_prepare", "scan", "select", "attention")
+
+
+def step_phases(F, st, q, K, V, B, k, sm, out, ws, stream, steps):
+    """Mean GPU time of each phase of the step over `steps` steps launched back to back
+    through fathom_step_timed (events recorded on the launch stream between kernels)."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(F.STEP_PHASES + 1)]
+           for _ in range(steps)]
+    for e in evs:
+        F.fathom_step_timed(st, q, K, V, B, k, sm, e, out=out, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    res = {}
+    for i, name in enumerate(PHASES):
+        res[name] = round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
+    res["step"] = round(float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])), 4)
+    return res
 
 
 def timed_ms(fn, stream, reps, flush=None, sink=None):

@@ -360,10 +360,13 @@ int fathom_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int
         launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, as_stream(stream)));
 }
 
-int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const uint16_t *V,
-                int G, int B, int k, float sm_scale, uint16_t *out, uint8_t *depth_out,
-                float *scores_out, int32_t *idx_out, void *ws, size_t ws_bytes,
-                void *stream) {
+// The step; with ev non-null, ev[0..FATHOM_STEP_PHASES] are recorded on the stream at
+// the phase boundaries (before the plan, after the plan and scan preparation, after the
+// scan, after the select, after the attention).
+static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
+                     const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                     uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                     size_t ws_bytes, void *stream, const hipEvent_t *ev) {
     FATHOM_TRY(check_store(st));
     if (!q || !K || !V || !out || !ws) return FATHOM_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 2) ||
@@ -394,19 +397,48 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const
     uint32_t *redo = reinterpret_cast<uint32_t *>(w);
 
     const hipStream_t s = as_stream(stream);
+    auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], s)) : FATHOM_OK; };
     // every score is asked for, or no threshold can help (k too close to n for the
     // sample, or B = 0: every score of a row is the same): scan all, then select
-    if (scores_out || sample_rank(n, k) == 0 || B == 0) {
-        FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, 0, depth, scan_ws, s)));
+    const bool full = scores_out || sample_rank(n, k) == 0 || B == 0;
+    FATHOM_TRY(mark(0));
+    FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, full ? 0 : k, depth, scan_ws, s)));
+    FATHOM_TRY(mark(1));
+    if (full) {
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
+        FATHOM_TRY(mark(2));
         FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
     } else {  // the filtering scan keeps the candidates only
-        FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, k, depth, scan_ws, s)));
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
+        FATHOM_TRY(mark(2));
         FATHOM_TRY(hip_status(
             launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
     }
-    return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
+    FATHOM_TRY(mark(3));
+    FATHOM_TRY(hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
+    return mark(4);
+}
+
+int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const uint16_t *V,
+                int G, int B, int k, float sm_scale, uint16_t *out, uint8_t *depth_out,
+                float *scores_out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                void *stream) {
+    return step_impl(st, q, K, V, G, B, k, sm_scale, out, depth_out, scores_out, idx_out, ws,
+                     ws_bytes, stream, nullptr);
+}
+
+int fathom_step_timed(const fathom_store *st, const float *q, const uint16_t *K,
+                      const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                      uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                      size_t ws_bytes, void *stream, void *const *events, int n_events) {
+    if (!events || n_events != FATHOM_STEP_PHASES + 1) return FATHOM_ERR_INVALID_ARG;
+    hipEvent_t ev[FATHOM_STEP_PHASES + 1];
+    for (int i = 0; i <= FATHOM_STEP_PHASES; ++i) {
+        if (!events[i]) return FATHOM_ERR_INVALID_ARG;
+        ev[i] = static_cast<hipEvent_t>(events[i]);
+    }
+    return step_impl(st, q, K, V, G, B, k, sm_scale, out, depth_out, scores_out, idx_out, ws,
+                     ws_bytes, stream, ev);
 }
 
 int fathom_stream_read(const void *src, size_t bytes, uint64_t *sink, void *stream) {

@@ -69,6 +69,9 @@ _SIGS = {
     "fathom_sparse_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P]),
     "fathom_step": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I, ctypes.c_float,
                          _P, _P, _P, _P, _P, _SZ, _P]),
+    "fathom_step_timed": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I,
+                               ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P,
+                               ctypes.POINTER(ctypes.c_void_p), _I]),
     "fathom_scan_extract": (_I, [_P, _P, _I, _P, _P, _P]),
     "fathom_pack_nibbles": (_I, [ctypes.POINTER(fathom_store), _P, _P]),
     "fathom_quantize_groups": (_I, [_P, ctypes.c_int64, ctypes.POINTER(fathom_gstore), _I, _I,
@@ -418,6 +421,35 @@ def fathom_step(store: Store, q, K, V, B: int, k: int, sm_scale: float, out=None
                              float(sm_scale), _ptr(out), _ptr(depth_out), _ptr(scores_out),
                              _ptr(idx_out), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(stream)), "fathom_step")
+    return out
+
+
+STEP_PHASES = 4  # plan + scan preparation, scan, select, attention
+
+
+def fathom_step_timed(store: Store, q, K, V, B: int, k: int, sm_scale: float, events,
+                      out=None, depth_out=None, scores_out=None, idx_out=None, ws=None,
+                      stream=None):
+    """fathom_step with STEP_PHASES + 1 torch.cuda.Event (enable_timing) recorded on the
+    stream at its phase boundaries: events[i].elapsed_time(events[i + 1]) is phase i."""
+    import torch
+    if len(events) != STEP_PHASES + 1:
+        raise ValueError(f"fathom_step_timed needs {STEP_PHASES + 1} events")
+    H, G, d = q.shape
+    if out is None:
+        out = torch.empty((H, G, d), dtype=torch.bfloat16, device=q.device)
+    ws = step_workspace(store, G, k, q.device) if ws is None else ws
+    st = store.descriptor()
+    tstream = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.current_stream()
+    for e in events:  # torch creates an event's handle at its first record
+        if not e.cuda_event:
+            e.record(tstream)
+    handles = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+    _check(lib().fathom_step_timed(ctypes.byref(st), _ptr(q), _ptr(K), _ptr(V), G, int(B),
+                                   int(k), float(sm_scale), _ptr(out), _ptr(depth_out),
+                                   _ptr(scores_out), _ptr(idx_out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream), handles,
+                                   len(events)), "fathom_step_timed")
     return out
 
 

@@ -321,6 +321,25 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K,
                 size_t ws_bytes, void *stream);
 
 /*
+ * fathom_step with its phases timed on the stream, for measuring each kernel inside a
+ * running sequence of steps (blog, "The catch": what a decode step waits on is the index
+ * scan, not the winner rows).  Same arguments, preconditions and results as fathom_step,
+ * plus
+ *   events  FATHOM_STEP_PHASES + 1 hipEvent_t handles created by the caller; events[0] is
+ *           recorded before the plan, events[1] after the plan and scan preparation,
+ *           events[2] after the scan, events[3] after the select, events[4] after the
+ *           attention, each on `stream`, so hipEventElapsedTime(events[i], events[i+1])
+ *           is phase i.  The library keeps no handle past the call.
+ *   n_events must be FATHOM_STEP_PHASES + 1 (else FATHOM_ERR_INVALID_ARG; a NULL handle
+ *           too).  A failed record returns FATHOM_ERR_HIP.
+ */
+#define FATHOM_STEP_PHASES 4
+int fathom_step_timed(const fathom_store *st, const float *q, const uint16_t *K,
+                      const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                      uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                      size_t ws_bytes, void *stream, void *const *events, int n_events);
+
+/*
  * Measurement helper for the roofline denominators (blog, "One measurement worth
  * carrying around": contiguous reads from pinned host memory): streams `bytes`
  * (multiple of 16) from the device-visible address `src` (HBM or pinned host) with

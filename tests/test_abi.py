@@ -129,6 +129,16 @@ def test_attn_and_step_checks():
     assert L.fathom_step(*args(92, 10, need - 1)) == F.ERR_WORKSPACE
     assert L.fathom_step(*args(600, 10, need)) == F.ERR_BUDGET
     assert L.fathom_step(*args(92, 101, need)) == F.ERR_INVALID_ARG
+    # the timed step: the event list is checked first, then everything fathom_step checks
+    # (fake handles are never recorded on these paths)
+    ev = (ctypes.c_void_p * 5)(*[FAKE + 256 * i for i in range(5)])
+    assert L.fathom_step_timed(*args(92, 10, need), None, 5) == F.ERR_INVALID_ARG
+    assert L.fathom_step_timed(*args(92, 10, need), ev, 4) == F.ERR_INVALID_ARG
+    bad = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
+    assert L.fathom_step_timed(*args(92, 10, need), bad, 5) == F.ERR_INVALID_ARG
+    assert L.fathom_step_timed(*args(92, 10, need - 1), ev, 5) == F.ERR_WORKSPACE
+    assert L.fathom_step_timed(*args(600, 10, need), ev, 5) == F.ERR_BUDGET
+    assert F.STEP_PHASES + 1 == 5
 
 
 def test_stream_read_and_host_alloc_checks():

@@ -225,3 +225,34 @@ def test_step_paths_agree_on_random_shapes(H, G, n, B, k, seed):
     assert torch.equal(o1, o2)
     assert np.array_equal(i1.cpu().numpy().reshape(H * G, k),
                           oracle.topk(scores.cpu().numpy().reshape(H * G, n), k))
+
+
+@pytest.mark.parametrize("with_scores", [False, True])
+def test_timed_step_equals_step_and_times_its_phases(with_scores):
+    """fathom_step_timed: the same winners and output as fathom_step (filtering path and
+    full path), with its phase events recorded in order on the stream."""
+    torch = torch_cuda()
+    H, G, n, B, k = 3, 4, 20000, 92, 256
+    print(f"[step timed] with_scores={with_scores}", flush=True)
+    keys, q, K, V = inputs(106, H, G, n, seed=3)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    s1 = torch.empty((H, G, n), dtype=torch.float32, device="cuda") if with_scores else None
+    s2 = torch.empty_like(s1) if with_scores else None
+    i1 = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    o1 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, scores_out=s1, idx_out=i1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(F.STEP_PHASES + 1)]
+    o2 = F.fathom_step_timed(st, q_t, Kd, Vd, B, k, sm, ev, scores_out=s2, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(o1, o2)
+    if with_scores:
+        assert torch.equal(s1, s2)
+    ph = [ev[i].elapsed_time(ev[i + 1]) for i in range(F.STEP_PHASES)]
+    assert all(t > 0 for t in ph)
+    assert abs(sum(ph) - ev[0].elapsed_time(ev[-1])) < 1e-3 + 1e-3 * sum(ph)
+    with pytest.raises(ValueError):
+        F.fathom_step_timed(st, q_t, Kd, Vd, B, k, sm, ev[:4])
