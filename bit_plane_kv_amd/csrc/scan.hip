@@ -44,94 +44,184 @@ __device__ int weight_digit(long long M, int d) {
     return (int)(((M & 255) ^ 128) - 128);
 }
 
+// Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
+// result is byte s of M_p (p = 0..3).  Two butterfly stages, each one DPP move of the
+// partner's word and one byte permute.
+__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t m, int s) {
+    const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
+    const uint32_t a = __builtin_amdgcn_perm(p, m, s < 2 ? 0x05040100u : 0x03020706u);
+    const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
+    return __builtin_amdgcn_perm(q, a, (s & 1) ? 0x03070105u : 0x06020400u);
+}
+
+// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h.
+// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h;
+// hi_mask = 0 when the upper 4 groups do not exist (their operand bytes are zero).
+template <int QS, bool kFirst>
+__device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4i (&A)[QS],
+                                          uint32_t hi_mask, int s, v4i (&acc)[2][8][QS]) {
+#pragma unroll
+    for (int pos = 0; pos < 2; ++pos) {
+        uint32_t x[2][2];  // [half][planes 0-3 / 4-7]
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            x[h][0] = quad_byte_transpose(w[h][0][pos], s);
+            x[h][1] = quad_byte_transpose(w[h][1][pos], s);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t mask = 0x01010101u << m;
+            const uint32_t mhi = mask & hi_mask;
+            const v4i b = {(int)(x[0][0] & mask), (int)(x[0][1] & mask), (int)(x[1][0] & mhi),
+                           (int)(x[1][1] & mhi)};
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {
+                const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[pos][m][set];
+                acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[set], b, c, 0, 0, 0);
+            }
+        }
+    }
+}
+
+// One score from its query's 4 digit sums d (column of bit m of a byte): C + (D0 + 256 D1
+// + 65536 (D2 + 256 D3)) * S / (byte value of bit m).  small: the head has at most 480
+// planes, so D0 + 256 D1 fits int32.
+template <int QS>
+__device__ __forceinline__ float combined_score(const v4i &d, int m, float C, float S,
+                                                bool small) {
+    const float lo = small ? (float)(d[0] + d[1] * 256) : fmaf((float)d[1], 256.0f, (float)d[0]);
+    const float hi = (float)(d[2] + d[3] * 256);
+    const float f = fmaf(hi, 65536.0f, lo);
+    const float mult = m < 7 ? S * (1.0f / (float)(1 << m)) : S * (-1.0f / 128.0f);
+    return fmaf(f, mult, C);
+}
+
 // Candidate thresholds of one head (256 threads).  A guess of each query's score
-// quantile from a sample of the head's tokens (sample_run_word), scored in fp32 from the
-// fp64 weights -- not the scan's arithmetic: only the count of kept tokens decides
-// correctness, and the select checks it.  The sample_rank-th largest sampled key is the
-// threshold: about five standard deviations of the sample quantile above the k the
-// select needs.  The sampled words of up to 128 planes at a time are staged in LDS,
-// one 16-byte load per (plane, run), all in flight together; thread t then scores byte
-// (t & 3) of sampled word (t & 127) >> 2 for the two queries 2 (t >> 7) + {0, 1} of
-// each set of 4.
+// quantile from a sample of the head's tokens (sample_run_word): the sampled tokens are
+// scored exactly as the scan scores them -- the same operand records, matrix-core digit
+// sums and fp32 combine -- and the sample_rank-th largest sampled key is the threshold,
+// about five standard deviations of the sample quantile above the k the select needs.
+// Only the count of kept tokens decides correctness, and the select checks it.  The
+// sampled words of up to 128 planes (two K-pairs) at a time are staged in LDS, 16 bytes
+// per (plane, run), all in flight together (those of the first 128 planes are loaded by
+// sample_issue as soon as the plane list is known); wave v then takes sampled words
+// 8v .. 8v+7 the way a scan wave takes its 8 words of a super-step.
 constexpr int kSamplePlanes = 128;
+constexpr int kSamplePer = kSamplePlanes * kSampleRuns / 256;  // 16-byte loads a thread
+static_assert(kSampleWords == 32, "four waves of 8 sampled words");
+
+// Loads (plane p0 + e / 8, run e % 8), e = tid + 256 u, of the head's plane list pl
+// (np planes from p0).  Every load is unconditional -- a plane past the list reads the
+// store's row 0, a run past a short row the row's first 16 bytes -- so that the
+// compiler keeps them all in flight; sample_stage drops those values.
+__device__ __forceinline__ void sample_issue(const uint32_t *__restrict__ hp, int W,
+                                             int word_stride, const uint32_t *pl, int p0,
+                                             int np, uint4 (&v)[kSamplePer]) {
+#pragma unroll
+    for (int u = 0; u < kSamplePer; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int p = e / kSampleRuns, r = e % kSampleRuns;
+        const int w0 = sample_run_word(r, W);
+        const uint32_t row = p < np ? pl[p0 + p] : 0u;
+        // a run that starts below W lies in the row (word_stride >= 4 * ceil(W / 4))
+        v[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)row * word_stride +
+                                                (w0 < W ? w0 : 0));
+    }
+}
+// Writes the loaded values of real (plane, run) pairs to sw; a run past a short row is
+// zero.  Rows of sw past np keep whatever they hold: their planes have zero weights.
+__device__ __forceinline__ void sample_stage(const uint4 (&v)[kSamplePer], int W, int np,
+                                             uint32_t (*sw)[kSampleWords]) {
+#pragma unroll
+    for (int u = 0; u < kSamplePer; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int p = e / kSampleRuns, r = e % kSampleRuns;
+        const bool live = sample_run_word(r, W) < W;
+        if (p < np)
+            *reinterpret_cast<uint4 *>(&sw[p][kSampleRunWords * r]) =
+                live ? v[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// la: the head's A operand halves [K-block][lane][QS] (8 bytes, as in the records);
+// C, S: each query's constant term and weight unit as the scan reads them.
 template <int QS>
 __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ planes, int n,
                                                   int word_stride, int k, int h,
-                                                  int nplanes, const uint32_t *pl,
-                                                  const double (*wt)[kMaxPlanesPerHead],
-                                                  const double (*red)[kD], ScanMeta *meta) {
+                                                  int nplanes, int nkb, const uint32_t *pl,
+                                                  const uint4 (&first)[kSamplePer],
+                                                  const uint2 *la, const float *C,
+                                                  const float *S, ScanMeta *meta) {
     constexpr int kST = kSampleWords * 32;  // sampled tokens per query
     // the staged words and, once they are used, the sampled keys share one buffer
     __shared__ __align__(16) uint32_t sbuf[kSamplePlanes * kSampleWords];
     static_assert(kSamplePlanes * kSampleWords >= 4 * kST, "sample keys");
     uint32_t(*sw)[kSampleWords] = reinterpret_cast<uint32_t(*)[kSampleWords]>(sbuf);
     uint32_t(*skey)[kST] = reinterpret_cast<uint32_t(*)[kST]>(sbuf);
-    __shared__ float wf[4][kSamplePlanes];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
     const int W = (n + 31) >> 5;
-    const int qh = tid >> 7, rest = tid & 127;
-    const int i = rest >> 2, sb = rest & 3;  // byte sb of sampled word i
-    const int word = sample_run_word(i / kSampleRunWords, W) + i % kSampleRunWords;
-    const bool ok = word < W;
     const uint32_t m = (uint32_t)sample_rank(n, k);
     const uint32_t *hp = planes + (size_t)h * kMaxPlanesPerHead * word_stride;
+    const int npr = (nkb + 1) >> 1;  // K-pairs (nkb >= 1)
+    v4i acc[2][8][QS];
+    for (int kp0 = 0; kp0 < npr; kp0 += 2) {  // batches of two K-pairs (128 planes)
+        const int p0 = 64 * kp0;
+        const int np = max(0, min(kSamplePlanes, nplanes - p0));
+        if (kp0) __syncthreads();  // the previous batch is no longer read
+        if (kp0 == 0) {
+            sample_stage(first, W, np, sw);
+        } else {
+            uint4 v[kSamplePer];
+            sample_issue(hp, W, word_stride, pl, p0, np, v);
+            sample_stage(v, W, np, sw);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int kp = kp0 + kk;
+            if (kp >= npr) break;
+            const bool hi = 2 * kp + 1 < nkb;  // upper 4 groups of the K-pair exist
+            uint32_t w[2][2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                    for (int pos = 0; pos < 2; ++pos)
+                        w[hh][pp][pos] =
+                            sw[64 * kk + 8 * (jq + 4 * hh) + s + 4 * pp][8 * wave + 2 * wq + pos];
+            v4i A[QS];
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {
+                const uint2 alo = la[((2 * kp) * 64 + lane) * QS + set];
+                const uint2 ahi = hi ? la[((2 * kp + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
+                A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
+            }
+            const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
+            if (kp == 0) mma_kpair<QS, true>(w, A, hi_mask, s, acc);
+            else mma_kpair<QS, false>(w, A, hi_mask, s, acc);
+        }
+    }
+    const bool small = nkb < kMaxKBlocks;
 #pragma unroll
     for (int set = 0; set < QS; ++set) {
-        float acc[2][8];
+        __syncthreads();  // the staged words (or the previous set's keys) are no longer read
+        const int g = 4 * set + jq;
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) acc[gg][mm] = (float)red[4 * set + 2 * qh + gg][0];
-        for (int p0 = 0; p0 < nplanes; p0 += kSamplePlanes) {
-            const int np = min(kSamplePlanes, nplanes - p0);
-            __syncthreads();  // the previous batch is no longer read
-            {   // every (plane, run) of the batch: at most 4 per thread, loads first
-                constexpr int kPer = kSamplePlanes * kSampleRuns / 256;
-                uint4 v[kPer];
-#pragma unroll
-                for (int u = 0; u < kPer; ++u) {
-                    const int e = tid + 256 * u;
-                    const int p = e / kSampleRuns, r = e % kSampleRuns;
-                    const int w0 = sample_run_word(r, W);
-                    v[u] = make_uint4(0u, 0u, 0u, 0u);
-                    // a run starts below W and the row holds word_stride >= 4 * ceil(W / 4)
-                    // words, so the 16 bytes lie in the row
-                    if (p < np && w0 < W)
-                        v[u] = *reinterpret_cast<const uint4 *>(
-                            hp + (size_t)pl[p0 + p] * word_stride + w0);
-                }
-#pragma unroll
-                for (int u = 0; u < kPer; ++u) {
-                    const int e = tid + 256 * u;
-                    const int p = e / kSampleRuns, r = e % kSampleRuns;
-                    if (p < np) *reinterpret_cast<uint4 *>(&sw[p][kSampleRunWords * r]) = v[u];
-                }
-            }
-            for (int e = tid; e < 4 * np; e += 256)
-                wf[e / np][e % np] = (float)wt[4 * set + e / np][p0 + e % np];
-            __syncthreads();
-            for (int p = 0; p < np; ++p) {
-                const uint32_t bits = sw[p][i] >> (8 * sb);
-                const float w0 = wf[2 * qh][p], w1 = wf[2 * qh + 1][p];
-#pragma unroll
-                for (int mm = 0; mm < 8; ++mm) {
-                    const float b = (float)((bits >> mm) & 1u);  // 0 or 1: the fma is exact
-                    acc[0][mm] = fmaf(b, w0, acc[0][mm]);
-                    acc[1][mm] = fmaf(b, w1, acc[1][mm]);
-                }
-            }
-        }
-        __syncthreads();  // the staged words are no longer read
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg)
+        for (int pos = 0; pos < 2; ++pos) {
+            const int i = 8 * wave + 2 * wq + pos;  // sampled word
+            const int word = sample_run_word(i / kSampleRunWords, W) + i % kSampleRunWords;
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) {
-                const bool valid = ok && 32 * word + 8 * sb + mm < n;
-                skey[2 * qh + gg][8 * rest + mm] = valid ? order_key(acc[gg][mm]) : 0u;
+                const float v = combined_score<QS>(acc[pos][mm][set], mm, C[g], S[g], small);
+                const bool valid = word < W && 32 * word + 8 * s + mm < n;
+                skey[jq][32 * i + 8 * s + mm] = valid ? order_key(v) : 0u;
             }
+        }
         __syncthreads();
         {   // wave gq: the m-th largest sampled key of query 4*set + gq, bit by bit
-            const int gq = tid >> 6;
+            const int gq = wave;
             constexpr int kPerLane = kST / 64;
             uint32_t kk[kPerLane];
 #pragma unroll
@@ -149,25 +239,48 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             }
             if (lane == 0) meta->tkey[4 * set + gq] = T;
         }
-        __syncthreads();  // skey is reused by the next set
     }
+}
+
+// Inputs of the prepare step a thread reads (threads 0..127: channel tid): the head's
+// queries, scale and zero, loaded together at the start of a kernel.
+template <int QS>
+struct PrepIn {
+    float q[4 * QS];
+    float s, z;
+};
+template <int QS>
+__device__ __forceinline__ void load_prep_in(const float *__restrict__ q,
+                                             const float *__restrict__ scale,
+                                             const float *__restrict__ zero, int G, int h,
+                                             PrepIn<QS> &in) {
+    // unconditional loads (channel and query clamped) so that all are in flight
+    // together; the values a thread does not need are never used or zeroed
+    const int c = min((int)threadIdx.x, kD - 1);
+#pragma unroll
+    for (int g = 0; g < 4 * QS; ++g) in.q[g] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
+    in.s = scale[(size_t)h * kD + c];
+    in.z = zero[(size_t)h * kD + c];
+#pragma unroll
+    for (int g = 0; g < 4 * QS; ++g) in.q[g] = g < G ? in.q[g] : 0.0f;
 }
 
 // Body of the prepare step for head h; tc[c] (LDS, complete) holds the channel depths.
 // 256 threads.
 template <int QS>
-__device__ __forceinline__ void prepare_head(const float *__restrict__ q, const int *tc,
-                                             const float *__restrict__ scale,
-                                             const float *__restrict__ zero, int H, int G,
-                                             const uint32_t *__restrict__ planes, int n,
-                                             int word_stride, int k,
-                                             char *__restrict__ ws, int h) {
+__device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc, int H,
+                                             int G, const uint32_t *__restrict__ planes, int n,
+                                             int word_stride, int k, char *__restrict__ ws,
+                                             int h) {
     constexpr int NQ = 4 * QS;
     __shared__ int off[kD + 1];
     __shared__ uint32_t pl[kMaxPlanesPerHead];
     __shared__ double wt[NQ][kMaxPlanesPerHead];
     __shared__ double red[NQ][kD];
+    __shared__ double inv_unit[NQ];
     __shared__ double unit[NQ];
+    __shared__ uint2 la[kMaxKBlocks * 64 * QS];  // A operand halves, as in the records
+    __shared__ float cf[NQ], sf[NQ];             // C_g and S_g as the scan reads them
     const int tid = threadIdx.x, lane = tid & 63;
     ScanMeta *meta = reinterpret_cast<ScanMeta *>(ws + (size_t)h * kMetaBytes);
     uint32_t *rec = reinterpret_cast<uint32_t *>(ws + (size_t)H * kMetaBytes +
@@ -192,18 +305,23 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
     const int nkb = max(1, (ngroups + kKBlockGroups - 1) / kKBlockGroups);
     if (tid < kD) {
         const int c = tid, t = tc[c], o = off[c];
-        const double s = (double)scale[(size_t)h * kD + c];
-        const double z = (double)zero[(size_t)h * kD + c];
+        const double s = (double)in.s;
+        const double z = (double)in.z;
         const double hm = (double)((16 >> t) - 1) * 0.5;  // bin-midpoint offset h(t)
         for (int j = 0; j < t; ++j) pl[o + j] = (uint32_t)(c * kPlanes + j);
 #pragma unroll
         for (int g = 0; g < NQ; ++g) {
-            const double qv = g < G ? (double)q[((size_t)h * G + g) * kD + c] : 0.0;
+            const double qv = (double)in.q[g];
             for (int j = 0; j < t; ++j) wt[g][o + j] = (qv * s) * (double)(8 >> j);
             red[g][c] = qv * (z + s * hm);  // this channel's share of C_g
         }
     }
     __syncthreads();
+    // the threshold sample's first loads go out now and land during the work below
+    uint4 first[kSamplePer];
+    if (k > 0)
+        sample_issue(planes + (size_t)h * kMaxPlanesPerHead * word_stride, (n + 31) >> 5,
+                     word_stride, pl, 0, min(nplanes, kSamplePlanes), first);
     for (int s2 = kD / 2; s2 > 0; s2 >>= 1) {  // C_g: fixed-order tree sum over channels
         if (tid < s2) {
 #pragma unroll
@@ -221,6 +339,8 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
             int e = 0;
             frexp(mx, &e);  // mx < 2^e
             unit[g] = mx > 0.0 ? ldexp(1.0, e - 30) : 1.0;
+            // a power of two: multiplying by its inverse divides exactly
+            inv_unit[g] = mx > 0.0 ? ldexp(1.0, 30 - e) : 1.0;
         }
     }
     __syncthreads();
@@ -228,6 +348,10 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
     if (tid < FATHOM_MAX_G) {
         meta->C[tid] = tid < G ? (float)red[tid][0] : 0.0f;
         meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
+    }
+    if (tid < NQ) {
+        cf[tid] = tid < G ? (float)red[tid][0] : 0.0f;
+        sf[tid] = tid < G ? (float)unit[tid] : 0.0f;
     }
     if (tid == 0) {
         meta->n_planes = nplanes;
@@ -251,13 +375,14 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
             for (int i = 0; i < kGroupBits; ++i) {
                 const int p = grp * kGroupBits + i;
                 const long long M =
-                    (g < G && p < nplanes) ? llrint(wt[g][p] / unit[g]) : 0LL;
+                    (g < G && p < nplanes) ? llrint(wt[g][p] * inv_unit[g]) : 0LL;
                 const uint32_t byte = (uint32_t)(weight_digit(M, dg) & 0xFF);
                 if (i < 4) wlo |= byte << (8 * i);
                 else whi |= byte << (8 * (i - 4));
             }
             dst[2 + 2 * set] = wlo;
             dst[3 + 2 * set] = whi;
+            la[e * QS + set] = make_uint2(wlo, whi);
         }
         if (QS == 2) dst[6] = dst[7] = 0;
     }
@@ -266,7 +391,8 @@ __device__ __forceinline__ void prepare_head(const float *__restrict__ q, const 
         if (tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
         return;
     }
-    sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, pl, wt, red, meta);
+    sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
+                          meta);
 }
 
 template <int QS>
@@ -277,13 +403,16 @@ __global__ __launch_bounds__(256) void k_scan_prepare(
     char *__restrict__ ws) {
     __shared__ int tc[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
-    if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
+    PrepIn<QS> in;
+    load_prep_in<QS>(q, scale, zero, G, h, in);
+    const int t = depth[(size_t)h * kD + min(tid, kD - 1)];
+    if (tid < kD) tc[tid] = min(t, kPlanes);
     __syncthreads();
-    prepare_head<QS>(q, tc, scale, zero, H, G, planes, n, word_stride, k, ws, h);
+    prepare_head<QS>(in, tc, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // A decode step's plan and prepare in one kernel: the depths stay in LDS between them
-// (and are also written to `depth`).
+// (and are also written to `depth`).  Every input of both is loaded up front.
 template <int QS>
 __global__ __launch_bounds__(256) void k_plan_prepare(
     const float *__restrict__ q, const float *__restrict__ var,
@@ -292,9 +421,13 @@ __global__ __launch_bounds__(256) void k_plan_prepare(
     uint8_t *__restrict__ depth, char *__restrict__ ws) {
     __shared__ int tc[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
-    plan_head(q, var, G, B, h, tc);
+    PrepIn<QS> in;
+    load_prep_in<QS>(q, scale, zero, G, h, in);
+    float qp[2][FATHOM_MAX_G], vp[2];
+    plan_load(q, var, G, h, qp, vp);
+    plan_from(qp, vp, G, B, tc);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];
-    prepare_head<QS>(q, tc, scale, zero, H, G, planes, n, word_stride, k, ws, h);
+    prepare_head<QS>(in, tc, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -354,45 +487,6 @@ constexpr size_t scan_lds_bytes() {
     return 2 * lds_head_bytes<QS>() + (size_t)kTiles * kTileBytes;
 }
 
-// Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
-// result is byte s of M_p (p = 0..3).  Two butterfly stages, each one DPP move of the
-// partner's word and one byte permute.
-__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t m, int s) {
-    const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
-    const uint32_t a = __builtin_amdgcn_perm(p, m, s < 2 ? 0x05040100u : 0x03020706u);
-    const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
-    return __builtin_amdgcn_perm(q, a, (s & 1) ? 0x03070105u : 0x06020400u);
-}
-
-// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h.
-// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h;
-// hi_mask = 0 when the upper 4 groups do not exist (their operand bytes are zero).
-template <int QS, bool kFirst>
-__device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4i (&A)[QS],
-                                          uint32_t hi_mask, int s, v4i (&acc)[2][8][QS]) {
-#pragma unroll
-    for (int pos = 0; pos < 2; ++pos) {
-        uint32_t x[2][2];  // [half][planes 0-3 / 4-7]
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            x[h][0] = quad_byte_transpose(w[h][0][pos], s);
-            x[h][1] = quad_byte_transpose(w[h][1][pos], s);
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const uint32_t mask = 0x01010101u << m;
-            const uint32_t mhi = mask & hi_mask;
-            const v4i b = {(int)(x[0][0] & mask), (int)(x[0][1] & mask), (int)(x[1][0] & mhi),
-                           (int)(x[1][1] & mhi)};
-#pragma unroll
-            for (int set = 0; set < QS; ++set) {
-                const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[pos][m][set];
-                acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[set], b, c, 0, 0, 0);
-            }
-        }
-    }
-}
-
 // score = C + (D0 + 256 D1 + 65536 (D2 + 256 D3)) * S / (byte value of bit m); the
 // digit sums of a head with at most 480 planes fit D0 + 256 D1 in int32.
 template <int QS>
@@ -437,15 +531,6 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
 // tokens grows by the block's.  Within a block the kept scores are ordered by word in
 // the order wb, wb+2, wb+4, wb+6, wb+1, wb+3, wb+5, wb+7 (pos, then w: lane 4w + s of a
 // query's 16 holds byte s of words wb + 2w + pos), and by token within a word.
-template <int QS>
-__device__ __forceinline__ float combined_score(const v4i &d, int m, float C, float S,
-                                                bool small) {
-    const float lo = small ? (float)(d[0] + d[1] * 256) : fmaf((float)d[1], 256.0f, (float)d[0]);
-    const float hi = (float)(d[2] + d[3] * 256);
-    const float f = fmaf(hi, 65536.0f, lo);
-    const float mult = m < 7 ? S * (1.0f / (float)(1 << m)) : S * (-1.0f / 128.0f);
-    return fmaf(f, mult, C);
-}
 
 template <int QS>
 __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const float (&Cq)[QS],
