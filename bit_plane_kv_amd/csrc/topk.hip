@@ -276,8 +276,13 @@ __device__ __forceinline__ void select_chunk(
             key[e + 3] = order_key(f.w);
         }
     } else {
+        // unconditional loads (positions past the chunk read its last entry, then are
+        // dropped), so that all of them are in flight together
+        float x[kEPT];
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) key[e] = e < nvalid ? order_key(v[p0 + e]) : 0u;
+        for (int e = 0; e < kEPT; ++e) x[e] = v[min(p0 + e, len - 1)];
+#pragma unroll
+        for (int e = 0; e < kEPT; ++e) key[e] = e < nvalid ? order_key(x[e]) : 0u;
     }
 
     // ---- pass 1: top 12 bits of every key
@@ -476,13 +481,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     const int wl = kSelWords * tid;
     const int64_t wg = (int64_t)chunk * (kTopkChunk / 32) + wl;
     uint32_t mk[kSelWords], c[kSelWords];
+    // every load unconditional (a word past the row reads the row's last word, then
+    // masked off), so that they are all in flight together
+#pragma unroll
+    for (int j = 0; j < kSelWords; ++j)
+        mk[j] = fa.masks[row * fa.W + min(wg + j, (int64_t)fa.W - 1)];
+    const uint32_t kept = meta->cnt[g];
 #pragma unroll
     for (int j = 0; j < kSelWords; ++j) {
         const int t0 = 32 * (wl + j);  // first chunk token of the word
         const uint32_t lm = t0 >= len ? 0u : (len - t0 >= 32 ? 0xFFFFFFFFu : (1u << (len - t0)) - 1u);
-        mk[j] = wg + j < fa.W ? fa.masks[row * fa.W + wg + j] & lm : 0u;
+        mk[j] = wg + j < fa.W ? mk[j] & lm : 0u;
     }
-    const bool full = meta->cnt[g] < (uint32_t)k;  // the row is rescored by the full select
+    const bool full = kept < (uint32_t)k;  // the row is rescored by the full select
 #pragma unroll
     for (int j = 0; j < kSelWords; ++j) {
         if (full) mk[j] = 0u;
