@@ -33,15 +33,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // prepare: plane list, constant terms, weight units and MFMA operand records of one
 // head (one workgroup)
 // ---------------------------------------------------------------------------------
-// Digit d (0..3) of M in signed base 256: M = sum_d 256^d digit_d, digits 0..2 in
-// [-128, 127]; for |M| <= 2^30 the top digit lies in [-64, 64].
-__device__ int weight_digit(long long M, int d) {
-    for (int k = 0; k < d; ++k) {
-        const long long low = ((M & 255) ^ 128) - 128;
-        M = (M - low) >> 8;
-    }
-    if (d == kDigits - 1) return (int)M;
-    return (int)(((M & 255) ^ 128) - 128);
+// Signed base-256 digits of M: M = sum_d 256^d digit_d, digits 0..2 in [-128, 127];
+// for |M| <= 2^30 the top digit lies in [-64, 64].  With u = M + kDigitBias, bits
+// 8d .. 8d+7 of u are digit_d + 128 for d < 3 (adding 128 to each lower digit makes
+// it a byte, and the carries line up), and u >> 24 is the top digit.
+constexpr long long kDigitBias = 128LL * (1 + 256 + 65536);
+// Byte d (0..3) of an operand record: digit d of M as a two's-complement byte, from
+// u = M + kDigitBias.
+__device__ __forceinline__ uint32_t weight_byte(long long u, int d) {
+    return d < kDigits - 1 ? ((uint32_t)(u >> (8 * d)) & 255u) ^ 128u
+                           : (uint32_t)(u >> 24) & 255u;
 }
 
 // Byte transpose across a quad: lane s holds word M_s; afterwards byte p of lane s's
@@ -143,6 +144,55 @@ __device__ __forceinline__ void sample_stage(const uint4 (&v)[kSamplePer], int W
     }
 }
 
+// The m-th largest (m >= 1) of the wave's 64 N keys with its low 12 bits cleared (the
+// top 20 bits suffice for a guess), bit by bit from the top: the largest such T with at
+// least m keys >= T.
+template <int N>
+__device__ __forceinline__ uint32_t rank_top_bits(const uint32_t (&kk)[N], uint32_t m) {
+    uint32_t T = 0u;
+    for (int b = 31; b >= 12; --b) {
+        const uint32_t cand = T | (1u << b);
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < N; ++e) c += (uint32_t)__popcll(__ballot(kk[e] >= cand));
+        if (c >= m) T = cand;
+    }
+    return T;
+}
+
+// rank_top_bits of the wave's 1024 sampled keys, searched over fewer keys: with L the
+// same search over the 64 lane maxima (m <= 64), at least m keys are >= L, so the
+// m-th largest key is too, and every count the search compares with m is the same over
+// the keys >= L as over all of them (below L both are >= m).  When at most 128 keys
+// are >= L they are compacted into buf (this wave's 128 words of LDS) and searched two
+// a lane; otherwise all 16 a lane are.
+__device__ __forceinline__ uint32_t sample_quantile(const uint32_t (&kk)[16], uint32_t m,
+                                                    int lane, uint32_t *buf) {
+    if (m > 64u) return rank_top_bits(kk, m);
+    uint32_t mx[1] = {kk[0]};
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx[0] = max(mx[0], kk[e]);
+    const uint32_t L = rank_top_bits(mx, m);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c += kk[e] >= L;
+    uint32_t inc = c;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)inc, 63, 64);
+    if (total > 128u) return rank_top_bits(kk, m);
+    uint32_t pos = inc - c;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        if (kk[e] >= L) buf[pos++] = kk[e];
+    const uint32_t two[2] = {(uint32_t)lane < total ? buf[lane] : 0u,
+                             (uint32_t)lane + 64u < total ? buf[lane + 64] : 0u};
+    return rank_top_bits(two, m);
+}
+
 // la: the head's A operand halves [K-block][lane][QS] (8 bytes, as in the records);
 // C, S: each query's constant term and weight unit as the scan reads them.
 template <int QS>
@@ -220,23 +270,14 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             }
         }
         __syncthreads();
-        {   // wave gq: the m-th largest sampled key of query 4*set + gq, bit by bit
+        {   // wave gq: the m-th largest sampled key of query 4*set + gq
             const int gq = wave;
             constexpr int kPerLane = kST / 64;
             uint32_t kk[kPerLane];
 #pragma unroll
             for (int e = 0; e < kPerLane; ++e) kk[e] = skey[gq][lane + 64 * e];
-            uint32_t T = 0u;  // the top 20 bits of the key suffice for a guess
-            if (m > 0u) {
-                for (int b = 31; b >= 12; --b) {
-                    const uint32_t cand = T | (1u << b);
-                    uint32_t c = 0u;
-#pragma unroll
-                    for (int e = 0; e < kPerLane; ++e)
-                        c += (uint32_t)__popcll(__ballot(kk[e] >= cand));
-                    if (c >= m) T = cand;
-                }
-            }
+            // the wave's own row of skey, now in registers, holds the compacted keys
+            const uint32_t T = m > 0u ? sample_quantile(kk, m, lane, skey[gq]) : 0u;
             if (lane == 0) meta->tkey[4 * set + gq] = T;
         }
     }
@@ -344,6 +385,14 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         }
     }
     __syncthreads();
+    // each weight as an integer count of its query's unit, biased by 128 (1 + 256 +
+    // 65536) so that its signed base-256 digits are plain bytes (weight_byte); written
+    // over the weight it comes from
+    long long(*Mu)[kMaxPlanesPerHead] = reinterpret_cast<long long(*)[kMaxPlanesPerHead]>(wt);
+    for (int e = tid; e < NQ * nplanes; e += 256) {
+        const int g = e / nplanes, p = e - g * nplanes;
+        Mu[g][p] = (g < G ? llrint(wt[g][p] * inv_unit[g]) : 0LL) + kDigitBias;
+    }
     for (int p = tid; p < nplanes; p += 256) meta->plane[p] = pl[p];
     if (tid < FATHOM_MAX_G) {
         meta->C[tid] = tid < G ? (float)red[tid][0] : 0.0f;
@@ -359,6 +408,7 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         meta->n_kblocks = nkb;
         meta->redo = 0u;
     }
+    __syncthreads();
     // operand records: lane ln of K-block kbl serves group 4*kbl + (ln >> 4)
     for (int e = tid; e < nkb * 64; e += 256) {
         const int kbl = e >> 6, ln = e & 63;
@@ -372,11 +422,10 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         for (int set = 0; set < QS; ++set) {
             const int g = 4 * set + (r >> 2), dg = r & 3;
             uint32_t wlo = 0, whi = 0;
+#pragma unroll
             for (int i = 0; i < kGroupBits; ++i) {
                 const int p = grp * kGroupBits + i;
-                const long long M =
-                    (g < G && p < nplanes) ? llrint(wt[g][p] * inv_unit[g]) : 0LL;
-                const uint32_t byte = (uint32_t)(weight_digit(M, dg) & 0xFF);
+                const uint32_t byte = weight_byte(p < nplanes ? Mu[g][p] : kDigitBias, dg);
                 if (i < 4) wlo |= byte << (8 * i);
                 else whi |= byte << (8 * (i - 4));
             }
