@@ -10,7 +10,7 @@ __global__ __launch_bounds__(256) void k_plan(const float *__restrict__ q,
                                               uint8_t *__restrict__ depth) {
     __shared__ int cnt[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
-    float qp[2][FATHOM_MAX_G], vp[2];
+    float qp[FATHOM_MAX_G], vp;
     plan_load(q, var, G, h, qp, vp);
     plan_from(qp, vp, G, B, cnt);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)cnt[tid];

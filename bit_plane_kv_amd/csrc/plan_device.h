@@ -9,23 +9,21 @@
 // The greedy form (B times, give a plane to the channel with the largest w_c 4^-t_c,
 // equal values to the lower channel index) takes exactly the first B of the 4d items
 // (c, t) ordered by key w_c 4^-t descending, then c ascending, then t ascending, because
-// each channel's keys fall with t.  The body sorts those 512 items (a bitonic network)
-// and counts, per channel, the items among the first B.
+// each channel's keys fall with t.  So depth_c = #{t : rank(c, t) < B}, rank = the
+// number of items before (c, t) in that order.
 //
-// Sort layout: item i = 4c + t; wave v holds items 128v .. 128v+127, lane l items
-// 128v + l (register 0) and 128v + 64 + l (register 1).  Compare-exchanges of stride
-// < 64 pair lanes of one wave (shuffles), stride 64 pairs a lane's two registers, and
-// only the strides 128 and 256 (three stages) go through LDS with a barrier.
+// The ranks come from the channels alone.  With the channels sorted by (w descending,
+// c ascending) and pos(X, c) = #{c' : w_c' > X, or w_c' = X and c' < c} (a binary search
+// in that order), item (c', t') comes before (c, t) exactly when channel c' comes
+// before (X, c) for X = w_c 4^(t' - t) (an exact scaling), except that the items of a
+// channel with w_c = 0 are all equal and ordered by t.  Hence
+//   rank(c, t) = sum over t' = 0..3 of pos(w_c 4^(t' - t), c)  (+ t when w_c = 0),
+// seven searches per channel (t' - t = -3 .. 3).
 #pragma once
 
 #include "common.h"
 
 namespace fathom {
-
-// item a precedes item b: larger key first, then lower item number (= c*4 + t)
-__device__ __forceinline__ bool plan_precedes(uint64_t ka, int ia, uint64_t kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
 
 // Importance of a channel from its G query values and its variance: w_c =
 // (sum_g q_gc^2) * var_c in fp64; each square is exact, the sum runs over g ascending,
@@ -43,115 +41,87 @@ __device__ __forceinline__ double plan_importance(const float (&qc)[FATHOM_MAX_G
     return sq * (double)v;
 }
 
-// Position i of the sorted order keeps, from the pair (mine, the partner at i ^ stride),
-// the item that comes first when i is the lower position of an ascending block or the
-// upper of a descending one, else the other.
-__device__ __forceinline__ void plan_keep(uint64_t &k, int &it, uint64_t ok, int oi, int i,
-                                          int stride, int size) {
-    const bool want_first = ((i & stride) == 0) == ((i & size) == 0);
-    const bool mine_first = plan_precedes(k, it, ok, oi);
-    if (want_first != mine_first) {
-        k = ok;
-        it = oi;
-    }
+// The channel a thread plans: two threads per channel.
+__device__ __forceinline__ int plan_channel() { return (int)(threadIdx.x >> 1); }
+
+// Loads the plan's inputs of this thread's channel: its G queries and its variance.
+// Every load is unconditional (query clamped to a real one) so that all of them are in
+// flight together; the unused values are zeroed afterwards.
+__device__ __forceinline__ void plan_load(const float *__restrict__ q,
+                                          const float *__restrict__ var, int G, int h,
+                                          float (&qp)[FATHOM_MAX_G], float &vp) {
+    const int c = plan_channel();
+#pragma unroll
+    for (int g = 0; g < FATHOM_MAX_G; ++g) qp[g] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
+    vp = var[(size_t)h * kD + c];
+#pragma unroll
+    for (int g = 0; g < FATHOM_MAX_G; ++g) qp[g] = g < G ? qp[g] : 0.0f;
 }
 
-// Sorts the 512 items of one head and writes each channel's depth (the number of its
-// items among the first B) to cnt[0..127] (LDS); 256 threads.  wc[r] is the importance
-// of the channel of this thread's item r (see the layout above).  Ends with a barrier,
-// so cnt is complete for every thread.
-__device__ __forceinline__ void plan_sort(const double (&wc)[2], int B, int *cnt) {
-    __shared__ uint64_t xk[2][kMaxPlanesPerHead];
-    __shared__ int xi[2][kMaxPlanesPerHead];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < kD) cnt[tid] = 0;  // complete after the first cross-wave stage's barrier
-    uint64_t k[2];
-    int it[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        it[r] = 128 * wave + 64 * r + lane;
-        // keys are >= +0, so their bit patterns order like the values; w 4^-t is exact
-        k[r] = (uint64_t)__double_as_longlong(ldexp(wc[r], -2 * (it[r] & 3)));
+// Whole plan of head h from the loaded inputs: each channel's depth to cnt[0..127]
+// (LDS); 256 threads; ends with a barrier, so cnt is complete for every thread.
+__device__ __forceinline__ void plan_from(const float (&qp)[FATHOM_MAX_G], float vp, int G,
+                                          int B, int *cnt) {
+    struct Entry {  // a channel in sorted order
+        double w;
+        int c, pad;
+    };
+    __shared__ double wsh[kD];
+    __shared__ Entry srt[kD];
+    const int tid = threadIdx.x, c = plan_channel(), half = tid & 1;
+    const double w = plan_importance(qp, vp, G);
+    if (!half) wsh[c] = w;
+    __syncthreads();
+    // the channel's place in (w descending, c ascending): each thread counts half
+    int rank = 0;
+#pragma unroll 8
+    for (int o = 64 * half; o < 64 * half + 64; ++o) {
+        const double x = wsh[o];
+        rank += (x > w) || (x == w && o < c);
     }
-    int buf = 0;
+    rank += __shfl_xor(rank, 1, 64);
+    if (!half) srt[rank] = Entry{w, c, 0};
+    __syncthreads();
+    // pos(w 4^j, c): thread half 0 searches j = -3 .. 0, half 1 j = 1 .. 3 (j = 4 is a
+    // dummy), all four at once: the length of the prefix of the sorted channels that
+    // comes before (X, c), found by steps of 128, 64, .., 1 (0 .. 128 channels)
+    double X[4];
+    int pos[4];
 #pragma unroll
-    for (int size = 2; size <= kMaxPlanesPerHead; size <<= 1) {
+    for (int s = 0; s < 4; ++s) {
+        X[s] = ldexp(w, 2 * (half ? s + 1 : s - 3));
+        pos[s] = 0;
+    }
 #pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride >= 128) {  // across waves, through LDS (two buffers alternate)
+    for (int step = kD; step > 0; step >>= 1) {
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int i = 128 * wave + 64 * r + lane;
-                    xk[buf][i] = k[r];
-                    xi[buf][i] = it[r];
-                }
-                __syncthreads();
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int i = 128 * wave + 64 * r + lane;
-                    plan_keep(k[r], it[r], xk[buf][i ^ stride], xi[buf][i ^ stride], i, stride,
-                              size);
-                }
-                buf ^= 1;
-            } else if (stride == 64) {  // a lane's two registers
-                const int i = 128 * wave + lane;
-                const uint64_t k0 = k[0];
-                const int i0 = it[0];
-                plan_keep(k[0], it[0], k[1], it[1], i, 64, size);
-                plan_keep(k[1], it[1], k0, i0, i + 64, 64, size);
-            } else {  // lanes of one wave
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int i = 128 * wave + 64 * r + lane;
-                    const uint64_t ok = (uint64_t)__shfl_xor((long long)k[r], stride, 64);
-                    const int oi = __shfl_xor(it[r], stride, 64);
-                    plan_keep(k[r], it[r], ok, oi, i, stride, size);
-                }
+        for (int s = 0; s < 4; ++s) {
+            if (pos[s] + step <= kD) {
+                const Entry e = srt[pos[s] + step - 1];
+                if (e.w > X[s] || (e.w == X[s] && e.c < c)) pos[s] += step;
             }
         }
     }
+    // P[j + 3] = pos(w 4^j, c) for j = -3 .. 3, from both threads of the channel
+    int P[7];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int i = 128 * wave + 64 * r + lane;  // position in the sorted order
-        if (i < B) atomicAdd(&cnt[it[r] >> 2], 1);
+    for (int s = 0; s < 4; ++s) {
+        const int other = __shfl_xor(pos[s], 1, 64);
+        const int lo = half ? other : pos[s];   // j = s - 3
+        const int hi = half ? pos[s] : other;   // j = s + 1
+        P[s] = lo;
+        if (s < 3) P[s + 4] = hi;
     }
+    int depth = 0;
+#pragma unroll
+    for (int t = 0; t < kPlanes; ++t) {
+        int r = w == 0.0 ? t : 0;
+#pragma unroll
+        for (int tp = 0; tp < kPlanes; ++tp) r += P[tp - t + 3];
+        depth += r < B;
+    }
+    if (!half) cnt[c] = depth;
     __syncthreads();
-}
-
-// The channel of this thread's sort item r (see the layout above).
-__device__ __forceinline__ int plan_item_channel(int r) {
-    return (128 * (threadIdx.x >> 6) + 64 * r + (threadIdx.x & 63)) >> 2;
-}
-
-// Loads the plan's inputs for this thread's two sort items: the G queries and the
-// variance of each item's channel.
-__device__ __forceinline__ void plan_load(const float *__restrict__ q,
-                                          const float *__restrict__ var, int G, int h,
-                                          float (&qp)[2][FATHOM_MAX_G], float (&vp)[2]) {
-    // every load is unconditional (index clamped to a real query) so that all of them
-    // are in flight together; the unused values are zeroed afterwards
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int c = plan_item_channel(r);
-#pragma unroll
-        for (int g = 0; g < FATHOM_MAX_G; ++g)
-            qp[r][g] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
-        vp[r] = var[(size_t)h * kD + c];
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int g = 0; g < FATHOM_MAX_G; ++g) qp[r][g] = g < G ? qp[r][g] : 0.0f;
-}
-
-// Whole plan of head h from the loaded inputs: depths to cnt[0..127] (LDS); 256
-// threads; ends with a barrier.
-__device__ __forceinline__ void plan_from(const float (&qp)[2][FATHOM_MAX_G],
-                                          const float (&vp)[2], int G, int B, int *cnt) {
-    double wc[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) wc[r] = plan_importance(qp[r], vp[r], G);
-    plan_sort(wc, B, cnt);
 }
 
 }  // namespace fathom

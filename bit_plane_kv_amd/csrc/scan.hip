@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256) void k_plan_prepare(
     const int h = blockIdx.x, tid = threadIdx.x;
     PrepIn<QS> in;
     load_prep_in<QS>(q, scale, zero, G, h, in);
-    float qp[2][FATHOM_MAX_G], vp[2];
+    float qp[FATHOM_MAX_G], vp;
     plan_load(q, var, G, h, qp, vp);
     plan_from(qp, vp, G, B, tc);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];

@@ -79,6 +79,28 @@ def test_plan_matches_oracle(G, B):
     assert (depth.cpu().numpy().astype(int).sum(axis=1) == B).all()
 
 
+@pytest.mark.parametrize("value", [0.0, 3.0])
+@pytest.mark.parametrize("B", [0, 1, 92, 127, 128, 129, 136, 384, 511, 512])
+def test_plan_all_channels_equal(value, B):
+    """Every channel of equal importance: ties everywhere, including the case where
+    every channel outranks an item.  Equal nonzero w, B = 136: depth 2 on channels
+    0-7 and 1 on the rest; w = 0: every key is 0, so items go by (c, t) and whole
+    channels fill in index order."""
+    torch = torch_cuda()
+    H, G = 3, 4
+    q = np.ones((H, G, 128), np.float32)
+    var = np.full((H, 128), value, np.float32)
+    st = F.Store.empty(H, 64, "cuda")
+    st.var.copy_(to_dev(var))
+    depth = F.fathom_plan(st, to_dev(q), B).cpu().numpy()
+    ref = oracle.plan(q, var, B)
+    assert np.array_equal(depth, ref)
+    if B == 136 and value > 0:
+        assert (ref[:, :8] == 2).all() and (ref[:, 8:] == 1).all()
+    if value == 0:
+        assert (ref[:, :B // 4] == 4).all() and (ref[:, B // 4 + 1:] == 0).all()
+
+
 @pytest.mark.parametrize("nc", [0, 1, 34, 128])
 def test_plan_fixed_matches_oracle(nc):
     torch = torch_cuda()
