@@ -47,10 +47,12 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_groups(
     {
         constexpr int kPer = kGroup * kD / 4 / kQThreads;  // float4 loads per thread: 8
         float4 v[kPer];
+        // unconditional loads (a slot past the group's tokens reads its last token's, and
+        // is dropped), so that all of them are in flight together; nt >= 1
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
             const int e = tid + kQThreads * r;  // float4 e: token e / 32, channels 4 (e % 32)..
-            if (e / (kD / 4) < nt) v[r] = src[e];
+            v[r] = src[min(e / (kD / 4), nt - 1) * (kD / 4) + e % (kD / 4)];
         }
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
@@ -168,6 +170,7 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
     __shared__ __align__(16) uint32_t words[kGRowsMax][kGRowPad];
     __shared__ float qs[GP][kD];
     __shared__ __half sgrp[kD][kGGroups];
+    __shared__ __half zgrp[kD][kGGroups];
     __shared__ float cg[kGGroups][GP];
     __shared__ int tc[kD];
     __shared__ int off[kD + 1];
@@ -177,15 +180,36 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
     const int n = gs.n_tokens, W = (n + 31) >> 5;
     const int ng = (n + kGroup - 1) / kGroup;
     const int w0 = tile * kGWords, gb = w0 / kGroupWords;  // first word, first group
-    if (tid < kD) tc[tid] = min((int)depth[(size_t)h * kD + tid], kPlanes);
-    for (int e = tid; e < GP * kD; e += kGThreads) {
-        const int g = e / kD, c = e - g * kD;
-        qs[g][c] = g < G ? q[((size_t)h * G + g) * kD + c] : 0.0f;
+    // Every input load is unconditional (indices clamped into the head's tables) and
+    // issued before any is used, so that they are all in flight together.
+    constexpr int kQPer = (GP * kD + kGThreads - 1) / kGThreads;
+    constexpr int kSPer = kD * kGGroups / kGThreads;  // 8
+    const int tdep = depth[(size_t)h * kD + min(tid, kD - 1)];
+    float qv[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+        const int e = min(tid + kGThreads * u, GP * kD - 1), g = e / kD, c = e - g * kD;
+        qv[u] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
     }
-    for (int e = tid; e < kD * kGGroups; e += kGThreads) {
-        const int c = e / kGGroups, gg = e - c * kGGroups;
-        const int Gi = min(gb + gg, ng - 1);
-        sgrp[c][gg] = __ushort_as_half(gs.scale16[((size_t)h * kD + c) * gs.group_stride + Gi]);
+    uint16_t sv[kSPer], zv[kSPer];
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+        const int e = tid + kGThreads * u, c = e / kGGroups, gg = e - c * kGGroups;
+        const size_t t = ((size_t)h * kD + c) * gs.group_stride + min(gb + gg, ng - 1);
+        sv[u] = gs.scale16[t];
+        zv[u] = gs.zero16[t];
+    }
+    if (tid < kD) tc[tid] = min(tdep, kPlanes);
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+        const int e = tid + kGThreads * u, g = e / kD, c = e - g * kD;
+        if (e < GP * kD) qs[g][c] = g < G ? qv[u] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+        const int e = tid + kGThreads * u, c = e / kGGroups, gg = e - c * kGGroups;
+        sgrp[c][gg] = __ushort_as_half(sv[u]);
+        zgrp[c][gg] = __ushort_as_half(zv[u]);
     }
     __syncthreads();
     if (tid < 64) {  // exclusive prefix sum of the depths, 2 channels a lane
@@ -204,13 +228,11 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
     // C per (group, query): fp64 over channels ascending
     if (tid < kGGroups * GP) {
         const int gg = tid / GP, g = tid - gg * GP;
-        const int Gi = min(gb + gg, ng - 1);
         double acc = 0.0;
         for (int c = 0; c < kD; ++c) {
-            const size_t t = ((size_t)h * kD + c) * gs.group_stride + Gi;
-            const double zf = (double)__half2float(__ushort_as_half(gs.zero16[t]));
-            const double sf = (double)__half2float(__ushort_as_half(gs.scale16[t]));
-            const double hm = (double)((16 >> min((int)depth[(size_t)h * kD + c], kPlanes)) - 1) * 0.5;
+            const double zf = (double)__half2float(zgrp[c][gg]);
+            const double sf = (double)__half2float(sgrp[c][gg]);
+            const double hm = (double)((16 >> tc[c]) - 1) * 0.5;
             acc += (double)qs[g][c] * (zf + sf * hm);
         }
         cg[gg][g] = (float)acc;
@@ -236,13 +258,28 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
         while (c1 < kD && off[c1 + 1] - off[c0] <= kGRowsMax) ++c1;
         const int r0 = off[c0], nr = off[c1] - r0;
         __syncthreads();  // the previous batch's words are no longer read
-        for (int e = tid; e < nr * 16; e += kGThreads) {
-            const int r = e >> 4, v = e & 15;
-            const int wv = w0 + 4 * v;
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (wv < gs.word_stride)  // word_stride is a multiple of 4
-                x = *reinterpret_cast<const uint4 *>(hp + (size_t)pl[r0 + r] * gs.word_stride + wv);
-            *reinterpret_cast<uint4 *>(&words[r][4 * v]) = x;
+        if (nr > 0) {  // pl holds the batch's rows only when it has any (all depths 0:
+                       // no row, no load)
+            // the batch's rows, 16 bytes a load, all loads unconditional and in flight
+            // together (a slot past the batch reads its last row, one past the row the
+            // row's first 16 bytes, and is dropped)
+            constexpr int kBPer = kGRowsMax * 16 / kGThreads;  // 6
+            uint4 x[kBPer];
+#pragma unroll
+            for (int u = 0; u < kBPer; ++u) {
+                const int e = tid + kGThreads * u, r = e >> 4, v = e & 15;
+                const int wv = w0 + 4 * v;  // word_stride is a multiple of 4
+                const int row = pl[r0 + min(r, nr - 1)];
+                x[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)row * gs.word_stride +
+                                                        (wv < gs.word_stride ? wv : 0));
+            }
+#pragma unroll
+            for (int u = 0; u < kBPer; ++u) {
+                const int e = tid + kGThreads * u, r = e >> 4, v = e & 15;
+                if (r < nr)
+                    *reinterpret_cast<uint4 *>(&words[r][4 * v]) =
+                        w0 + 4 * v < gs.word_stride ? x[u] : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         __syncthreads();
         for (int c = c0; c < c1; ++c) {
