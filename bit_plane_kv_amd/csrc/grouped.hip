@@ -13,12 +13,13 @@
 //   term by term, groups ascending, var = (n Q - S^2) / n^2 rounded once to fp32.
 // * The scan reads a channel's planes to its depth as the bit-plane scan does, with each
 //   group's fp16 scale and zero: score_g(i) = C_gG + sum_c fl32(q_gc sf_cG) P_c(i), P the
-//   t-plane prefix times 2^(4-t), C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64.
-//   The matrix-core scan does not apply: its weights are shared by the 16 tokens of an
-//   MFMA column block, which here would straddle two groups with different scales.
+//   t-plane prefix times 2^(4-t), C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64.  It
+//   runs on the int8 matrix cores like the per-channel scan, with weights rebuilt for
+//   every group and MFMA column blocks that never straddle two groups (below).
 #include <hip/hip_fp16.h>
 
 #include "common.h"
+#include "scan_device.h"
 
 namespace fathom {
 namespace {
@@ -54,11 +55,11 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_groups(
             const int e = tid + kQThreads * r;  // float4 e: token e / 32, channels 4 (e % 32)..
             v[r] = src[min(e / (kD / 4), nt - 1) * (kD / 4) + e % (kD / 4)];
         }
+        // rows past the group's tokens get the copies (they are never read: every read
+        // below stays below the thread's own token count)
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int e = tid + kQThreads * r;
-            if (e / (kD / 4) < nt) reinterpret_cast<float4 *>(&tile[0][0])[e] = v[r];
-        }
+        for (int r = 0; r < kPer; ++r)
+            reinterpret_cast<float4 *>(&tile[0][0])[tid + kQThreads * r] = v[r];
     }
     __syncthreads();
     const int nb = min(32, max(0, nt - 32 * w));  // this thread's tokens
@@ -153,48 +154,61 @@ __global__ __launch_bounds__(kD) void k_var_groups(fathom_gstore gs, int g0) {
 }
 
 // ---------------------------------------------------------------------------------
-// scan: one workgroup of 256 threads per 2048 tokens (64 words, 16 groups) of a head;
-// channel rows staged in LDS a batch at a time; thread (w, s) owns byte s of word w,
-// i.e. 8 tokens of group w / 4.
+// scan on the matrix cores.  A score is C_gG + sum over the planes P = (c, j) the plan
+// reads of bit_P * w_gGP, w_gGP = fl32(q_gc sf_cG) 2^(3-j): the per-channel scan's
+// product of a token-by-plane bit matrix and a plane-by-query weight matrix, except
+// that the weights change every 128-token group.  So each 16-column MFMA block must lie
+// in one group: wave v of a workgroup scores words 8v .. 8v+7 (groups 2v and 2v+1 of a
+// 32-word tile), and lane 16 q + 4 w + s reads word 8v + 4 pos + w of planes s and s+4
+// of plane groups q and q+4 of the K-pair, so that pos picks the group.  The A operand
+// (16 rows = 4 queries x 4 digits, K = 64 planes) of each (K-pair, group) is built in
+// registers: each weight becomes an integer count of a per-(query, group) power-of-two
+// unit (2^(e-30), e the binary exponent just above the group's largest weight of that
+// query), split into 4 signed base-256 digits; the four lanes of a quad (one digit each)
+// share the 16 weights of their K-slice, computing 4 each.  The int32 digit sums are
+// exact; each score is C + S (D0 + 256 D1 + 65536 (D2 + 256 D3)) / 2^m in fp32 as in the
+// per-channel scan, C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64 rounded once.
 // ---------------------------------------------------------------------------------
-constexpr int kGThreads = 256;
-constexpr int kGWords = 64;
-constexpr int kGGroups = kGWords / kGroupWords;  // 16
-constexpr int kGRowsMax = 96;
-constexpr int kGRowPad = kGWords + 4;
+constexpr int kMThreads = 256;                     // 4 waves
+constexpr int kMWords = 32;                        // words per tile: 8 per wave
+constexpr int kMGroups = kMWords / kGroupWords;    // 8 groups per tile, 2 per wave
+constexpr int kMBatch = 128;                       // planes staged at once: two K-pairs
+constexpr int kMRowPad = kMWords + 4;              // 16-byte aligned LDS rows
 
-template <int GP>
-__global__ __launch_bounds__(kGThreads) void k_scan_grouped(
+template <int QS>
+__global__ __launch_bounds__(kMThreads) void k_scan_grouped_mma(
     fathom_gstore gs, const float *__restrict__ q, const uint8_t *__restrict__ depth, int G,
     float *__restrict__ scores, int tiles_per_head) {
-    __shared__ __align__(16) uint32_t words[kGRowsMax][kGRowPad];
-    __shared__ float qs[GP][kD];
-    __shared__ __half sgrp[kD][kGGroups];
-    __shared__ __half zgrp[kD][kGGroups];
-    __shared__ float cg[kGGroups][GP];
+    constexpr int NQ = 4 * QS;
+    __shared__ __align__(16) uint32_t words[kMBatch][kMRowPad];
+    __shared__ float qs[NQ][kD];
+    __shared__ __half sgrp[kD][kMGroups];
+    __shared__ __half zgrp[kD][kMGroups];
+    __shared__ float cg[kMGroups][NQ];
     __shared__ int tc[kD];
     __shared__ int off[kD + 1];
     __shared__ uint16_t pl[kMaxPlanesPerHead];
     const int h = blockIdx.x / tiles_per_head, tile = blockIdx.x - h * tiles_per_head;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = gs.n_tokens, W = (n + 31) >> 5;
     const int ng = (n + kGroup - 1) / kGroup;
-    const int w0 = tile * kGWords, gb = w0 / kGroupWords;  // first word, first group
-    // Every input load is unconditional (indices clamped into the head's tables) and
-    // issued before any is used, so that they are all in flight together.
-    constexpr int kQPer = (GP * kD + kGThreads - 1) / kGThreads;
-    constexpr int kSPer = kD * kGGroups / kGThreads;  // 8
+    const int w0 = tile * kMWords, gb = w0 / kGroupWords;  // first word, first group
+
+    // inputs: every load unconditional (indices clamped into the head's tables) and
+    // issued before any is used, so that they are all in flight together
+    constexpr int kQPer = NQ * kD / kMThreads;       // 2 or 4
+    constexpr int kSPer = kD * kMGroups / kMThreads;  // 4
     const int tdep = depth[(size_t)h * kD + min(tid, kD - 1)];
     float qv[kQPer];
 #pragma unroll
     for (int u = 0; u < kQPer; ++u) {
-        const int e = min(tid + kGThreads * u, GP * kD - 1), g = e / kD, c = e - g * kD;
+        const int e = tid + kMThreads * u, g = e / kD, c = e - g * kD;
         qv[u] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
     }
     uint16_t sv[kSPer], zv[kSPer];
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
-        const int e = tid + kGThreads * u, c = e / kGGroups, gg = e - c * kGGroups;
+        const int e = tid + kMThreads * u, c = e / kMGroups, gg = e - c * kMGroups;
         const size_t t = ((size_t)h * kD + c) * gs.group_stride + min(gb + gg, ng - 1);
         sv[u] = gs.scale16[t];
         zv[u] = gs.zero16[t];
@@ -202,12 +216,12 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
     if (tid < kD) tc[tid] = min(tdep, kPlanes);
 #pragma unroll
     for (int u = 0; u < kQPer; ++u) {
-        const int e = tid + kGThreads * u, g = e / kD, c = e - g * kD;
-        if (e < GP * kD) qs[g][c] = g < G ? qv[u] : 0.0f;
+        const int e = tid + kMThreads * u, g = e / kD, c = e - g * kD;
+        qs[g][c] = g < G ? qv[u] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
-        const int e = tid + kGThreads * u, c = e / kGGroups, gg = e - c * kGGroups;
+        const int e = tid + kMThreads * u, c = e / kMGroups, gg = e - c * kMGroups;
         sgrp[c][gg] = __ushort_as_half(sv[u]);
         zgrp[c][gg] = __ushort_as_half(zv[u]);
     }
@@ -225,17 +239,22 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
         off[2 * lane + 1] = ex + a;
         if (lane == 63) off[kD] = inc;
     }
-    // C per (group, query): fp64 over channels ascending
-    if (tid < kGGroups * GP) {
-        const int gg = tid / GP, g = tid - gg * GP;
+    // C per (group, query) in fp64: eight adjacent threads take 16 channels each and
+    // combine their sums with three lane exchanges (rounded once to fp32)
+#pragma unroll
+    for (int pr = tid >> 3; pr < kMGroups * NQ; pr += kMThreads / 8) {
+        const int gg = pr / NQ, g = pr - gg * NQ, c0 = 16 * (tid & 7);
         double acc = 0.0;
-        for (int c = 0; c < kD; ++c) {
+#pragma unroll
+        for (int c = c0; c < c0 + 16; ++c) {
             const double zf = (double)__half2float(zgrp[c][gg]);
             const double sf = (double)__half2float(sgrp[c][gg]);
             const double hm = (double)((16 >> tc[c]) - 1) * 0.5;
             acc += (double)qs[g][c] * (zf + sf * hm);
         }
-        cg[gg][g] = (float)acc;
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        if ((tid & 7) == 0) cg[gg][g] = (float)acc;
     }
     __syncthreads();
     if (tid < kD) {
@@ -243,91 +262,174 @@ __global__ __launch_bounds__(kGThreads) void k_scan_grouped(
         for (int j = 0; j < t; ++j) pl[off[c] + j] = (uint16_t)(c * kPlanes + j);
     }
     __syncthreads();
-    const uint32_t *hp = gs.planes + (size_t)h * kMaxPlanesPerHead * gs.word_stride;
-    const int my_w = tid >> 2, my_s = tid & 3;
-    const int my_g = my_w / kGroupWords;  // group within the tile
-    float acc[8][GP];
+    const int nplanes = off[kD];
+    const int ngr8 = (nplanes + kGroupBits - 1) / kGroupBits;
+    const int nkb = max(1, (ngr8 + kKBlockGroups - 1) / kKBlockGroups);
+    const int npr = (nkb + 1) >> 1;  // K-pairs
+    const bool small = nkb < kMaxKBlocks;
+
+    const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
+    // unit exponent of each (group pos of this wave, query): the group's largest weight
+    // fl32(q sf) 8 over the channels read, from two channels a lane and a wave maximum
+    int eu[2][NQ];
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        const float c0 = cg[my_g][g];
+    for (int pos = 0; pos < 2; ++pos) {
+        const int gr = 2 * wave + pos;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m][g] = c0;
+        for (int g = 0; g < NQ; ++g) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int c = lane + 64 * cc;
+                if (tc[c] > 0) mx = fmaxf(mx, fabsf(qs[g][c] * __half2float(sgrp[c][gr])) * 8.0f);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            int e = 0;
+            frexpf(mx, &e);  // mx < 2^e
+            eu[pos][g] = mx > 0.0f ? e : 0;
+        }
     }
-    for (int c0 = 0; c0 < kD;) {
-        int c1 = c0;
-        while (c1 < kD && off[c1 + 1] - off[c0] <= kGRowsMax) ++c1;
-        const int r0 = off[c0], nr = off[c1] - r0;
-        __syncthreads();  // the previous batch's words are no longer read
-        if (nr > 0) {  // pl holds the batch's rows only when it has any (all depths 0:
-                       // no row, no load)
-            // the batch's rows, 16 bytes a load, all loads unconditional and in flight
-            // together (a slot past the batch reads its last row, one past the row the
-            // row's first 16 bytes, and is dropped)
-            constexpr int kBPer = kGRowsMax * 16 / kGThreads;  // 6
+
+    const uint32_t *hp = gs.planes + (size_t)h * kMaxPlanesPerHead * gs.word_stride;
+    v4i acc[2][8][QS];
+    for (int kp0 = 0; kp0 < npr; kp0 += 2) {  // batches of two K-pairs
+        const int p0 = 64 * kp0;
+        const int np = max(0, min(kMBatch, nplanes - p0));
+        if (kp0) __syncthreads();  // the previous batch's words are no longer read
+        if (np > 0) {  // the plane list holds the batch's rows only when it has any
+            // 16 bytes a load, all unconditional and in flight together (a slot past the
+            // batch reads its last row, one past the row the row's first 16 bytes, and
+            // is dropped); word_stride is a multiple of 4
+            constexpr int kBPer = kMBatch * (kMWords / 4) / kMThreads;  // 4
             uint4 x[kBPer];
 #pragma unroll
             for (int u = 0; u < kBPer; ++u) {
-                const int e = tid + kGThreads * u, r = e >> 4, v = e & 15;
-                const int wv = w0 + 4 * v;  // word_stride is a multiple of 4
-                const int row = pl[r0 + min(r, nr - 1)];
+                const int e = tid + kMThreads * u, r = e >> 3, v = e & 7;
+                const int wv = w0 + 4 * v;
+                const int row = pl[p0 + min(r, np - 1)];
                 x[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)row * gs.word_stride +
                                                         (wv < gs.word_stride ? wv : 0));
             }
 #pragma unroll
             for (int u = 0; u < kBPer; ++u) {
-                const int e = tid + kGThreads * u, r = e >> 4, v = e & 15;
-                if (r < nr)
+                const int e = tid + kMThreads * u, r = e >> 3, v = e & 7;
+                if (r < np)
                     *reinterpret_cast<uint4 *>(&words[r][4 * v]) =
                         w0 + 4 * v < gs.word_stride ? x[u] : make_uint4(0u, 0u, 0u, 0u);
             }
         }
         __syncthreads();
-        for (int c = c0; c < c1; ++c) {
-            const int t = tc[c];
-            if (t == 0) continue;
-            const int o = off[c] - r0;
-            const float sf = __half2float(sgrp[c][my_g]);
-            float a[GP];
 #pragma unroll
-            for (int g = 0; g < GP; ++g) a[g] = qs[g][c] * sf;
-            uint32_t b[kPlanes];
+        for (int kk = 0; kk < 2; ++kk) {
+            const int kp = kp0 + kk;
+            if (kp >= npr) break;
 #pragma unroll
-            for (int j = 0; j < kPlanes; ++j) {
-                b[j] = 0u;
-                if (j < t) b[j] = words[o + j][my_w] >> (8 * my_s);
-            }
+            for (int pos = 0; pos < 2; ++pos) {
+                const int gr = 2 * wave + pos;
+                // A operand: this lane's row is (query 4 set + (lane & 15) / 4, digit s)
+                // over planes 64 kp + 8 jq + i (i < 8) and 64 kp + 32 + 8 jq + i - 8
+                v4i A[QS];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                uint32_t P = 0;
+                for (int set = 0; set < QS; ++set) {
+                    const int g = 4 * set + ((lane & 15) >> 2);
+                    int mine[4];  // weights 4 s .. 4 s + 3 of the lane's 16, biased
 #pragma unroll
-                for (int j = 0; j < kPlanes; ++j) P |= ((b[j] >> m) & 1u) << (3 - j);
-                const float pf = (float)P;
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int i = 4 * s + ii;
+                        const int P = 64 * kp + (i < 8 ? 8 * jq + i : 32 + 8 * jq + i - 8);
+                        int M = 0;
+                        if (P < nplanes) {
+                            const int row = pl[P], c = row >> 2, j = row & 3;
+                            const float w = qs[g][c] * __half2float(sgrp[c][gr]);
+                            // w 2^(3-j) / 2^(e-30), an exact power-of-two scaling
+                            M = (int)rintf(ldexpf(w, 33 - j - eu[pos][g]));
+                        }
+                        mine[ii] = M + (int)kDigitBias;  // |M| <= 2^30: no overflow
+                    }
+                    // dword src of the operand holds weights 4 src .. 4 src + 3 (lane src
+                    // of the quad computed them): byte s of each biased weight, gathered
+                    // with byte permutes, is digit s + 128 (s < 3, flipped back to a
+                    // two's-complement byte) or the top digit (s = 3)
+                    const uint32_t sel = (uint32_t)s | ((uint32_t)(4 + s) << 8) | 0x0C0C0000u;
+                    const uint32_t flip = s < 3 ? 0x80808080u : 0u;
+                    uint32_t bytes[4];
 #pragma unroll
-                for (int g = 0; g < GP; ++g) acc[m][g] = fmaf(a[g], pf, acc[m][g]);
+                    for (int src = 0; src < 4; ++src) {
+                        uint32_t u[4];
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            if (src == 0) u[ii] = (uint32_t)__builtin_amdgcn_mov_dpp(mine[ii], 0x00, 0xF, 0xF, false);
+                            else if (src == 1) u[ii] = (uint32_t)__builtin_amdgcn_mov_dpp(mine[ii], 0x55, 0xF, 0xF, false);
+                            else if (src == 2) u[ii] = (uint32_t)__builtin_amdgcn_mov_dpp(mine[ii], 0xAA, 0xF, 0xF, false);
+                            else u[ii] = (uint32_t)__builtin_amdgcn_mov_dpp(mine[ii], 0xFF, 0xF, 0xF, false);
+                        }
+                        const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], sel);
+                        const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], sel);
+                        bytes[src] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ flip;
+                    }
+                    A[set] = v4i{(int)bytes[0], (int)bytes[1], (int)bytes[2], (int)bytes[3]};
+                }
+                // B operand: planes s, s+4 of plane groups jq, jq+4 at word 8v + 4 pos + wq
+                uint32_t x[2][2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp)
+                        x[hh][pp] = quad_byte_transpose(
+                            words[64 * kk + 8 * (jq + 4 * hh) + s + 4 * pp][8 * wave + 4 * pos + wq],
+                            s);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const uint32_t mask = 0x01010101u << m;
+                    const v4i b = {(int)(x[0][0] & mask), (int)(x[0][1] & mask),
+                                   (int)(x[1][0] & mask), (int)(x[1][1] & mask)};
+#pragma unroll
+                    for (int set = 0; set < QS; ++set) {
+                        const v4i c0 = kp == 0 ? v4i{0, 0, 0, 0} : acc[pos][m][set];
+                        acc[pos][m][set] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[set], b, c0, 0, 0, 0);
+                    }
+                }
             }
         }
-        c0 = c1;
     }
-    const int tok = (w0 + my_w) * 32 + 8 * my_s;
-    if (w0 + my_w < W) {
+    // scores: lane 16 j + 4 w + s holds query j's digit sums of byte s of word
+    // 8v + 4 pos + w, bit m
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            if (g >= G) break;
+    for (int pos = 0; pos < 2; ++pos) {
+        const int gr = 2 * wave + pos;
+        const int word = w0 + 8 * wave + 4 * pos + wq;
+        if (word >= W) continue;
+        const int tok = 32 * word + 8 * s;
+#pragma unroll
+        for (int set = 0; set < QS; ++set) {
+            const int g = 4 * set + jq;
+            if (g >= G) continue;
+            const float C = cg[gr][g];
+            const float S = ldexpf(1.0f, eu[pos][g] - 30);
+            float v[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) v[m] = combined_score<QS>(acc[pos][m][set], m, C, S, small);
             float *row = scores + ((size_t)h * G + g) * n;
+            if ((n & 3) == 0 && tok + 8 <= n) {
+                *reinterpret_cast<float4 *>(row + tok) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(row + tok + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
-                if (tok + m < n) row[tok + m] = acc[m][g];
+                for (int m = 0; m < 8; ++m)
+                    if (tok + m < n) row[tok + m] = v[m];
+            }
         }
     }
 }
 
-template <int GP>
-void launch_scan_gp(const fathom_gstore &gs, const float *q, const uint8_t *depth, int G,
-                    float *scores, hipStream_t s) {
+template <int QS>
+void launch_scan_mma(const fathom_gstore &gs, const float *q, const uint8_t *depth, int G,
+                     float *scores, hipStream_t s) {
     const int W = (gs.n_tokens + 31) >> 5;
-    const int tiles = (W + kGWords - 1) / kGWords;
-    hipLaunchKernelGGL(k_scan_grouped<GP>, dim3(gs.n_heads * tiles), dim3(kGThreads), 0, s, gs,
-                       q, depth, G, scores, tiles);
+    const int tiles = (W + kMWords - 1) / kMWords;
+    hipLaunchKernelGGL(k_scan_grouped_mma<QS>, dim3(gs.n_heads * tiles), dim3(kMThreads), 0, s,
+                       gs, q, depth, G, scores, tiles);
 }
 
 }  // namespace
@@ -342,10 +444,8 @@ hipError_t launch_quantize_groups(const float *keys, int64_t head_stride,
 
 hipError_t launch_scan_grouped(const fathom_gstore &gs, const float *q, const uint8_t *depth,
                                int G, float *scores, hipStream_t s) {
-    if (G <= 1) launch_scan_gp<1>(gs, q, depth, G, scores, s);
-    else if (G <= 2) launch_scan_gp<2>(gs, q, depth, G, scores, s);
-    else if (G <= 4) launch_scan_gp<4>(gs, q, depth, G, scores, s);
-    else launch_scan_gp<8>(gs, q, depth, G, scores, s);
+    if (query_sets(G) == 1) launch_scan_mma<1>(gs, q, depth, G, scores, s);
+    else launch_scan_mma<2>(gs, q, depth, G, scores, s);
     return hipGetLastError();
 }
 
