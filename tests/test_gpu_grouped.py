@@ -77,7 +77,8 @@ def test_grouped_requantize_an_earlier_group():
 
 @pytest.mark.parametrize("H,G,n,kind", [(2, 4, 3000, "plan92"), (1, 1, 4096, "b512"),
                                         (2, 8, 777, "random"), (1, 3, 33, "plan92"),
-                                        (1, 4, 9000, "b0")])
+                                        (1, 4, 9000, "b0"), (2, 6, 5000, "plan92"),
+                                        (1, 8, 4100, "b512")])
 def test_grouped_plan_and_scan_match_oracle(H, G, n, kind):
     torch = torch_cuda()
     print(f"[grouped scan] H={H} G={G} n={n} {kind}", flush=True)
