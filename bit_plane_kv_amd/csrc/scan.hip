@@ -13,11 +13,12 @@
 // plane-by-query weight matrix, so it runs on the matrix cores in int8: each weight
 // becomes an integer count of a per-query unit S_g = 2^(e_g - 30) (e_g: the binary
 // exponent just above the largest |w_gP| of the head, so the error is at most 2^-31 of
-// the largest weight), written as 4 signed base-256 digits.  One 16x16x32 i8 MFMA takes
-// 16 rows = 4 queries x 4 digits, K = 32 planes (4 groups of 8) and 16 columns = 16
+// the largest weight), written as 4 signed base-256 digits.  One 16x16x64 i8 MFMA takes
+// 16 rows = 4 queries x 4 digits, K = 64 planes (8 groups of 8) and 16 columns = 16
 // tokens whose plane bits are bytes; the int32 sums are exact, and one fp32 combine per
-// score gives C_g + S_g * sum_d 256^d D_d.  Per 8 tokens and 8 planes a lane spends two
-// byte transposes across its quad and two masks per token; no table lookups.
+// score gives C_g + S_g * sum_d 256^d D_d.  For each 16-column block a lane turns words of
+// 16 planes into its operand with four byte transposes across its quad and one mask per
+// 4 bytes for each of the 8 token bits; no table lookups.
 #include <algorithm>
 #include <mutex>
 

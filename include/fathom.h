@@ -239,9 +239,10 @@ int fathom_plan_grouped(const fathom_gstore *gs, const float *q, int G, int B,
  * each channel read to its depth, reconstructed at the bin midpoint with its token's
  * group scale and zero:  score_g(i) = C_gG + sum_c fl32(q_gc sf_cG) * P_c(i), P the
  * t-plane prefix times 2^(4-t), C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64 rounded
- * once, the channel sum in fp32 ascending.  Bits are extracted on the vector units (the
- * matrix-core scan needs weights shared by 16 consecutive token columns, which straddle
- * groups).  q [H][G][d] fp32, depth [H][d], scores [H][G][n] fp32 out.
+ * once.  The sum over the planes runs on the int8 matrix cores as in fathom_scan, with
+ * each weight an integer count of a power-of-two unit of its (query, group), so scores
+ * are within a few fp32 ulps of that sum (1e-5 of the row's largest score).
+ * q [H][G][d] fp32, depth [H][d], scores [H][G][n] fp32 out.
  */
 int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const uint8_t *depth,
                         float *scores, void *stream);
