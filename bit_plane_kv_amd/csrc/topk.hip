@@ -545,10 +545,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
             const int e = tid + kSelThreads * u;
             v[u] = e < (int)C ? crow[skey[e]] : 0.0f;
         }
+        // the keys' minimum and maximum on the way (for the radix start below)
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = tid + kSelThreads * u;
-            if (e < (int)C) skey[e] = order_key(v[u]);
+            if (e < (int)C) {
+                const uint32_t key = order_key(v[u]);
+                skey[e] = key;
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+        }
+        if ((tid & 63) == 0) {
+            smm[0][tid >> 6] = kmin;
+            smm[1][tid >> 6] = kmax;
         }
     }
     __syncthreads();
@@ -563,24 +579,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     // radix select starts below the bits all of them share (from their min and max), so
     // that its first histogram spreads them over many bins instead of a few contended
     // ones.  Digits of up to 11 bits.
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = tid; i < (int)C; i += kSelThreads) {
-        const uint32_t key = skey[i];
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    }
-    if ((tid & 63) == 0) {
-        smm[0][tid >> 6] = kmin;
-        smm[1][tid >> 6] = kmax;
-    }
-    __syncthreads();
-    kmin = min(min(smm[0][0], smm[0][1]), min(smm[0][2], smm[0][3]));
-    kmax = max(max(smm[1][0], smm[1][1]), max(smm[1][2], smm[1][3]));
+    const uint32_t kmin = min(min(smm[0][0], smm[0][1]), min(smm[0][2], smm[0][3]));
+    const uint32_t kmax = max(max(smm[1][0], smm[1][1]), max(smm[1][2], smm[1][3]));
     const uint32_t diff = kmin ^ kmax;
     int shift = diff == 0u ? 0 : 32 - __clz(diff);  // bits >= shift: the same in every key
     uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift), need = (uint32_t)kr;
