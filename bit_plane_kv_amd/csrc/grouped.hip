@@ -177,10 +177,10 @@ constexpr int kMRowPad = kMWords + 4;              // 16-byte aligned LDS rows
 
 // Four waves per SIMD for one query set (117 registers, no spills: each tile's chain of
 // loads and barriers is hidden by more resident tiles; five spill to scratch and run
-// slower).
+// slower), two for two sets (198 registers; three spill).
 template <int QS>
 __global__ __launch_bounds__(kMThreads)
-__attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 1))) void k_scan_grouped_mma(
+__attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
     fathom_gstore gs, const float *__restrict__ q, const uint8_t *__restrict__ depth, int G,
     float *__restrict__ scores, int tiles_per_head) {
     constexpr int NQ = 4 * QS;
