@@ -673,7 +673,7 @@ def host_model(args, name, L):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     t0 = time.time()
-    Wst = ((n + 31) // 32 + 3) // 4 * 4
+    Wst = int(F.lib().fathom_word_stride(n))  # the library's row stride for n tokens
     planes_h = torch.empty((H, 128, 4, Wst), dtype=torch.int32, pin_memory=True)
     kw = dict(dtype=torch.float32, device=dev)
     st_h = F.Store(planes_h, torch.empty((H, 128), **kw), torch.empty((H, 128), **kw),

@@ -101,6 +101,14 @@ extern "C" {
 
 int fathom_version(void) { return FATHOM_VERSION; }
 
+int32_t fathom_word_stride(int32_t n_tokens) {
+    constexpr int64_t kPageWords = 1024;  // 4 KiB
+    const int64_t W = ((int64_t)std::max<int32_t>(n_tokens, 1) + 31) / 32;
+    if (W < 16 * kPageWords) return (int32_t)((W + 3) / 4 * 4);
+    const int64_t pages = ((W + kPageWords - 1) / kPageWords) | 1;  // odd
+    return (int32_t)(pages * kPageWords);
+}
+
 int fathom_last_hip_error(void) { return g_last_hip; }
 
 const char *fathom_status_string(int status) {

@@ -55,6 +55,7 @@ _I = ctypes.c_int
 _SZ = ctypes.c_size_t
 _SIGS = {
     "fathom_version": (_I, []),
+    "fathom_word_stride": (_I, [_I]),
     "fathom_last_hip_error": (_I, []),
     "fathom_status_string": (ctypes.c_char_p, [_I]),
     "fathom_workspace_size": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)]),
@@ -172,7 +173,7 @@ class Store:
     def empty(H: int, n: int, device, word_stride: int | None = None, planes=None) -> "Store":
         """Allocate the store's buffers; `planes` may be supplied (e.g. pinned host)."""
         import torch
-        W = ((n + 31) // 32 + 3) // 4 * 4 if word_stride is None else word_stride
+        W = int(lib().fathom_word_stride(int(n))) if word_stride is None else word_stride
         if planes is None:
             planes = torch.empty((H, D, PLANES, W), dtype=torch.int32, device=device)
         kw = dict(dtype=torch.float32, device=device)
@@ -215,7 +216,8 @@ class GStore:
         import torch
         ng = (n_max + GROUP - 1) // GROUP
         i32 = dict(dtype=torch.int32, device=device)
-        return GStore(torch.zeros((H, D, PLANES, 4 * ng), **i32),
+        ws = int(lib().fathom_word_stride(GROUP * ng))  # >= 4 ng words, whole groups
+        return GStore(torch.zeros((H, D, PLANES, ws), **i32),
                       torch.zeros((H, D, ng), dtype=torch.int16, device=device),
                       torch.zeros((H, D, ng), dtype=torch.int16, device=device),
                       torch.zeros((H, D, ng, 2), **i32),

@@ -136,6 +136,19 @@ int fathom_last_hip_error(void);
 int fathom_version(void);
 
 /*
+ * A plane-row stride (uint32 words) for a store of n_tokens tokens, for callers that
+ * allocate one (either store): ceil(n/32) rounded up to a multiple of 4; once a row is
+ * 16 pages of 4 KiB or more (n >= 524288), whole 4 KiB pages, an odd number of them.
+ * Host-resident scans read a few hundred bytes of each planned row at a time, and with the
+ * index in pinned host memory (blog, "Where the memory lives changes the answer": there
+ * bytes are time) rows a large power of two apart read slower over the link: at n = 1M
+ * (32-page rows) a plan reading one plane of each of 92 channels ran at 75% of the link
+ * rate, at 94% with 33-page rows; strides that leave rows unaligned to pages were slower
+ * still.  Returns 4 for n < 1 (no error is reported).
+ */
+int32_t fathom_word_stride(int32_t n_tokens);
+
+/*
  * Build the store from fp32 keys (blog, "How to read fewer bits per key": 4-bit
  * storage; "Bit planes": the plane layout; Glonce: 4-bit per-channel K cache).
  *   keys [H][n][d] fp32, device-visible, finite.

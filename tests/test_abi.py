@@ -31,6 +31,27 @@ def test_every_declared_call_is_exported():
     assert sorted(F.EXPORTS) == names
 
 
+def test_word_stride():
+    """Rows of at least 16 pages of 4 KiB become an odd number of whole pages; shorter
+    rows only round up to 4 words."""
+    L = F.lib()
+    assert L.fathom_word_stride(1) == 4
+    assert L.fathom_word_stride(100) == 4
+    assert L.fathom_word_stride(4096) == 128
+    assert L.fathom_word_stride(32768) == 1024
+    assert L.fathom_word_stride(262144) == 8192
+    assert L.fathom_word_stride(524256) == 16384          # 16383 words: below 16 pages
+    assert L.fathom_word_stride(524287) == 17 * 1024      # 16384 words: 16 pages -> 17
+    assert L.fathom_word_stride(524288) == 17 * 1024
+    assert L.fathom_word_stride(1 << 20) == 33 * 1024     # 32 pages -> 33
+    assert L.fathom_word_stride((1 << 20) + 1) == 33 * 1024
+    for n in [1, 33, 777, 32769, 600000, 1 << 20, 3000000]:
+        ws = L.fathom_word_stride(n)
+        assert ws >= (n + 31) // 32 and ws % 4 == 0
+        if ws >= 16 * 1024:
+            assert ws % 1024 == 0 and (ws // 1024) % 2 == 1
+
+
 def test_version_and_status_strings():
     L = F.lib()
     assert L.fathom_version() == 100
