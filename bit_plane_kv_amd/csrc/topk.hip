@@ -165,9 +165,12 @@ __device__ __forceinline__ uint32_t load_kept(const float *row_cand, const uint3
 // Hs = sum bit * (d2 + 256 d3) over the head's planes (d the weight's base-256 digits),
 // f = fl(fl(Hs) 65536 + fl(L)), and with m the token's bit within its byte the scan's
 // final step fl(f 2^m * fl(S 2^-m) + C) (-128 in place of 2^7).  tab: 3*512 words of LDS.
-// Kept out of line: it runs only for rows whose threshold guess failed, and inlined it
-// makes the compiler duplicate the select around it.
-__device__ __noinline__ void rescore_word(const FilterArgs &fa, int h, int g, int word,
+// It runs only for rows whose threshold guess failed.  Inlined into the final select
+// (rows of one chunk), which then needs no scratch memory: a kernel that uses scratch
+// cost ~3 us more a launch in the decode step, even with an empty redo list.  Called out
+// of line from the candidate level, where inlined it makes the compiler duplicate the
+// select around it and spill.
+__device__ __forceinline__ void rescore_word(const FilterArgs &fa, int h, int g, int word,
                                              uint32_t lenmask, uint32_t *tab,
                                              uint32_t (&key)[kEPT]) {
     const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
@@ -224,6 +227,12 @@ __device__ __noinline__ void rescore_word(const FilterArgs &fa, int h, int g, in
     __syncthreads();  // the tables are no longer read
 }
 
+__device__ __noinline__ void rescore_word_call(const FilterArgs &fa, int h, int g, int word,
+                                               uint32_t lenmask, uint32_t *tab,
+                                               uint32_t (&key)[kEPT]) {
+    rescore_word(fa, h, g, word, lenmask, tab, key);
+}
+
 
 // kExplicit: input entries carry their own int32 index (candidate levels); otherwise
 // the index is the position in the row.  kCandOut: write (value, index) candidates
@@ -256,7 +265,10 @@ __device__ __forceinline__ void select_chunk(
             reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
         const int word = chunk * kThreads + tid;
         if (meta->cnt[g] < (uint32_t)k) {
-            rescore_word(fa, h, g, word, vmask, hist, key);
+            if constexpr (kCandOut)
+                rescore_word_call(fa, h, g, word, vmask, hist, key);
+            else
+                rescore_word(fa, h, g, word, vmask, hist, key);
         } else {
             vmask = load_kept(vals + row * in_stride, fa.masks + row * fa.W, word, fa.W, vmask,
                               key);
@@ -417,8 +429,9 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
 // count is the head-0 meta block's redo field), a grid-stride loop over the list: a
 // small grid, as the list is usually empty.
 constexpr int kRedoGrid = 16;
+// The final select (!kCandOut) may use 128 VGPRs, so that it needs no scratch.
 template <bool kCandOut>
-__global__ __launch_bounds__(kThreads, 8) void k_topk_redo(
+__global__ __launch_bounds__(kThreads, kCandOut ? 8 : 1) void k_topk_redo(
     const float *__restrict__ vals, int64_t row_len, int k, float *__restrict__ out_val,
     int32_t *__restrict__ out_idx, int64_t out_stride, FilterArgs fa,
     const uint32_t *__restrict__ list, int nch) {
