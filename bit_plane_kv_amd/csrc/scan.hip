@@ -798,14 +798,23 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         if (++ppr == (k ? npr1 : npr0)) {
             const int hh = k ? h1 : h0;
             const int wi = ((k ? pss - h1rel : ss0 + pss) * kWaves + wave) * 8 + 2 * wq;
+            // the head's constants, picked element by element: choosing between the two
+            // arrays as a whole made them addressable, i.e. scratch memory
+            float Ck[QS], Sk[QS], Tk[QS];
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {
+                Ck[set] = k ? C1[set] : C0[set];
+                Sk[set] = k ? S1[set] : S0[set];
+                Tk[set] = k ? T1[set] : T0[set];
+            }
             if constexpr (kFilter) {
                 ScanMeta *mh = reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) +
                                                             (size_t)hh * kMetaBytes);
-                combine_filter<QS>(acc, k ? C1 : C0, k ? S1 : S0, k ? T1 : T0, small, G, jq,
-                                   s, wq, lane, wi, n, scores + (size_t)hh * G * n,
+                combine_filter<QS>(acc, Ck, Sk, Tk, small, G, jq, s, wq, lane, wi, n,
+                                   scores + (size_t)hh * G * n,
                                    masks + (size_t)hh * G * ((n + 31) >> 5), mh->cnt);
             } else {
-                combine_store<QS>(acc, k ? C1 : C0, k ? S1 : S0, small, G, jq, s, wi, n,
+                combine_store<QS>(acc, Ck, Sk, small, G, jq, s, wi, n,
                                   scores + (size_t)hh * G * n);
             }
             ppr = 0;
