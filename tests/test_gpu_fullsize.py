@@ -1,4 +1,4 @@
-"""The decode step at the benchmark's full size, launched as the benchmark launches it.
+"""The decode step at the benchmark's full sizes, launched as the benchmark launches it.
 
 288 (layer, KV head) pairs x 32768 tokens, G = 4 queries per KV head, B = 92, k = 512
 (a Qwen3-8B-shaped cache), one fathom_step on the filtering path with its workspace and
@@ -8,7 +8,11 @@ neighbours) are checked one by one: plan bit-exact; the step's winners equal to 
 exact top-k of the full-score scan's fp32 scores (the same arithmetic, computed on its
 own path); those scores within the fp32 bar of the oracle's fp64 scores; the winners
 within the end-to-end bar of the oracle's own top-k; and the attention output within the
-bf16 bar of the oracle's attention over the step's winners.
+bf16 bar of the oracle's attention over the step's winners.  The one-layer step at a
+million tokens (8 KV heads x 1048576 tokens, rows of 32 top-k chunks: the candidate
+level, its redo and the final level) is checked the same way, with the store and the
+rows in HBM (the same kernels read pinned host memory in the benchmark's host-resident
+line; residency itself is tested at small sizes in test_gpu_parity.py).
 """
 import numpy as np
 import pytest
@@ -23,14 +27,15 @@ from gpu_util import ATTN_ABS_TOL, SCORE_REL_TOL, bf16_to_f32, check_rows, to_de
 pytestmark = pytest.mark.gpu
 
 SEED = 11
-SAMPLED = [0, 1, 143, 144, 286, 287]
 
 
-def test_step_full_size_sampled_heads():
+@pytest.mark.parametrize("name,sampled", [("qwen3_8b_32k_hbm", [0, 1, 143, 144, 286, 287]),
+                                          ("qwen3_8b_1m_layer_step", [0, 7])])
+def test_step_full_size_sampled_heads(name, sampled):
     torch = torch_cuda()
-    cfg = synth.CONFIGS["qwen3_8b_32k_hbm"]
+    cfg = synth.CONFIGS[name]
     H, G, n, B, k = cfg.H, cfg.G, cfg.n, cfg.budgets[0], cfg.k
-    print(f"[step full size] H={H} G={G} n={n} B={B} k={k} seed={SEED}", flush=True)
+    print(f"[step full size] {name} H={H} G={G} n={n} B={B} k={k} seed={SEED}", flush=True)
     st = F.Store.empty(H, n, "cuda")
     K = torch.empty((H, n, 128), dtype=torch.bfloat16, device="cuda")
     qws = torch.empty(F.workspace_size(F.OP_QUANTIZE, 32, 1, n, 1), dtype=torch.uint8,
@@ -54,8 +59,10 @@ def test_step_full_size_sampled_heads():
     full = F.fathom_scan(st, q_t, depth)
     torch.cuda.synchronize()
     depth_np, idx_np, full_np = depth.cpu().numpy(), idx.cpu().numpy(), full.cpu().numpy()
+    del qws
     out_np = bf16_to_f32(out)
-    for h in SAMPLED:
+    del full
+    for h in sampled:
         print(f"[step full size] head {h}", flush=True)
         kh = synth.keys_torch(SEED, cfg.cfg_id, [h], n, "cuda")
         s, z, codes = oracle.quantize(kh.cpu().numpy())
