@@ -223,8 +223,8 @@ int fathom_scan_extract(const fathom_store *st, const float *q, int G, const uin
 /*
  * Build and decode-time append of the grouped store (the 68-byte index the pages count,
  * read as fp16 scale and zero per 128-token group; blog, "Bit planes" for the layout):
- * (re)quantize groups g0 .. g1-1 of
- * every head from keys, then recompute var from all groups' sums.
+ * (re)quantize groups g0 .. g1-1 of every head from keys, then recompute var from all
+ * groups' sums.
  *   keys: fp32, head h's tokens 128*g0 .. min(n, 128*g1) - 1 at keys + h*keys_head_stride,
  *         d floats per token (keys 16-byte aligned; keys_head_stride in floats, a
  *         multiple of 4, >= (min(n,128*g1) - 128*g0)*d).
