@@ -74,6 +74,8 @@ def _load():
         "oracle_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
         "oracle_f32_to_bf16_array": (None, [P, ctypes.c_size_t, P]),
         "oracle_threads": (I, []),
+        "oracle_topk_f64_batch": (I, [P, I, I, I, P]),
+        "oracle_logits_batch": (None, [P, P, I, I, I, I, D, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -307,6 +309,33 @@ def topk(scores_rows, k: int):
     if rc != 0:
         raise ValueError(f"oracle top-k rejected k={k} for n={n}")
     return idx[0] if squeeze else idx
+
+
+def topk_f64(scores_rows, k: int):
+    """fp64 scores [R][n] -> int32 idx [R][k], ascending by index (same order rule as
+    topk: larger first, equal values to the lower index, -0 as +0)."""
+    s = _c(scores_rows, np.float64)
+    squeeze = s.ndim == 1
+    if squeeze:
+        s = s[None]
+    R, n = s.shape
+    idx = np.empty((R, k), np.int32)
+    rc = _load().oracle_topk_f64_batch(_p(s), R, n, int(k), _p(idx))
+    if rc != 0:
+        raise ValueError(f"oracle top-k rejected k={k} for n={n}")
+    return idx[0] if squeeze else idx
+
+
+def logits(q, K, sm_scale: float):
+    """q fp32 [H][G][d]; K bf16 bits (uint16) [H][n][d] -> fp64 logits [H][G][n] of
+    every token (the attention's first step over all n rows)."""
+    qq = _c(q, np.float32)
+    KK = _c(K, np.uint16)
+    H, G, d = qq.shape
+    n = KK.shape[1]
+    out = np.empty((H, G, n), np.float64)
+    _load().oracle_logits_batch(_p(qq), _p(KK), H, G, n, d, float(sm_scale), _p(out))
+    return out
 
 
 def attention(q, K, V, idx, sm_scale: float):

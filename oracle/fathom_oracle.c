@@ -436,6 +436,37 @@ int oracle_topk(const float *scores, int n, int k, int32_t *idx)
     return 0;
 }
 
+/* The same order over fp64 values (the exact attention logits of every token, whose */
+/* k largest are the exact top-k the approximate scan is measured against).          */
+typedef struct {
+    double s;
+    int32_t i;
+} oracle_entry64;
+
+static int oracle_entry64_cmp(const void *a, const void *b)
+{
+    const oracle_entry64 *x = (const oracle_entry64 *)a, *y = (const oracle_entry64 *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->i < y->i) ? -1 : (x->i > y->i);
+}
+
+int oracle_topk_f64(const double *scores, int n, int k, int32_t *idx)
+{
+    if (k < 1 || k > n) return -1;
+    oracle_entry64 *e = (oracle_entry64 *)malloc(sizeof(oracle_entry64) * (size_t)n);
+    if (!e) return -2;
+    for (int i = 0; i < n; ++i) {
+        e[i].s = scores[i] == 0.0 ? 0.0 : scores[i]; /* -0 ranks as +0 */
+        e[i].i = i;
+    }
+    qsort(e, (size_t)n, sizeof(oracle_entry64), oracle_entry64_cmp);
+    for (int r = 0; r < k; ++r) idx[r] = e[r].i;
+    free(e);
+    qsort(idx, (size_t)k, sizeof(int32_t), oracle_int_cmp);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------ */
 /* bf16 <-> fp32.  A bf16 value is the upper 16 bits of an fp32 value; the widening  */
 /* is exact.  The narrowing rounds to nearest, ties to even (NaN kept quiet).        */
@@ -498,6 +529,20 @@ void oracle_attention(const float *q, const uint16_t *K, const uint16_t *V, int 
         for (int c = 0; c < d; ++c) out[c] += p * (double)oracle_bf16_to_f32(row[c]);
     }
     free(l);
+}
+
+/* Exact attention logits of every one of the n rows (the first step of the         */
+/* attention above, over all tokens):  l_i = sm_scale * sum_c q_c * K[i][c]  (fp64). */
+void oracle_logits(const float *q, const uint16_t *K, int n, int d, double sm_scale,
+                   double *out)
+{
+    for (int i = 0; i < n; ++i) {
+        const uint16_t *row = K + (size_t)i * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += (double)q[c] * (double)oracle_bf16_to_f32(row[c]);
+        out[i] = dot * sm_scale;
+    }
 }
 
 /* ============================================================================== */
@@ -615,4 +660,24 @@ void oracle_attention_batch(const float *q, const uint16_t *K, const uint16_t *V
                              V + (size_t)h * n * d, d,
                              idx + ((size_t)h * G + g) * k, k, sm_scale,
                              out + ((size_t)h * G + g) * d);
+}
+
+int oracle_topk_f64_batch(const double *scores, int R, int n, int k, int32_t *idx)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < R; ++r)
+        bad |= oracle_topk_f64(scores + (size_t)r * n, n, k, idx + (size_t)r * k) != 0;
+    return bad ? -1 : 0;
+}
+
+/* q [H][G][d]; K [H][n][d]; out [H][G][n]. */
+void oracle_logits_batch(const float *q, const uint16_t *K, int H, int G, int n, int d,
+                         double sm_scale, double *out)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h)
+        for (int g = 0; g < G; ++g)
+            oracle_logits(q + ((size_t)h * G + g) * d, K + (size_t)h * n * d, n, d,
+                          sm_scale, out + ((size_t)h * G + g) * n);
 }

@@ -95,3 +95,49 @@ def test_batched_scores_equal_per_head():
     for h in range(2):
         one = oracle.scores(codes[h], s[h], z[h], depth[h], q[h])
         assert (one == got[h]).all()
+
+
+# ---- the dequantized keys z + s*code (the 4-bit values every plane prefix refines) ----
+
+def test_dequantize_elementwise_definition():
+    """Arbitrary codes, scales and offsets (negative offsets included): every element is
+    z_c + s_c * code in fp64."""
+    rng = np.random.default_rng(11)
+    n, d = 257, 128
+    codes = rng.integers(0, 16, (n, d)).astype(np.uint8)
+    s = (rng.uniform(0.01, 3.0, d) * rng.choice([1, 1, 0], d)).astype(np.float32)
+    z = rng.uniform(-20, 20, d).astype(np.float32)
+    got = oracle.dequantize(codes, s, z)
+    for i in (0, 1, 100, n - 1):
+        for c in (0, 5, 77, d - 1):
+            assert got[i, c] == float(z[c]) + float(s[c]) * int(codes[i, c])
+    ref = z.astype(np.float64)[None, :] + s.astype(np.float64)[None, :] * codes
+    assert (got == ref).all()
+
+
+def test_dequantize_within_half_a_step_of_the_keys():
+    """A 4-bit min/max quantizer reconstructs every key to within half a step, the
+    channel's minimum exactly and its maximum to rounding (independent of the
+    formula: a dropped offset or a wrong scale breaks it on shifted channels)."""
+    x = synth.keys_np(3, 7, [0], 999, 128)[0]
+    x = x + np.linspace(-40, 40, 128, dtype=np.float32)[None, :]   # channels off zero
+    s, z, codes = oracle.quantize(x)
+    deq = oracle.dequantize(codes, s, z)
+    step = s.astype(np.float64)[None, :]
+    err = np.abs(deq - x.astype(np.float64))
+    assert (err <= 0.5 * step * (1 + 1e-5) + 1e-6 * np.abs(x)).all()
+    lo = x.argmin(axis=0)
+    hi = x.argmax(axis=0)
+    cols = np.arange(128)
+    assert (deq[lo, cols] == x[lo, cols].astype(np.float64)).all()
+    assert np.allclose(deq[hi, cols], x[hi, cols], rtol=1e-5, atol=0)
+
+
+def test_full_depth_scores_are_query_times_dequantized_keys():
+    """At depth 4 on every channel the scan's definition reduces to q . dequantize."""
+    x, q, s, z, codes = _head(n=300, G=2)
+    x2 = x + np.float32(5.0)                     # a nonzero offset on every channel
+    s, z, codes = oracle.quantize(x2)
+    got = oracle.scores(codes, s, z, np.full(128, 4, np.uint8), q)
+    ref = q.astype(np.float64) @ oracle.dequantize(codes, s, z).T
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())

@@ -121,3 +121,50 @@ def test_attention_ignores_index_order():
     a = oracle.attention(q, K, V, np.sort(idx)[None, None], 0.09)
     b = oracle.attention(q, K, V, idx[None, None], 0.09)
     assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+def _lexsort_topk64(s, k):
+    s = np.where(s == 0, 0.0, s)
+    order = np.lexsort((np.arange(s.size), -s))
+    return np.sort(order[:k])
+
+
+@settings(max_examples=30, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1), n=st.integers(1, 2000), frac=st.floats(0, 1),
+       levels=st.sampled_from([0, 3, 50]))
+def test_topk_f64_equals_full_sort(seed, n, frac, levels):
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal(n)
+    if levels:
+        s = np.round(s * levels)
+    # values that differ below fp32 resolution must still be told apart
+    s = s + rng.integers(0, 3, n) * 1e-12
+    k = max(1, min(n, int(round(frac * n))))
+    assert (oracle.topk_f64(s, k) == _lexsort_topk64(s, k)).all()
+
+
+def test_topk_f64_signed_zero_and_fine_differences():
+    s = np.array([-0.0, 0.0, 1.0, 1.0 + 1e-15, 1.0, -1e-300], np.float64)
+    assert oracle.topk_f64(s, 1).tolist() == [3]
+    assert oracle.topk_f64(s, 3).tolist() == [2, 3, 4]
+    assert oracle.topk_f64(s, 4).tolist() == [0, 2, 3, 4]     # -0 ties +0: lower index
+
+
+def test_logits_equal_a_library_matmul():
+    n, d, G = 777, 128, 3
+    K = synth.values_np(8, 6, [0, 1], n, d)
+    q = synth.queries_np(9, 6, [0, 1], G, d)
+    sm = 0.0883883461356163
+    got = oracle.logits(q, K, sm)
+    Kf = oracle.bf16_to_f32(K).astype(np.float64)
+    for h in range(2):
+        ref = (q[h].astype(np.float64) @ Kf[h].T) * sm
+        assert np.allclose(got[h], ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    # the attention over every row is the softmax of these logits applied to V
+    V = synth.values_np(10, 6, [0, 1], n, d)
+    idx = np.tile(np.arange(n, dtype=np.int32), (2, G, 1))
+    att = oracle.attention(q, K, V, idx, sm)
+    p = np.exp(got - got.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    ref = np.einsum("hgn,hnd->hgd", p, oracle.bf16_to_f32(V).astype(np.float64))
+    assert np.allclose(att, ref, rtol=1e-10, atol=1e-12)
