@@ -532,16 +532,68 @@ def grouped_lines(args, kern):
 ACC_BUDGETS = (16, 24, 32, 40, 48, 56, 64, 72, 80, 92, 104, 120, 136, 168, 200, 256, 512)
 
 
+def attention_references(q, K, V, k, sm):
+    """The accuracy sweep's two references, head by head on the GPU in fp64: dense
+    softmax attention over all n tokens (logits q . K_i * sm on the bf16 rows, maximum
+    subtracted), and the exact top-k -- the k largest fp64 logits, equal logits to the
+    lower token index, ascending by index.  tests/test_gpu_accuracy.py checks both
+    against the oracle's attention over every row and its fp64 top-k of its logits.
+    Returns (dense fp64 [H][G][128], top int32 [H][G][k])."""
+    import torch
+    H, G = q.shape[0], q.shape[1]
+    dense = torch.empty((H, G, 128), dtype=torch.float64, device=q.device)
+    top = torch.empty((H, G, k), dtype=torch.int32, device=q.device)
+    for h in range(H):
+        Kd = K[h].to(torch.float64)                       # exact widening of bf16
+        logits = torch.matmul(q[h].to(torch.float64), Kd.t().contiguous()) * sm
+        # exp and the normalisation written out: torch's fp64 softmax on this ROCm
+        # build agrees with the oracle only to ~2e-8 (an fp32-accurate exponential)
+        e = torch.exp(logits - logits.max(dim=-1, keepdim=True).values)
+        p = e / e.sum(dim=-1, keepdim=True)
+        dense[h] = torch.matmul(p, V[h].to(torch.float64))
+        # stable sort: among equal logits the lower index comes first
+        order = torch.sort(logits, dim=-1, descending=True, stable=True).indices[:, :k]
+        top[h] = order.sort(dim=-1).values.to(torch.int32)
+        del Kd, logits, e, p, order
+    return dense, top
+
+
+def accuracy_rows(F, st, q, K, V, k, sm, fixed, budgets, dense, top):
+    """Attention error of the per-query plan at each budget (through fathom_step), of
+    the fixed-depth comparator plan `fixed` and of the exact top-k, against `dense`."""
+    import torch
+    H, G = q.shape[0], q.shape[1]
+    dn = dense.norm(dim=-1)
+
+    def err(out):
+        e = (out.to(torch.float64) - dense).norm(dim=-1) / dn
+        return {"mean": round(float(e.mean()), 5), "max": round(float(e.max()), 5)}
+
+    r = {"fathom": {}}
+    out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=q.device)
+    for B in budgets:
+        F.fathom_step(st, q, K, V, B, k, sm, out=out)
+        r["fathom"][str(B)] = err(out)
+    idx = F.fathom_topk(F.fathom_scan(st, q, fixed), k)
+    r["fixed136"] = err(F.fathom_sparse_attn(q, K, V, idx, sm))
+    r["exact_topk"] = err(F.fathom_sparse_attn(q, K, V, top, sm))
+    match = [B for B in budgets if r["fathom"][str(B)]["mean"] <= r["fixed136"]["mean"]]
+    r["bits_to_match_fixed136"] = match[0] if match else None
+    r["bytes_ratio_vs_fixed136"] = round(136 / match[0], 2) if match else None
+    return r
+
+
 def accuracy_sweep(args):
     """Attention error against budget on a synthetic cache (blog, "Accuracy per byte": the
     bits per token the per-query plan needs to match the attention error of the 136-bit
     fixed-depth scans).  Four layers of the Qwen3-8B-shaped cache (32 KV heads x 4
     queries, n = 32768, k = 512).  Error of a row = ||o - o_dense|| / ||o_dense||, o_dense =
-    softmax attention over all n tokens (fp32 arithmetic on the bf16 K/V rows).  For every
-    budget B the Fathom plan runs through fathom_step; the comparators are the 136-bit
-    fixed-depth scan (34 channels of largest variance, all four planes) and the exact
-    top-k (the k largest exact logits).  Synthetic keys and queries stand in for the
-    pages' five models, so this is a proxy for their 46-74-bit finding, not a check of it."""
+    softmax attention over all n tokens in fp64 on the bf16 K/V rows (attention_references,
+    checked against the oracle).  For every budget B the Fathom plan runs through
+    fathom_step; the comparators are the 136-bit fixed-depth scan (34 channels of largest
+    variance, all four planes) and the exact top-k (the k largest fp64 logits, ties to the
+    lower index).  Synthetic keys and queries stand in for the pages' five models, so this
+    is a proxy for their 46-74-bit finding, not a check of it."""
     import torch
     from bit_plane_kv_amd import fathom as F
     from bit_plane_kv_amd import synth
@@ -559,40 +611,17 @@ def accuracy_sweep(args):
     sm = float(np.float32(1.0 / np.sqrt(128)))
     fixed = F.fathom_plan_fixed(st, 34)
     res = {"workload": "qwen3_8b_32k_hbm, layers 0-3 (32 KV heads x 4 queries)", "k": k,
-           "error": "mean over rows of ||o - o_dense|| / ||o_dense||"}
+           "error": "mean over rows of ||o - o_dense|| / ||o_dense||, o_dense in fp64"}
     regimes = {"iid_queries": synth.queries_np(args.seed, cfg.cfg_id, heads, G),
                "heavy_tailed_queries": synth.queries_heavy_np(args.seed, cfg.cfg_id, heads, G)}
     for name, q_np in regimes.items():
         q = torch.from_numpy(q_np).to(dev)
-        # dense reference, fp32 arithmetic, head by head
-        logits = torch.empty((H, G, n), dtype=torch.float32, device=dev)
-        dense = torch.empty((H, G, 128), dtype=torch.float32, device=dev)
-        for h in range(H):
-            logits[h] = torch.matmul(q[h], K[h].float().t().contiguous()) * sm
-            dense[h] = torch.matmul(torch.softmax(logits[h], -1), V[h].float())
-        dn = dense.norm(dim=-1)
-
-        def err(out):
-            e = (out.float() - dense).norm(dim=-1) / dn
-            return {"mean": round(float(e.mean()), 5), "max": round(float(e.max()), 5)}
-
-        r = {"fathom": {}}
-        out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
-        for B in ACC_BUDGETS:
-            F.fathom_step(st, q, K, V, B, k, sm, out=out)
-            r["fathom"][str(B)] = err(out)
-        idx = F.fathom_topk(F.fathom_scan(st, q, fixed), k)
-        r["fixed136"] = err(F.fathom_sparse_attn(q, K, V, idx, sm))
-        top = torch.topk(logits, k, dim=-1).indices.sort(dim=-1).values.to(torch.int32)
-        r["exact_topk"] = err(F.fathom_sparse_attn(q, K, V, top.contiguous(), sm))
-        match = [B for B in ACC_BUDGETS
-                 if r["fathom"][str(B)]["mean"] <= r["fixed136"]["mean"]]
-        r["bits_to_match_fixed136"] = match[0] if match else None
-        r["bytes_ratio_vs_fixed136"] = round(136 / match[0], 2) if match else None
+        dense, top = attention_references(q, K, V, k, sm)
+        r = accuracy_rows(F, st, q, K, V, k, sm, fixed, ACC_BUDGETS, dense, top)
         res[name] = r
         log(f"[bench] accuracy ({name}): fixed-136 {r['fixed136']}, exact top-k "
             f"{r['exact_topk']}, bits to match {r['bits_to_match_fixed136']}")
-        del logits, dense
+        del dense, top
     log(f"[bench] accuracy sweep in {time.time() - t0:.1f}s")
     del K, V, st
     torch.cuda.empty_cache()

@@ -137,13 +137,15 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ s
 }
 
 // Runs of run_vec 16-byte vectors, the r-th starting at src + r * stride bytes; the
-// work-items walk all runs' vectors in order (total < 2^32).
+// work-items walk all runs' vectors in order.  The index is 64-bit, so the stride
+// over the grid cannot wrap it below `total` (total < 2^32 keeps the division cheap).
 __global__ __launch_bounds__(256) void k_stream_runs(const char *__restrict__ src,
                                                      uint32_t run_vec, uint64_t stride,
-                                                     uint32_t total, uint64_t *__restrict__ sink) {
+                                                     uint64_t total, uint64_t *__restrict__ sink) {
     uint32_t a = 0, b = 0, c = 0, d = 0;
-    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
-        const uint32_t r = i / run_vec, o = i - r * run_vec;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * 256u) {
+        const uint32_t r = (uint32_t)i / run_vec, o = (uint32_t)i - r * run_vec;
         const uint4 v = *reinterpret_cast<const uint4 *>(src + r * stride + (uint64_t)o * 16u);
         a ^= v.x;
         b ^= v.y;
@@ -176,8 +178,8 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint64_t *sink,
 hipError_t launch_stream_runs(const void *src, size_t run_bytes, size_t stride_bytes,
                               size_t n_runs, uint64_t *sink, hipStream_t s) {
     const uint32_t run_vec = (uint32_t)(run_bytes / 16);
-    const uint32_t total = (uint32_t)(run_vec * n_runs);
-    const int grid = (int)std::min<size_t>((total + 255) / 256, 4096);
+    const uint64_t total = (uint64_t)run_vec * (uint64_t)n_runs;  // < 2^32 (checked)
+    const int grid = (int)std::min<uint64_t>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(k_stream_runs, dim3(std::max(grid, 1)), dim3(256), 0, s,
                        static_cast<const char *>(src), run_vec, (uint64_t)stride_bytes, total,
                        sink);

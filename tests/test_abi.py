@@ -171,6 +171,9 @@ def test_stream_read_and_host_alloc_checks():
     assert L.fathom_stream_read_runs(FAKE, 32, 32, 0, FAKE, None) == F.ERR_INVALID_ARG
     assert L.fathom_stream_read_runs(FAKE, 1 << 20, 1 << 20, 1 << 20, FAKE,
                                      None) == F.ERR_UNSUPPORTED
+    # 2^32 vectors of 16 bytes in all: refused (the kernel's run division is 32-bit)
+    assert L.fathom_stream_read_runs(FAKE, 16, 16, 1 << 32, FAKE, None) == F.ERR_UNSUPPORTED
+    assert L.fathom_stream_read_runs(FAKE, 64, 64, 1 << 30, FAKE, None) == F.ERR_UNSUPPORTED
     p = ctypes.c_void_p()
     assert L.fathom_host_alloc(0, 0, ctypes.byref(p)) == F.ERR_INVALID_ARG
     assert L.fathom_host_alloc(16, 2, ctypes.byref(p)) == F.ERR_INVALID_ARG
@@ -202,3 +205,4 @@ def test_workspace_formulas():
         F.workspace_size(F.OP_STEP, 8, 9, 100, 10)
     with pytest.raises(F.FathomError):
         F.workspace_size(7, 8, 1, 100, 10)
+
