@@ -2,6 +2,7 @@
 // when they fail), device-visibility checks of the pointers, then the launches.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -89,6 +90,32 @@ size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
+// The workspace of fathom_step_noalloc: device memory the library owns, one copy on
+// each GPU that loads it.  In host code this name stands for a host-side shadow, not a
+// device address; the device address comes from hipGetSymbolAddress (scratch_address)
+// and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[FATHOM_STATIC_SCRATCH_BYTES];
+
+// Device address of the current device's scratch array, looked up once per device.
+int scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return FATHOM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (g != hipSuccess) return hip_status(g);
+        if (!p) return hip_status(hipErrorInvalidSymbol);
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return FATHOM_OK;
+}
+
 #define FATHOM_TRY(expr)                                                                 \
     do {                                                                                 \
         const int rc__ = (expr);                                                         \
@@ -120,6 +147,7 @@ const char *fathom_status_string(int status) {
     case FATHOM_ERR_WORKSPACE: return "workspace too small";
     case FATHOM_ERR_NOT_MAPPED: return "pointer not accessible by the GPU";
     case FATHOM_ERR_HIP: return "HIP runtime error";
+    case FATHOM_ERR_SCRATCH: return "problem needs more than the 64 MiB static scratch";
     default: return "unknown status";
     }
 }
@@ -433,6 +461,23 @@ int fathom_step(const fathom_store *st, const float *q, const uint16_t *K, const
                 void *stream) {
     return step_impl(st, q, K, V, G, B, k, sm_scale, out, depth_out, scores_out, idx_out, ws,
                      ws_bytes, stream, nullptr);
+}
+
+int fathom_step_noalloc(const fathom_store *st, const float *q, const uint16_t *K,
+                        const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                        uint8_t *depth_out, float *scores_out, int32_t *idx_out,
+                        void *stream) {
+    FATHOM_TRY(check_store(st));
+    FATHOM_TRY(check_g(G));
+    FATHOM_TRY(check_topk_k(st->n_tokens, k));
+    if (B < 0 || B > FATHOM_D * FATHOM_PLANES) return FATHOM_ERR_BUDGET;
+    if (step_ws_bytes(st->n_heads, G, st->n_tokens, k) > FATHOM_STATIC_SCRATCH_BYTES)
+        return FATHOM_ERR_SCRATCH;
+    if (!q || !K || !V || !out) return FATHOM_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    FATHOM_TRY(scratch_address(&ws));
+    return step_impl(st, q, K, V, G, B, k, sm_scale, out, depth_out, scores_out, idx_out, ws,
+                     FATHOM_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int fathom_step_timed(const fathom_store *st, const float *q, const uint16_t *K,

@@ -21,8 +21,9 @@ PLANES = 4
 MAX_G = 8
 TOPK_CHUNK = 32768
 
-OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_MAPPED, ERR_HIP = \
-    range(7)
+(OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_MAPPED, ERR_HIP,
+ ERR_SCRATCH) = range(8)
+STATIC_SCRATCH_BYTES = 64 << 20  # the static workspace of fathom_step_noalloc
 OP_QUANTIZE, OP_SCAN, OP_TOPK, OP_STEP, OP_SCAN_TOPK = range(5)
 
 
@@ -73,6 +74,8 @@ _SIGS = {
     "fathom_step_timed": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I,
                                ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P,
                                ctypes.POINTER(ctypes.c_void_p), _I]),
+    "fathom_step_noalloc": (_I, [ctypes.POINTER(fathom_store), _P, _P, _P, _I, _I, _I,
+                                 ctypes.c_float, _P, _P, _P, _P, _P]),
     "fathom_scan_extract": (_I, [_P, _P, _I, _P, _P, _P]),
     "fathom_pack_nibbles": (_I, [ctypes.POINTER(fathom_store), _P, _P]),
     "fathom_quantize_groups": (_I, [_P, ctypes.c_int64, ctypes.POINTER(fathom_gstore), _I, _I,
@@ -423,6 +426,19 @@ def fathom_step(store: Store, q, K, V, B: int, k: int, sm_scale: float, out=None
                              float(sm_scale), _ptr(out), _ptr(depth_out), _ptr(scores_out),
                              _ptr(idx_out), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(stream)), "fathom_step")
+    return out
+
+
+def fathom_step_noalloc(store: Store, q, K, V, B: int, k: int, sm_scale: float, out,
+                        depth_out=None, scores_out=None, idx_out=None, stream=None):
+    """fathom_step on the library's static scratch: no workspace argument, and nothing is
+    allocated here either, so `out` (bf16 [H][G][128]) must be given."""
+    H, G, d = q.shape
+    st = store.descriptor()
+    _check(lib().fathom_step_noalloc(ctypes.byref(st), _ptr(q), _ptr(K), _ptr(V), G, int(B),
+                                     int(k), float(sm_scale), _ptr(out), _ptr(depth_out),
+                                     _ptr(scores_out), _ptr(idx_out), _stream(stream)),
+           "fathom_step_noalloc")
     return out
 
 

@@ -52,7 +52,8 @@ enum fathom_status {
     FATHOM_ERR_UNSUPPORTED = 3, /* d != 128, G > 8, or k beyond the top-k limits */
     FATHOM_ERR_WORKSPACE = 4,   /* ws too small (see fathom_workspace_size) */
     FATHOM_ERR_NOT_MAPPED = 5,  /* a pointer the GPU cannot read or write */
-    FATHOM_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+    FATHOM_ERR_HIP = 6,         /* a HIP runtime call or launch failed */
+    FATHOM_ERR_SCRATCH = 7      /* needs more than the static scratch of fathom_step_noalloc */
 };
 
 #define FATHOM_D 128          /* channels per head this build supports */
@@ -353,6 +354,25 @@ int fathom_step_timed(const fathom_store *st, const float *q, const uint16_t *K,
                       const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
                       uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
                       size_t ws_bytes, void *stream, void *const *events, int n_events);
+
+/*
+ * fathom_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * preconditions and results as fathom_step, without ws / ws_bytes: the intermediates
+ * live in a static device array of the library, FATHOM_STATIC_SCRATCH_BYTES (64 MiB)
+ * on each GPU the library runs on, held until the process ends.  The array of the
+ * current device is used (the stream must belong to it).  A problem whose
+ * FATHOM_OP_STEP workspace exceeds it is refused on the host with FATHOM_ERR_SCRATCH
+ * (one layer of 8 KV heads x 4 queries fits up to about 480k tokens; 288 heads x 4
+ * queries up to about 12k).  The call allocates nothing and frees nothing; every value
+ * its kernels need to start from zero is cleared by them.  Calls share the array:
+ * calls that overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.
+ */
+#define FATHOM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int fathom_step_noalloc(const fathom_store *st, const float *q, const uint16_t *K,
+                        const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                        uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *stream);
 
 /*
  * Measurement helper for the roofline denominators (blog, "One measurement worth

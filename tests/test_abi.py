@@ -55,7 +55,7 @@ def test_word_stride():
 def test_version_and_status_strings():
     L = F.lib()
     assert L.fathom_version() == 100
-    for s in range(7):
+    for s in range(8):
         assert F.status_string(s)
     assert F.status_string(99) == "unknown status"
     assert L.fathom_last_hip_error() == 0
@@ -205,4 +205,27 @@ def test_workspace_formulas():
         F.workspace_size(F.OP_STEP, 8, 9, 100, 10)
     with pytest.raises(F.FathomError):
         F.workspace_size(7, 8, 1, 100, 10)
+
+
+def test_step_noalloc_refuses_what_exceeds_its_scratch():
+    """The allocation-free step checks its size on the host: a problem whose step
+    workspace exceeds the static 64 MiB is refused before any GPU call."""
+    L = F.lib()
+    assert F.STATIC_SCRATCH_BYTES == 64 << 20
+
+    def store(H, n):
+        st = F.fathom_store(H, n, 128, L.fathom_word_stride(n), FAKE, FAKE, FAKE, FAKE)
+        return ctypes.byref(st)
+
+    def call(H, n, G=4, B=92, k=512):
+        return L.fathom_step_noalloc(store(H, n), FAKE, FAKE, FAKE, G, B, k, 0.088, FAKE,
+                                     None, None, None, None)
+
+    assert F.workspace_size(F.OP_STEP, 288, 4, 32768, 512) > F.STATIC_SCRATCH_BYTES
+    assert call(288, 32768) == F.ERR_SCRATCH
+    assert call(8, 1 << 20) == F.ERR_SCRATCH
+    assert call(8, 1 << 20, B=600) == F.ERR_BUDGET
+    assert call(8, 32768, G=9) == F.ERR_UNSUPPORTED
+    assert call(8, 32768, k=0) == F.ERR_INVALID_ARG
+    assert F.status_string(F.ERR_SCRATCH).startswith("problem needs more")
 
