@@ -76,14 +76,16 @@ int check_topk_k(int n, int k) {
 }
 
 size_t step_ws_bytes(int H, int G, int n, int k) {
-    return round256(scan_ws_bytes(H, G)) + round256((size_t)H * G * n * sizeof(float)) +
+    // the score area holds every score (full path) or the candidate records (filtering
+    // path), whose rows are rounded up to whole 256-token blocks
+    return round256(scan_ws_bytes(H, G)) + round256(cand_bytes(H, G, n)) +
            round256(topk_ws_bytes(H * G, n, k)) + round256((size_t)H * G * k * sizeof(int32_t)) +
            round256((size_t)H * FATHOM_D) + round256(filter_mask_bytes(H, G, n)) +
            round256(filter_redo_bytes(H, G, n));
 }
 
 size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
-    return round256(scan_ws_bytes(H, G)) + round256((size_t)H * G * n * sizeof(float)) +
+    return round256(scan_ws_bytes(H, G)) + round256(cand_bytes(H, G, n)) +
            round256(filter_mask_bytes(H, G, n)) + round256(topk_ws_bytes(H * G, n, k)) +
            round256(filter_redo_bytes(H, G, n));
 }
@@ -351,7 +353,7 @@ int fathom_scan_topk(const fathom_store *st, const float *q, int G, const uint8_
     void *scan_ws = w;
     w += round256(scan_ws_bytes(H, G));
     float *cand = reinterpret_cast<float *>(w);
-    w += round256((size_t)H * G * n * sizeof(float));
+    w += round256(cand_bytes(H, G, n));
     uint32_t *masks = reinterpret_cast<uint32_t *>(w);
     w += round256(filter_mask_bytes(H, G, n));
     void *topk_ws = w;
@@ -420,8 +422,8 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     char *w = static_cast<char *>(ws);
     void *scan_ws = w;
     w += round256(scan_ws_bytes(H, G));
-    float *scores = scores_out ? scores_out : reinterpret_cast<float *>(w);
-    w += round256((size_t)H * G * n * sizeof(float));
+    float *scores = reinterpret_cast<float *>(w);  // every score, or candidate records
+    w += round256(cand_bytes(H, G, n));
     void *topk_ws = w;
     w += round256(topk_ws_bytes(H * G, n, k));
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(w);
@@ -435,15 +437,17 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     const hipStream_t s = as_stream(stream);
     auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], s)) : FATHOM_OK; };
     // every score is asked for, or no threshold can help (k too close to n for the
-    // sample, or B = 0: every score of a row is the same): scan all, then select
-    const bool full = scores_out || sample_rank(n, k) == 0 || B == 0;
+    // sample, or B = 0: every score of a row is the same), or the heads read more than
+    // 480 planes (the filter keeps no records for them): scan all, then select
+    const bool full = scores_out || sample_rank(n, k) == 0 || B == 0 || B > 480;
     FATHOM_TRY(mark(0));
     FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, full ? 0 : k, depth, scan_ws, s)));
     FATHOM_TRY(mark(1));
     if (full) {
-        FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s)));
+        float *all = scores_out ? scores_out : scores;
+        FATHOM_TRY(hip_status(launch_scan_main(*st, G, all, scan_ws, s)));
         FATHOM_TRY(mark(2));
-        FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
+        FATHOM_TRY(hip_status(launch_topk(all, H * G, n, k, idx, topk_ws, s)));
     } else {  // the filtering scan keeps the candidates only
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
         FATHOM_TRY(mark(2));

@@ -27,7 +27,10 @@ constexpr int kDigits = 4;                   // signed base-256 digits per weigh
 //   query); float S[8] (power-of-two weight unit of each query); uint32 tkey[8]
 //   (candidate threshold of each query as an order key, 0: keep every key); uint32
 //   cnt[8] (candidates the filtering scan kept per query); uint32 plane[512]
-//   (c*4 + j, channels ascending, planes ascending within a channel).
+//   (c*4 + j, channels ascending, planes ascending within a channel); uint32
+//   cnt_exact[8] (candidates whose exact score clears the threshold, counted by the
+//   select); uint32 ovf (bit g: a 256-token block of query g had more candidates than
+//   its record area holds); int32 xthr[8][8] (the filter's integer thresholds, below).
 //   record (kblock, lane), lane = 16*kb + 4*w + s:  uint32 row of plane s and of plane
 //   s+4 of group 4*kblock + kb (kSkipRow: no plane, load nothing), then for each set of
 //   4 queries the 8 bytes of A row (lane & 15) = (query 4*set + ((lane & 15) >> 2),
@@ -45,6 +48,9 @@ struct ScanMeta {
     uint32_t tkey[FATHOM_MAX_G];
     uint32_t cnt[FATHOM_MAX_G];
     uint32_t plane[kMaxPlanesPerHead];
+    uint32_t cnt_exact[FATHOM_MAX_G];
+    uint32_t ovf;
+    int32_t xthr[FATHOM_MAX_G][8];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
 
@@ -56,13 +62,23 @@ inline size_t scan_ws_bytes(int H, int G) {
     return (size_t)H * (kMetaBytes + scan_rec_bytes_per_head(G));
 }
 
-// Candidate filter.  The filtering scan keeps, per row (head, query), the tokens whose
-// score key is >= the row's threshold key: their scores go, in token order, to the
-// front of their 256-token block of a [H][G][n] fp32 buffer, and bit i of word w of a
-// [H][G][ceil(n/32)] uint32 mask marks token 32w + i as kept.  Any threshold is safe
-// once at least k tokens of the row are kept (the k-th largest score is then >= it);
-// the select recomputes a row that kept fewer.
+// Candidate filter.  Each row (head, query) has a threshold score T.  The filtering
+// scan decides in integers which tokens may clear it: with the digit sums of a token's
+// score (bit m of its byte), X = D2 + 256 D3 bounds the score to within the largest
+// possible contribution of the two low digits plus fp32 rounding, so the test
+// X >= xthr[g][m] (X <= xthr[g][7] for m = 7, whose byte value is negative) keeps every
+// token whose score is >= T and a few more.  A kept token's record -- int32 X and the
+// low part R = D0 + 256 D1 (int32: heads of more than 480 planes, where that sum could
+// overflow, keep no records and have all their rows rescored) -- goes, in token order, to the
+// front of its 256-token block of a [H][G][cand_stride(n)] area of 4-byte words (at
+// most kBlockRecords records a block; a block with more sets the row's ovf bit), and
+// bit i of word w of a [H][G][ceil(n/32)] uint32 mask marks token 32w + i as kept.
+// The select turns each record into the scan's exact fp32 score and counts the
+// candidates whose score is >= T: with at least k of them the row's k-th largest score
+// is >= T, so every winner was kept; a row with fewer (or with ovf set) is rescored.
 constexpr int kFilterBlockWords = 8;  // words per compaction block (256 tokens)
+constexpr int kBlockRecords = 128;    // 8-byte records in a block's 256 4-byte words
+__host__ __device__ inline int64_t cand_stride(int64_t n) { return (n + 255) / 256 * 256; }
 constexpr int kSampleRuns = 8;        // threshold sample: runs of 4 words per head
 constexpr int kSampleRunWords = 4;
 constexpr int kSampleWords = kSampleRuns * kSampleRunWords;  // 32 words: 1024 tokens
@@ -88,6 +104,9 @@ __host__ __device__ inline int sample_rank(int n, int k) {
     const double x = 0.5 * (5.0 + sqrt(25.0 + 4.0 * (double)k * (double)S / (double)n));
     const double m = ceil(x * x);
     return m > (double)S ? 0 : (int)m;
+}
+inline size_t cand_bytes(int H, int G, int n) {
+    return (size_t)H * G * (size_t)cand_stride(n) * sizeof(float);
 }
 inline size_t filter_mask_bytes(int H, int G, int n) {
     return (size_t)H * G * (size_t)((n + 31) / 32) * sizeof(uint32_t);

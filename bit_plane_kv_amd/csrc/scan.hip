@@ -33,16 +33,18 @@ namespace {
 // prepare: plane list, constant terms, weight units and MFMA operand records of one
 // head (one workgroup)
 // ---------------------------------------------------------------------------------
-// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h;
-// hi_mask = 0 when the upper 4 groups do not exist (their operand bytes are zero).
-template <int QS, bool kFirst>
+// One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h.
+// kHi: the upper 4 groups exist; without them their operand bytes are zero and their
+// words are neither transposed nor masked.
+template <int QS, bool kFirst, bool kHi>
 __device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4i (&A)[QS],
-                                          uint32_t hi_mask, int s, v4i (&acc)[2][8][QS]) {
+                                          int s, bool hi, v4i (&acc)[2][8][QS]) {
+    const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int pos = 0; pos < 2; ++pos) {
         uint32_t x[2][2];  // [half][planes 0-3 / 4-7]
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < (kHi ? 2 : 1); ++h) {
             x[h][0] = quad_byte_transpose(w[h][0][pos], s);
             x[h][1] = quad_byte_transpose(w[h][1][pos], s);
         }
@@ -50,8 +52,9 @@ __device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4
         for (int m = 0; m < 8; ++m) {
             const uint32_t mask = 0x01010101u << m;
             const uint32_t mhi = mask & hi_mask;
-            const v4i b = {(int)(x[0][0] & mask), (int)(x[0][1] & mask), (int)(x[1][0] & mhi),
-                           (int)(x[1][1] & mhi)};
+            const v4i b = kHi ? v4i{(int)(x[0][0] & mask), (int)(x[0][1] & mask),
+                                    (int)(x[1][0] & mhi), (int)(x[1][1] & mhi)}
+                              : v4i{(int)(x[0][0] & mask), (int)(x[0][1] & mask), 0, 0};
 #pragma unroll
             for (int set = 0; set < QS; ++set) {
                 const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[pos][m][set];
@@ -59,6 +62,13 @@ __device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4
             }
         }
     }
+}
+
+template <int QS>
+__device__ __forceinline__ void mma_item(const uint32_t (&w)[2][2][2], const v4i (&A)[QS], int s,
+                                         bool first, bool hi, v4i (&acc)[2][8][QS]) {
+    if (first) mma_kpair<QS, true, true>(w, A, s, hi, acc);
+    else mma_kpair<QS, false, true>(w, A, s, hi, acc);
 }
 
 // Candidate thresholds of one head (256 threads).  A guess of each query's score
@@ -212,9 +222,7 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
                 const uint2 ahi = hi ? la[((2 * kp + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
                 A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
             }
-            const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
-            if (kp == 0) mma_kpair<QS, true>(w, A, hi_mask, s, acc);
-            else mma_kpair<QS, false>(w, A, hi_mask, s, acc);
+            mma_item<QS>(w, A, s, kp == 0, hi, acc);
         }
     }
     const bool small = nkb < kMaxKBlocks;
@@ -245,6 +253,32 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             if (lane == 0) meta->tkey[4 * set + gq] = T;
         }
     }
+}
+
+// The filter's integer threshold for the tokens at bit m of their byte (see the
+// candidate filter in common.h).  With b = 2^m (-128 for m = 7), the token's score is
+// C + S (65536 X + R) / b, |R S / b| <= S rb (rb: the query's sum over planes of
+// |D0 + 256 D1| of its weights), and the scan's fp32 arithmetic is off the exact value
+// by less than 2^-22 (|C| + S mabs + S rb).  So a score >= T needs
+// 65536 X S / b >= T - C - eps - S rb, eps = 2^-20 (|C| + |T| + S mabs + S rb): for
+// b > 0 X >= that bound * b / (65536 S), for b < 0 X <= it.  One more unit of slack
+// covers the rounding of the bound itself.  live == false (no such query): keep none;
+// tkey 0: keep all.
+__device__ __forceinline__ int32_t filter_threshold(bool live, uint32_t tkey, float Cf, float Sf,
+                                                    double rbs, double mabs, int m) {
+    const bool neg = m == 7;
+    if (!live) return neg ? INT32_MIN : INT32_MAX;
+    if (tkey == 0u) return neg ? INT32_MAX : INT32_MIN;
+    const double T = (double)__uint_as_float((tkey & 0x80000000u) ? (tkey ^ 0x80000000u) : ~tkey);
+    const double C = (double)Cf, S = (double)Sf;
+    const double srb = rbs * S, w = mabs * S;
+    const double eps = ldexp(fabs(C) + fabs(T) + w + srb, -20);
+    const double bound = (T - C) - eps - srb;
+    const double q = bound * (neg ? -128.0 : (double)(1 << m)) / (65536.0 * S);
+    const double t = neg ? floor(q) + 1.0 : ceil(q) - 1.0;
+    if (t <= (double)INT32_MIN) return INT32_MIN;
+    if (t >= (double)INT32_MAX) return INT32_MAX;
+    return (int32_t)t;
 }
 
 // Inputs of the prepare step a thread reads (threads 0..127: channel tid): the head's
@@ -399,13 +433,45 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         }
         if (QS == 2) dst[6] = dst[7] = 0;
     }
-    if (tid < FATHOM_MAX_G) meta->cnt[tid] = 0u;
+    if (tid < FATHOM_MAX_G) {
+        meta->cnt[tid] = 0u;
+        meta->cnt_exact[tid] = 0u;
+    }
+    if (tid == 0) meta->ovf = 0u;
     if (k <= 0) {
         if (tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
         return;
     }
+    // per query: sum over the planes of |M| and of |D0 + 256 D1| of M's digits (the
+    // part of a weight the filter's integer test does not see), exact in fp64
+    __shared__ double rb[NQ], mabs[NQ];
+    for (int g = tid >> 6; g < NQ; g += 4) {
+        double r = 0.0, a = 0.0;
+        for (int p = lane; p < nplanes; p += 64) {
+            const long long u = Mu[g][p];
+            const int d0 = (int)(int8_t)(uint8_t)weight_byte(u, 0);
+            const int d1 = (int)(int8_t)(uint8_t)weight_byte(u, 1);
+            r += fabs((double)(d0 + 256 * d1));
+            a += fabs((double)(u - kDigitBias));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            r += __shfl_xor(r, o, 64);
+            a += __shfl_xor(a, o, 64);
+        }
+        if (lane == 0) {
+            rb[g] = r;
+            mabs[g] = a;
+        }
+    }
     sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
                           meta);
+    __syncthreads();  // the thresholds and the sums are complete
+    if (tid < NQ * 8) {
+        const int g = tid >> 3, m = tid & 7;
+        meta->xthr[g][m] = filter_threshold(g < G, meta->tkey[g], cf[g], sf[g], rb[g], mabs[g], m);
+    }
+    if (tid >= NQ * 8 && tid < FATHOM_MAX_G * 8) meta->xthr[tid >> 3][tid & 7] = 0;
 }
 
 template <int QS>
@@ -489,11 +555,18 @@ __device__ __forceinline__ int tile_slot(int i, int c) {
     return kRowChunks * i + (c ^ (2 * (i & 3)));
 }
 
-// LDS per head slot: A operand halves [K-block of 4 groups][lane][QS] (8 bytes), then
-// the word offsets of each K-block's 32 rows [K-block][32]; then the tile ring.
+// LDS per head slot: A operand halves [K-block of 4 groups][lane][QS] (8 bytes); the
+// rows the copies read, [K-pair][row r of a K-block half][half] (kWide: row index or
+// kNoRow; otherwise the row's byte offset from the head's first row, absent rows
+// pointing at a row the head reads anyway); the filter thresholds [query][m]; then,
+// after both head slots, the tile ring.
+template <int QS>
+constexpr size_t lds_rows_off() { return (size_t)kMaxKBlocks * 64 * QS * 8; }
+template <int QS>
+constexpr size_t lds_xthr_off() { return lds_rows_off<QS>() + (size_t)kMaxKBlocks * 32 * 4; }
 template <int QS>
 constexpr size_t lds_head_bytes() {
-    return (size_t)kMaxKBlocks * 64 * QS * 8 + (size_t)kMaxKBlocks * 32 * 4;
+    return lds_xthr_off<QS>() + (size_t)FATHOM_MAX_G * 8 * 4;
 }
 template <int QS>
 constexpr size_t scan_lds_bytes() {
@@ -538,39 +611,57 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
     }
 }
 
-// The filtering form of the combine: the same scores, of which only those whose key is
-// >= the row's threshold key are written to the front of the wave's 256-token block
-// (words wb .. wb+7) of the row, with the block's 8 mask words; the row's count of kept
-// tokens grows by the block's.  Within a block the kept scores are ordered by word in
-// the order wb, wb+2, wb+4, wb+6, wb+1, wb+3, wb+5, wb+7 (pos, then w: lane 4w + s of a
-// query's 16 holds byte s of words wb + 2w + pos), and by token within a word.
-
-template <int QS>
-__device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const float (&Cq)[QS],
-                                               const float (&Sq)[QS], const float (&Tq)[QS],
-                                               bool small, int G, int jq, int s, int wq,
-                                               int lane, int wi, int n, float *hcand,
-                                               uint32_t *hmask, uint32_t *hcnt) {
+// The filtering form of the combine (the candidate filter in common.h): per token the
+// integer test X = D2 + 256 D3 against the row's threshold for its bit m, then the
+// records of the tokens that pass go to the front of the wave's 256-token block (words
+// wb .. wb+7) of the row's record area, with the block's 8 mask words; the row's count
+// of kept tokens grows by the block's.  Within a block the records are ordered by word
+// in the order wb, wb+2, wb+4, wb+6, wb+1, wb+3, wb+5, wb+7 (pos, then w: lane 4w + s of
+// a query's 16 holds byte s of words wb + 2w + pos), and by token within a word.  A
+// block with more than kBlockRecords candidates sets the row's ovf bit (its records are
+// then incomplete and the row is rescored), as does every row of a head of more than
+// 480 planes (!small: R would not fit int32).  xt: the lane's query's thresholds (keep
+// none for a query past G); ragged: the super-step reaches past token n.  kWide: 64-bit
+// record addresses; otherwise 32-bit byte offsets from hcand.
+template <int QS, bool kWide>
+__device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const int (&xt)[QS][8],
+                                               bool ragged, bool small, int G, int jq, int s,
+                                               int wq, int lane, int wi, int n, int64_t cstride,
+                                               char *hcand, uint32_t *hmask, uint32_t *hcnt,
+                                               uint32_t *hovf, uint32_t, uint32_t) {
     const int W = (n + 31) >> 5;
     const int wb = wi - 2 * wq;   // first word of the block
+    const uint32_t below = (1u << (8 * s)) - 1u;  // bits of the quad's lower lanes
 #pragma unroll
     for (int set = 0; set < QS; ++set) {
         const int g = 4 * set + jq;
         const bool live = g < G;  // the same for a query's 16 lanes
-        float *blk = hcand + (size_t)g * n + (size_t)wb * 32;
-        uint32_t base = 0u;       // kept tokens of the block's earlier words
+        if (!small) {
+            if (live && (lane & 15) == 0) atomicOr(hovf, 1u << g);
+            continue;
+        }
+        const size_t blk_bytes = ((size_t)g * cstride + (size_t)wb * 32) * 4;
+        uint32_t base = 0u;       // records of the block's earlier words
 #pragma unroll
         for (int pos = 0; pos < 2; ++pos) {
-            const int left = live ? n - ((wi + pos) * 32 + 8 * s) : 0;  // tokens < n
-            float v[8];
+            int xp[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) xp[m] = xt[set][m];
+            if (ragged) {  // tokens >= n keep nothing
+                const int left = n - ((wi + pos) * 32 + 8 * s);
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if (m >= left) xp[m] = m < 7 ? INT32_MAX : INT32_MIN;
+            }
+            bool keep[8];
             uint32_t bits = 0u;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                v[m] = combined_score<QS>(acc[pos][m][set], m, Cq[set], Sq[set], small);
-                bits |= (uint32_t)(m < left && v[m] >= Tq[set]) << m;
+                const int X = acc[pos][m][set][2] + acc[pos][m][set][3] * 256;
+                keep[m] = m < 7 ? X >= xp[m] : X <= xp[7];
+                bits |= (uint32_t)keep[m] << m;
             }
-            // the quad's 4 bytes make the mask word; the bytes below this lane's come
-            // first
+            // the quad's 4 bytes make the mask word
             uint32_t x = bits << (8 * s);
             x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
             x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
@@ -582,17 +673,39 @@ __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const
             // and the inclusive suffix (row_shl 4 and 8): together the row's total
             uint32_t suf = t + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x104, 0xF, 0xF, true);
             suf += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)suf, 0x108, 0xF, 0xF, true);
-            const uint32_t tot = inc + suf - t;
-            uint32_t r = base + inc - t + (uint32_t)__popc(x & ((1u << (8 * s)) - 1u));
-            base += tot;
+            const uint32_t r = base + inc - t + (uint32_t)__popc(x & below);
+            base += inc + suf - t;
             if (live) {
-#pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    if ((bits >> m) & 1u) blk[r++] = v[m];
                 if (s == 0 && wi + pos < W) hmask[(size_t)g * W + wi + pos] = x;
+                if (base <= (uint32_t)kBlockRecords) {
+                    if constexpr (kWide) {
+                        int2 *rec = reinterpret_cast<int2 *>(hcand + blk_bytes) + r;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            if (keep[m]) {
+                                const v4i d = acc[pos][m][set];
+                                *rec++ = make_int2(d[2] + d[3] * 256, d[0] + d[1] * 256);
+                            }
+                        }
+                    } else {
+                        uint32_t off = (uint32_t)blk_bytes + 8u * r;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            if (keep[m]) {
+                                const v4i d = acc[pos][m][set];
+                                *reinterpret_cast<int2 *>(hcand + off) =
+                                    make_int2(d[2] + d[3] * 256, d[0] + d[1] * 256);
+                                off += 8u;
+                            }
+                        }
+                    }
+                }
             }
         }
-        if (live && (lane & 15) == 0 && base) atomicAdd(hcnt + g, base);
+        if (live && (lane & 15) == 0) {
+            if (base > (uint32_t)kBlockRecords) atomicOr(hovf, 1u << g);
+            if (base) atomicAdd(hcnt + g, base);
+        }
     }
 }
 
@@ -601,7 +714,9 @@ __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const
 // compiler's own wait insertion does not treat every later LDS read as depending on it
 // (it cannot tell the tiles apart); the tile reads wait for it explicitly.
 // m0 is a reserved register: it is saved and restored around the copy, so the statement
-// leaves it as it found it.
+// leaves it as it found it.  copy16_to_lds takes a 64-bit address per lane;
+// copy16_to_lds_off a base address common to the wave plus a 32-bit byte offset per
+// lane (no 64-bit arithmetic per copy).
 __device__ __forceinline__ void copy16_to_lds(const uint32_t *src, uint32_t m0) {
     uint32_t saved;
     __asm__ volatile(
@@ -609,6 +724,15 @@ __device__ __forceinline__ void copy16_to_lds(const uint32_t *src, uint32_t m0) 
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
+        : "memory");
+}
+__device__ __forceinline__ void copy16_to_lds_off(const char *base, uint32_t off, uint32_t m0) {
+    uint32_t saved;
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(m0))
         : "memory");
 }
 
@@ -625,21 +749,17 @@ struct ScanSplit {
 
 template <int QS>
 __device__ __forceinline__ void load_head_consts(const ScanMeta *meta, int G, int jq,
-                                                 float (&C)[QS], float (&S)[QS],
-                                                 float (&T)[QS]) {
+                                                 float (&C)[QS], float (&S)[QS]) {
 #pragma unroll
     for (int set = 0; set < QS; ++set) {
         const int g = 4 * set + jq;
         C[set] = g < G ? meta->C[g] : 0.0f;
         S[set] = g < G ? meta->S[g] : 0.0f;
-        // the threshold key as a float: for non-NaN scores v, order_key(v) >= key
-        // exactly when v >= this value (-0 and +0 compare equal); key 0 keeps all
-        const uint32_t key = g < G ? meta->tkey[g] : 0u;
-        T[set] = key == 0u ? -INFINITY
-                           : __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
     }
 }
 
+// kWide: a head's 512 rows span 4 GiB or more, so the copies take 64-bit addresses
+// per lane; otherwise 32-bit byte offsets from the head's first row.
 template <int QS, bool kWide, bool kFilter>
 __global__ __launch_bounds__(kScanThreads)
 __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) void k_scan_main(
@@ -648,7 +768,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     extern __shared__ uint4 lds_u4[];
     char *lds = reinterpret_cast<char *>(lds_u4);
     constexpr size_t kHeadBytes = lds_head_bytes<QS>();
-    constexpr size_t kRowsOff = (size_t)kMaxKBlocks * 64 * QS * 8;
+    constexpr size_t kRowsOff = lds_rows_off<QS>();
+    constexpr size_t kXthrOff = lds_xthr_off<QS>();
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
     const uint32_t tiles_base = lds_base + 2 * (uint32_t)kHeadBytes;
     const int nss = sp.nss;
@@ -676,6 +797,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         const int hk = k ? h1 : h0, nk = k ? nkb1 : nkb0;
         const uint4 *grec = reinterpret_cast<const uint4 *>(
             ws + (size_t)H * kMetaBytes + (size_t)hk * kMaxKBlocks * 64 * 16 * QS);
+        const uint32_t *grec32 = reinterpret_cast<const uint32_t *>(grec);
         uint2 *la = reinterpret_cast<uint2 *>(lds + k * kHeadBytes);
         uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + k * kHeadBytes + kRowsOff);
         for (int e = tid; e < nk * 64; e += kScanThreads) {
@@ -685,14 +807,29 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
                 const uint4 r2 = grec[(size_t)e * QS + 1];
                 la[e * QS + 1] = make_uint2(r2.x, r2.y);
             }
-            const int ln = e & 63;
-            if ((ln & 15) < 4) {  // lane 16*kb + s names planes s and s+4 of group kb
-                const int row = (e >> 6) * 32 + 8 * (ln >> 4) + (ln & 3);
-                lrow[row] = r.x < (uint32_t)kMaxPlanesPerHead
-                                ? (kWide ? r.x : r.x * (uint32_t)word_stride) : kNoRow;
-                lrow[row + 4] = r.y < (uint32_t)kMaxPlanesPerHead
-                                    ? (kWide ? r.y : r.y * (uint32_t)word_stride) : kNoRow;
+        }
+        // row r of K-block kb: plane (r & 7) of group 4 kb + (r >> 3), whose record lane
+        // is 16 (r >> 3) + (r & 3), word 0 (planes 0-3) or 1 (planes 4-7)
+        const uint32_t first_row = grec32[0];
+        const uint32_t dead = kWide ? kNoRow
+                                    : (first_row < (uint32_t)kMaxPlanesPerHead
+                                           ? first_row * (uint32_t)word_stride * 4u : 0u);
+        const int nk2 = 2 * ((nk + 1) >> 1);
+        for (int e = tid; e < nk2 * 32; e += kScanThreads) {
+            const int kb = e >> 5, r = e & 31;
+            uint32_t v = dead;
+            if (kb < nk) {
+                const uint32_t p =
+                    grec32[((size_t)kb * 64 + 16 * (r >> 3) + (r & 3)) * 4 * QS + ((r >> 2) & 1)];
+                if (p < (uint32_t)kMaxPlanesPerHead)
+                    v = kWide ? p : p * (uint32_t)word_stride * 4u;
             }
+            lrow[((kb >> 1) * 32 + r) * 2 + (kb & 1)] = v;
+        }
+        if constexpr (kFilter) {
+            const ScanMeta *mk = k ? meta1 : meta0;
+            int32_t *lx = reinterpret_cast<int32_t *>(lds + k * kHeadBytes + kXthrOff);
+            if (tid < FATHOM_MAX_G * 8) lx[tid] = mk->xthr[tid >> 3][tid & 7];
         }
     }
     __syncthreads();
@@ -701,9 +838,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
     const size_t head_words = (size_t)kMaxPlanesPerHead * word_stride;
     float C0[QS], S0[QS], C1[QS], S1[QS];
-    float T0[QS], T1[QS];
-    load_head_consts<QS>(meta0, G, jq, C0, S0, T0);
-    load_head_consts<QS>(meta1, G, jq, C1, S1, T1);
+    load_head_consts<QS>(meta0, G, jq, C0, S0);
+    load_head_consts<QS>(meta1, G, jq, C1, S1);
     const bool small = max(nkb0, nkb1) < kMaxKBlocks;
     const int npr0 = (nkb0 + 1) >> 1, npr1 = (nkb1 + 1) >> 1;  // K-pairs per super-step
     // super-steps of the run, counted from a: [0, h1rel) in head h0, [h1rel, len) in h1
@@ -717,28 +853,35 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int cgrp = wave / (kWaves / 4);
     const int crow = (wave % (kWaves / 4)) * kCopyRows + lane / kRowChunks;
     const int cchunk = (lane % kRowChunks) ^ (2 * (crow & 3));
+    const int crr = 8 * cgrp + crow;  // row of a K-block half
     const uint32_t cdst = (uint32_t)(cgrp * kGroupBytes +
                                      (wave % (kWaves / 4)) * kCopyRows * kRowChunks * 16);
+    // last 16-byte chunk of a row: chunks past the row's end read it instead
+    const uint32_t last_chunk = (uint32_t)(word_stride - 4) * 4u;
     int iss = 0, ipr = 0, fi = 0;
     auto issue = [&]() {
         const int k = iss >= h1rel ? 1 : 0;
         const int hh = k ? h1 : h0;
-        const int nk = k ? nkb1 : nkb0;
-        const int word = (k ? iss - h1rel : ss0 + iss) * kSuperWords + 4 * cchunk;
-        const uint32_t *lrow =
-            reinterpret_cast<const uint32_t *>(lds + k * kHeadBytes + kRowsOff);
-        const uint32_t *hbase = planes + (size_t)hh * head_words + word;
+        const int ss = k ? iss - h1rel : ss0 + iss;
+        const uint2 ro = *reinterpret_cast<const uint2 *>(
+            lds + k * kHeadBytes + kRowsOff + ((size_t)ipr * 32 + crr) * 8);
         const uint32_t tile = tiles_base + (uint32_t)((fi % kTiles) * kTileBytes) + cdst;
+        if constexpr (kWide) {
+            const int word = ss * kSuperWords + 4 * cchunk;
+            const uint32_t *hbase = planes + (size_t)hh * head_words + min(word, word_stride - 4);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int kb = 2 * ipr + half;
-            const uint32_t row = kb < nk ? lrow[kb * 32 + 8 * cgrp + crow] : kNoRow;
-            // rows not read and chunks past the row all fetch the store's first 16 bytes
-            const bool live = row != kNoRow && word < word_stride;
-            const uint32_t *src =
-                live ? hbase + (kWide ? (size_t)row * (size_t)word_stride : (size_t)row)
-                     : planes;
-            copy16_to_lds(src, tile + (uint32_t)(half * 4 * kGroupBytes));
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t row = half ? ro.y : ro.x;
+                // absent rows all fetch the store's first 16 bytes
+                const uint32_t *src =
+                    row != kNoRow ? hbase + (size_t)row * (size_t)word_stride : planes;
+                copy16_to_lds(src, tile + (uint32_t)(half * 4 * kGroupBytes));
+            }
+        } else {
+            const char *hbase = reinterpret_cast<const char *>(planes + (size_t)hh * head_words);
+            const uint32_t chunk = min((uint32_t)(ss * kSuperWords + 4 * cchunk) * 4u, last_chunk);
+            copy16_to_lds_off(hbase, ro.x + chunk, tile);
+            copy16_to_lds_off(hbase, ro.y + chunk, tile + (uint32_t)(4 * kGroupBytes));
         }
         ++fi;
         if (++ipr == (k ? npr1 : npr0)) {
@@ -754,6 +897,54 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int rchunk = 2 * wave + (wq >> 1);  // operand chunk and half of this lane
     const int rhalf = 8 * (wq & 1);
     const int qgrp = lane >> 4;               // operand group q (and q + 4)
+    // A super-step's scores are combined after the barrier of the next item, before
+    // that item's copies are issued: its stores then precede the newest copies in the
+    // wave's memory-instruction order, and the wait for the next tile (vmcnt(2): all but
+    // the newest copies) covers them rather than copies just issued.  pk: head slot of
+    // the pending combine (-1: none), pss_c: its super-step in the run.
+    int pk = -1, pss_c = 0;
+    uint32_t ptile = 0u;  // LDS address of the tile of the pending super-step's last item
+    auto combine = [&]() {
+        const int k = pk;
+        const int hh = k ? h1 : h0;
+        const int nk = k ? nkb1 : nkb0;
+        const int ssh = k ? pss_c - h1rel : ss0 + pss_c;  // super-step within the head
+        const int wi = (ssh * kWaves + wave) * 8 + 2 * wq;
+        if constexpr (kFilter) {
+            ScanMeta *mh =
+                reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) + (size_t)hh * kMetaBytes);
+            // this lane's queries' thresholds, from the head's LDS slot
+            const int32_t *lx = reinterpret_cast<const int32_t *>(lds + k * kHeadBytes + kXthrOff);
+            int xt[QS][8];
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {
+                const int4 x0 = *reinterpret_cast<const int4 *>(lx + (4 * set + jq) * 8);
+                const int4 x1 = *reinterpret_cast<const int4 *>(lx + (4 * set + jq) * 8 + 4);
+                xt[set][0] = x0.x; xt[set][1] = x0.y; xt[set][2] = x0.z; xt[set][3] = x0.w;
+                xt[set][4] = x1.x; xt[set][5] = x1.y; xt[set][6] = x1.z; xt[set][7] = x1.w;
+            }
+            const int64_t cs = cand_stride(n);
+            const bool ragged = (ssh + 1) * kSuperWords * 32 > n;
+            // stage and dummy slots: this wave's two 1 KiB copy areas of the tile its
+            // next copies will fill (every wave is done reading that tile)
+            const uint32_t mine = ptile + cdst;
+            combine_filter<QS, kWide>(acc, xt, ragged, nk < kMaxKBlocks, G, jq, s, wq, lane, wi,
+                                      n, cs, reinterpret_cast<char *>(scores + (size_t)hh * G * cs),
+                                      masks + (size_t)hh * G * ((n + 31) >> 5), mh->cnt,
+                                      &mh->ovf, mine, mine + (uint32_t)(4 * kGroupBytes) + 8u * lane);
+        } else {
+            // the head's constants, picked element by element: choosing between the two
+            // arrays as a whole made them addressable, i.e. scratch memory
+            float Ck[QS], Sk[QS];
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {
+                Ck[set] = k ? C1[set] : C0[set];
+                Sk[set] = k ? S1[set] : S0[set];
+            }
+            combine_store<QS>(acc, Ck, Sk, small, G, jq, s, wi, n, scores + (size_t)hh * G * n);
+        }
+        pk = -1;
+    };
     for (int f = 0; f < nitems; ++f) {
         // this wave's copies of item f have landed (2 copies per later item in flight)
         if (fi - f - 1 == kTiles - 2) {
@@ -768,6 +959,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // ... and every wave's; tile f-1 is free again
         __asm__ volatile("" ::: "memory");
+        if (pk >= 0) combine();
         if (fi < nitems) issue();
         const int k = pss >= h1rel ? 1 : 0;
         const int nk = k ? nkb1 : nkb0;
@@ -792,35 +984,16 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
             const uint2 ahi = hi ? la[((2 * ppr + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
             A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
         }
-        const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
-        if (ppr == 0) mma_kpair<QS, true>(w, A, hi_mask, s, acc);
-        else mma_kpair<QS, false>(w, A, hi_mask, s, acc);
+        mma_item<QS>(w, A, s, ppr == 0, hi, acc);
         if (++ppr == (k ? npr1 : npr0)) {
-            const int hh = k ? h1 : h0;
-            const int wi = ((k ? pss - h1rel : ss0 + pss) * kWaves + wave) * 8 + 2 * wq;
-            // the head's constants, picked element by element: choosing between the two
-            // arrays as a whole made them addressable, i.e. scratch memory
-            float Ck[QS], Sk[QS], Tk[QS];
-#pragma unroll
-            for (int set = 0; set < QS; ++set) {
-                Ck[set] = k ? C1[set] : C0[set];
-                Sk[set] = k ? S1[set] : S0[set];
-                Tk[set] = k ? T1[set] : T0[set];
-            }
-            if constexpr (kFilter) {
-                ScanMeta *mh = reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) +
-                                                            (size_t)hh * kMetaBytes);
-                combine_filter<QS>(acc, Ck, Sk, Tk, small, G, jq, s, wq, lane, wi, n,
-                                   scores + (size_t)hh * G * n,
-                                   masks + (size_t)hh * G * ((n + 31) >> 5), mh->cnt);
-            } else {
-                combine_store<QS>(acc, Ck, Sk, small, G, jq, s, wi, n,
-                                  scores + (size_t)hh * G * n);
-            }
+            pk = k;
+            pss_c = pss;
+            ptile = tiles_base + (uint32_t)((f % kTiles) * kTileBytes);
             ppr = 0;
             ++pss;
         }
     }
+    if (pk >= 0) combine();
 }
 
 // Resident workgroups of a kernel instance over the device (asked once per device).
@@ -870,8 +1043,8 @@ hipError_t launch_main_qs(const fathom_store &st, int G, float *scores, const ch
 template <int QS>
 hipError_t launch_main_q(const fathom_store &st, int G, float *scores, const char *ws,
                          uint32_t *masks, hipStream_t s) {
-    // word offsets of a head's 512 rows fit 32 bits (below the no-row marker)?
-    const bool wide = (uint64_t)kMaxPlanesPerHead * (uint64_t)st.word_stride >= 0xFFFFFFFFull;
+    // byte offsets within a head's 512 rows fit 32 bits?
+    const bool wide = (uint64_t)kMaxPlanesPerHead * (uint64_t)st.word_stride * 4u > 0xFFFFFFFFull;
     if (masks)
         return wide ? launch_main_qs<QS, true, true>(st, G, scores, ws, masks, s)
                     : launch_main_qs<QS, false, true>(st, G, scores, ws, masks, s);

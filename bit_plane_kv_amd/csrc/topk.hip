@@ -118,8 +118,28 @@ struct FilterArgs {
     const uint32_t *masks;    // [R][W] kept-token masks
     const char *scan_ws;      // the prepared scan workspace (meta blocks, records)
     const uint32_t *planes;   // the store, for rows that are rescored
+    int64_t cstride;          // 4-byte words per row of the candidate record area
     int word_stride, W, G, H, qs;
 };
+
+// The scan's fp32 score of a candidate from its record (the candidate filter in
+// common.h): the same operations, in the same order, as the scan's combine of the
+// digit sums, for the token at bit m of its byte (S 2^-m by ldexp: the same exact
+// power-of-two scaling the scan applies).  Records exist only for heads of at most
+// 480 planes, whose low part R is an int32 sum.
+__device__ __forceinline__ float record_score(int2 rec, int m, float C, float S) {
+    const float f = fmaf((float)rec.x, 65536.0f, (float)rec.y);
+    const float mult = m < 7 ? ldexpf(S, -m) : -ldexpf(S, -7);
+    return fmaf(f, mult, C);
+}
+
+// A row whose candidates may miss a winner: it kept fewer than k tokens, a block of it
+// overflowed its record area, or fewer than k of its candidates (as counted by the
+// select) clear its threshold exactly.  Such rows are rescored from the store.
+__device__ __forceinline__ bool needs_rescore(const ScanMeta *meta, int g, int k) {
+    return meta->cnt[g] < (uint32_t)k || ((meta->ovf >> g) & 1u) ||
+           meta->cnt_exact[g] < (uint32_t)k;
+}
 
 // Filler candidates for slots [from, to) of a chunk's output: value with key 0 (below
 // every score) and an index past any row.  They fill the slots of a chunk that kept
@@ -133,12 +153,12 @@ __device__ __forceinline__ void fill_slots(float *out_val, int32_t *out_idx, int
     }
 }
 
-// Kept-candidate keys of this thread's word (tokens 32*word .. +31): the block's kept
-// scores lie at the front of its 256-token region, words in the order 0,2,4,6,1,3,5,7
+// Kept-candidate keys of this thread's word (tokens 32*word .. +31): the block's
+// records lie at the front of its 256-token region, words in the order 0,2,4,6,1,3,5,7
 // of the block, tokens ascending within a word.  Returns the mask.
-__device__ __forceinline__ uint32_t load_kept(const float *row_cand, const uint32_t *row_mask,
-                                              int word, int W, uint32_t lenmask,
-                                              uint32_t (&key)[kEPT]) {
+__device__ __forceinline__ uint32_t load_kept(const int2 *row_rec, const uint32_t *row_mask,
+                                              int word, int W, uint32_t lenmask, float C,
+                                              float S, uint32_t (&key)[kEPT]) {
     const uint32_t mk = (word < W ? row_mask[word] : 0u) & lenmask;
     const uint32_t c = (uint32_t)__popc(mk);
     const int j = threadIdx.x & 7;  // word within the block (blocks are 8 threads)
@@ -149,12 +169,12 @@ __device__ __forceinline__ uint32_t load_kept(const float *row_cand, const uint3
         const uint32_t co = (uint32_t)__shfl((int)c, 2 * (o & 3) + (o >> 2), 8);
         if (o < oj) pre += co;
     }
-    const float *src = row_cand + (size_t)(word & ~7) * 32 + pre;
+    const int2 *src = row_rec + (size_t)(word & ~7) * 16 + pre;
     uint32_t r = 0u;
 #pragma unroll
     for (int e = 0; e < kEPT; ++e) {
         key[e] = 0u;
-        if ((mk >> e) & 1u) key[e] = order_key(src[r++]);
+        if ((mk >> e) & 1u) key[e] = order_key(record_score(src[r++], e & 7, C, S));
     }
     return mk;
 }
@@ -264,13 +284,14 @@ __device__ __forceinline__ void select_chunk(
         const ScanMeta *meta =
             reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
         const int word = chunk * kThreads + tid;
-        if (meta->cnt[g] < (uint32_t)k) {
+        if (needs_rescore(meta, g, k)) {
             if constexpr (kCandOut)
                 rescore_word_call(fa, h, g, word, vmask, hist, key);
             else
                 rescore_word(fa, h, g, word, vmask, hist, key);
         } else {
-            vmask = load_kept(vals + row * in_stride, fa.masks + row * fa.W, word, fa.W, vmask,
+            vmask = load_kept(reinterpret_cast<const int2 *>(vals + row * fa.cstride),
+                              fa.masks + row * fa.W, word, fa.W, vmask, meta->C[g], meta->S[g],
                               key);
             if (kCandOut) {  // this chunk may hold fewer than k candidates
                 uint32_t total;
@@ -425,9 +446,21 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
                                                out_stride, fa);
 }
 
+// A row of several chunks whose chunks the filtered select did not hand over, but which
+// must be rescored: its exact candidate count, summed over its chunks by the select,
+// fell short of k.
+__device__ __forceinline__ bool rescore_whole_row(const FilterArgs &fa, int64_t row, int k) {
+    const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
+    const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
+    return meta->cnt[g] >= (uint32_t)k && !((meta->ovf >> g) & 1u) &&
+           meta->cnt_exact[g] < (uint32_t)k;
+}
+
 // The row chunks the filtered select handed over (listed as row * nch + chunk; their
 // count is the head-0 meta block's redo field), a grid-stride loop over the list: a
-// small grid, as the list is usually empty.
+// small grid, as the list is usually empty.  Rows of several chunks (kCandOut) whose
+// exact count fell short are then redone chunk by chunk, each workgroup checking its
+// own rows (r = blockIdx.x + gridDim.x * thread) first.
 constexpr int kRedoGrid = 16;
 // The final select (!kCandOut) may use 128 VGPRs, so that it needs no scratch.
 template <bool kCandOut>
@@ -438,10 +471,35 @@ __global__ __launch_bounds__(kThreads, kCandOut ? 8 : 1) void k_topk_redo(
     const uint32_t total = reinterpret_cast<const ScanMeta *>(fa.scan_ws)->redo;
     for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
         const uint32_t item = list[it];
-        select_chunk<false, kCandOut, true>((int64_t)(item / (uint32_t)nch),
-                                            (int)(item % (uint32_t)nch), vals, nullptr, row_len,
-                                            row_len, k, out_val, out_idx, out_stride, fa);
+        const int64_t row = (int64_t)(item / (uint32_t)nch);
+        if (kCandOut && rescore_whole_row(fa, row, k)) continue;  // redone below
+        select_chunk<false, kCandOut, true>(row, (int)(item % (uint32_t)nch), vals, nullptr,
+                                            row_len, row_len, k, out_val, out_idx, out_stride,
+                                            fa);
         __syncthreads();  // LDS is reused by the next item
+    }
+    if constexpr (kCandOut) {
+        __shared__ uint32_t xrows[kThreads];
+        __shared__ uint32_t nx;
+        const int64_t R = (int64_t)fa.H * fa.G;
+        const int64_t step = (int64_t)gridDim.x * kThreads;
+        for (int64_t base = blockIdx.x; base < R; base += step) {
+            if (threadIdx.x == 0) nx = 0u;
+            __syncthreads();
+            const int64_t r = base + (int64_t)gridDim.x * threadIdx.x;
+            if (r < R && rescore_whole_row(fa, r, k)) xrows[atomicAdd(&nx, 1u)] = (uint32_t)r;
+            __syncthreads();
+            const uint32_t cnt = nx;
+            for (uint32_t i = 0; i < cnt; ++i) {
+                const int64_t row = xrows[i];
+                for (int c = 0; c < nch; ++c) {
+                    select_chunk<false, true, true>(row, c, vals, nullptr, row_len, row_len, k,
+                                                    out_val, out_idx, out_stride, fa);
+                    __syncthreads();
+                }
+            }
+            __syncthreads();  // xrows and nx are rewritten next round
+        }
     }
 }
 
@@ -481,15 +539,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     __shared__ uint32_t hist[kSelBins];
     __shared__ uint32_t sh[2][4];
     __shared__ uint32_t pick[2][3];
-    __shared__ uint32_t smm[2][4];  // per-wave min and max key
+    __shared__ uint32_t smm[3][4];  // per-wave min and max key, count clearing the threshold
     const int tid = threadIdx.x, chunk = blockIdx.x, nch = gridDim.x;
     const int64_t row = (int64_t)row0 + blockIdx.y;
     const int64_t start = (int64_t)chunk * kTopkChunk;
     const int len = (int)min((int64_t)kTopkChunk, n - start);
     const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
     ScanMeta *meta0 = reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws));
-    const ScanMeta *meta =
-        reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
+    ScanMeta *meta =
+        reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws) + (size_t)h * kMetaBytes);
     // this thread's 4 mask words: chunk words 4 tid .. 4 tid + 3
     const int wl = kSelWords * tid;
     const int64_t wg = (int64_t)chunk * (kTopkChunk / 32) + wl;
@@ -506,7 +564,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         const uint32_t lm = t0 >= len ? 0u : (len - t0 >= 32 ? 0xFFFFFFFFu : (1u << (len - t0)) - 1u);
         mk[j] = wg + j < fa.W ? mk[j] & lm : 0u;
     }
-    const bool full = kept < (uint32_t)k;  // the row is rescored by the full select
+    // the row is rescored by the full select
+    const bool full = kept < (uint32_t)k || ((meta->ovf >> g) & 1u);
 #pragma unroll
     for (int j = 0; j < kSelWords; ++j) {
         if (full) mk[j] = 0u;
@@ -532,8 +591,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         off[2] = eb + c[0];
         off[1] = te + ob;
         off[3] = te + ob + c[1];
-        // first the row offset of each kept score, in token order ...
-        const uint32_t blk = (uint32_t)(start + 32 * (int64_t)(wl & ~7));
+        // first the record index of each kept token in the row, in token order ...
+        const uint32_t blk = (uint32_t)((start + 32 * (int64_t)(wl & ~7)) / 2);
         uint32_t pos = pos0;
 #pragma unroll
         for (int j = 0; j < kSelWords; ++j) {
@@ -548,39 +607,55 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         }
     }
     __syncthreads();
-    {   // ... then all the loads at once, each thread up to kSelCap / 256 of them, and the
-        // first histogram (top 11 bits) on the way
+    {   // ... then all the loads at once, each thread up to kSelCap / 256 of them; each
+        // record becomes the scan's exact score and its order key
         constexpr int kPer = kSelCap / kSelThreads;
-        const float *crow = cand + row * n;
-        float v[kPer];
+        const int2 *crow = reinterpret_cast<const int2 *>(cand + row * fa.cstride);
+        int2 v[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = tid + kSelThreads * u;
-            v[u] = e < (int)C ? crow[skey[e]] : 0.0f;
+            v[u] = e < (int)C ? crow[skey[e]] : make_int2(0, 0);
         }
-        // the keys' minimum and maximum on the way (for the radix start below)
-        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+        const float Cg = meta->C[g], Sg = meta->S[g];
+        const uint32_t tkey = meta->tkey[g];
+        // the keys' minimum and maximum on the way (for the radix start below), and how
+        // many clear the row's threshold
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nex = 0u;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = tid + kSelThreads * u;
             if (e < (int)C) {
-                const uint32_t key = order_key(v[u]);
+                const uint32_t key = order_key(record_score(v[u], soff[e] & 7, Cg, Sg));
                 skey[e] = key;
                 kmin = min(kmin, key);
                 kmax = max(kmax, key);
+                nex += key >= tkey;
             }
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
             kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+            nex += (uint32_t)__shfl_xor((int)nex, o, 64);
         }
         if ((tid & 63) == 0) {
             smm[0][tid >> 6] = kmin;
             smm[1][tid >> 6] = kmax;
+            smm[2][tid >> 6] = nex;
         }
     }
     __syncthreads();
+    {   // the candidates clearing the threshold exactly: with fewer than k a winner may be
+        // missing (rows of one chunk go to the full select; a row of several chunks is
+        // judged on its sum over chunks by the redo kernel)
+        const uint32_t nex = smm[2][0] + smm[2][1] + smm[2][2] + smm[2][3];
+        if (tid == 0) atomicAdd(&meta->cnt_exact[g], nex);
+        if (!kCandOut && nex < (uint32_t)k) {
+            if (tid == 0) list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
+            return;
+        }
+    }
     const int kk = min(k, kTopkChunk);
     const int64_t obase = row * out_stride + (int64_t)chunk * kk;
     const int kr = min(min(k, len), (int)C);
@@ -760,6 +835,7 @@ hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand
     fa.planes = st.planes;
     fa.word_stride = st.word_stride;
     fa.W = (st.n_tokens + 31) / 32;
+    fa.cstride = cand_stride(st.n_tokens);
     fa.G = G;
     fa.H = st.n_heads;
     fa.qs = query_sets(G);
