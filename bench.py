@@ -48,7 +48,8 @@ def parse():
                     help="target wall time of the oracle sample")
     ap.add_argument("--kernel", default=None,
                     choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136",
-                             "scan_extract", "scan_topk", "scan_nibble", "scan_b512"],
+                             "scan_extract", "scan_topk", "scan_nibble", "scan_b512",
+                             "step_1m_host", "step_1m_hbm"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--no-host", action="store_true",
@@ -90,6 +91,10 @@ def main():
         return
     if args.accuracy_only:
         print(json.dumps(accuracy_sweep(args)), flush=True)
+        return
+
+    if args.kernel in ("step_1m_host", "step_1m_hbm"):
+        print(json.dumps(step_1m_kernel(args)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]
@@ -198,6 +203,18 @@ def main():
     kept_total = float(ws[:H * 4096].view(torch.int32).view(H, 1024)[:, 28:28 + G].sum())
     log(f"[bench] phases over {args.steps} steps (ms): {phases}")
 
+    # ---------------- the decode step layer by layer (one sequence, one token) --------
+    per_layer = None
+    if H % 8 == 0 and H >= 8:
+        per_layer, out_layers = decode_per_layer(F, st, q, K, V, B, k, sm_scale, dev, stream,
+                                                 passes=max(5, min(args.steps, 20)),
+                                                 layers=H // 8)
+        # the same winners and outputs as the 288-head call
+        F.fathom_step(st, q, K, V, B, k, sm_scale, out=out, ws=ws)
+        torch.cuda.synchronize()
+        per_layer["outputs_equal_batched_step"] = bool(torch.equal(out, out_layers))
+        log(f"[bench] per-layer decode: {per_layer}")
+
     # ---------------- per-kernel times (cold caches between launches) ----------------
     kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
                         stream, reps=max(10, min(args.steps, 30)))
@@ -257,6 +274,10 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "roofline_full_scan": roofline_full,
+        "step_is": "one fathom_step over all 36 x 8 (layer, KV head) pairs: the batched "
+                   "form (36 sequences x 1 layer), not one sequence's token; per-layer "
+                   "sequential decode is under decode_per_layer",
+        "decode_per_layer": per_layer,
         "step_phases_ms": phases,
         "step_phase_rooflines": phase_rooflines,
         "cpu_baseline": cpu,
@@ -270,11 +291,44 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_ms_single_launch": pct,
         "parity_before_timing": parity,
+        "decode_1m": one_m_summary(host, per_layer),
         "host_resident": host,
         "accuracy_per_byte": acc,
         "grouped_store": grouped,
     }
     print(json.dumps(result), flush=True)
+
+
+def one_m_summary(host, per_layer):
+    """The metric's "1M-token decode-step ms", lifted out of the host-resident lines: the
+    one-layer step at n = 1M (store and K/V rows in pinned host memory, and mirrored in
+    HBM), its fraction of the link bound (plane bytes + winner rows over the measured
+    link rate L), the full-model scan + top-k at 1M, and the oracle's time."""
+    if not host or not isinstance(host.get("layer_1m_step"), dict):
+        return None
+    ls = host["layer_1m_step"]
+    if "step_ms_host" not in ls:
+        return None
+    m = host.get("qwen3_8b_1m_host") or {}
+    f92 = (m.get("budgets") or {}).get("92") or {}
+    f136 = (m.get("budgets") or {}).get("fixed136") or {}
+    key = "step_ms_plan_fused_scan_topk"
+    cpu = ls.get("cpu_baseline") or {}
+    return {
+        "layer_step_ms_host": ls["step_ms_host"], "layer_step_ms_hbm": ls["step_ms_hbm"],
+        "layer_step_frac_of_link_bound": ls.get("step_frac_of_link_bound"),
+        "layer_scan_frac_of_link": ls.get("scan_frac_of_link"),
+        "L_GBps": ls.get("L_GBps"),
+        "model_scan_topk_ms_host_B92": f92.get(key),
+        "model_scan_topk_ms_host_fixed136": f136.get(key),
+        "model_decode_ms_host_36_layer_steps_extrapolated":
+            round(36 * ls["step_ms_host"], 2),
+        "model_decode_ms_hbm_36_layer_steps_extrapolated":
+            round(36 * ls["step_ms_hbm"], 2),
+        "oracle_layer_step_ms_extrapolated": cpu.get("layer_step_ms_extrapolated"),
+        "oracle_model_step_ms_extrapolated": cpu.get("model_step_ms_extrapolated"),
+        "oracle_cores": cpu.get("cores"),
+    }
 
 
 def check_sample(st, q_np, K, V, depth, scores, idx, out, sample_keys, B, k, sm):
@@ -438,6 +492,104 @@ def step_phases(F, st, q, K, V, B, k, sm, out, ws, stream, steps):
         res[name] = round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
     res["step"] = round(float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])), 4)
     return res
+
+
+def decode_per_layer(F, st, q, K, V, B, k, sm, dev, stream, passes, layers=36, per_layer=8):
+    """A real decode step's shape: the model's layers one after another, each a
+    fathom_step over its 8 KV heads (layer l+1's queries would depend on layer l's
+    output, so layers cannot be batched), on one stream, with the 256 MB last-level
+    cache flushed (a 1 GiB streaming read) before every pass over the layers.
+
+    Timed three ways: (a) eager: the layers' fathom_step calls launched back to back,
+    GPU time between events around the pass (host launch cost included if the GPU
+    waits for it; host time per layer reported beside it); (b) graph: the same pass
+    captured once as a HIP graph and replayed, GPU time per replay, each replay's
+    outputs checked against the eager pass; (c) phases: fathom_step_timed per layer
+    (events between kernels), mean per phase over all layers and passes."""
+    import torch
+    G = q.shape[1]
+    ws = F.step_workspace(st.view_heads(0, per_layer), G, k, dev)
+    views = [(st.view_heads(per_layer * l, per_layer * (l + 1)), q[per_layer * l:per_layer * (l + 1)],
+              K[per_layer * l:per_layer * (l + 1)], V[per_layer * l:per_layer * (l + 1)])
+             for l in range(layers)]
+    out = torch.empty((layers * per_layer, G, 128), dtype=torch.bfloat16, device=dev)
+    outs = [out[per_layer * l:per_layer * (l + 1)] for l in range(layers)]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def one_pass():
+        for (sv, qv, Kv, Vv), ov in zip(views, outs):
+            F.fathom_step(sv, qv, Kv, Vv, B, k, sm, out=ov, ws=ws)
+
+    one_pass()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    eager, host = [], []
+    for _ in range(passes):
+        F.fathom_stream_read(flush, flush.numel(), sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        t0 = time.perf_counter()
+        one_pass()
+        host.append((time.perf_counter() - t0) * 1e6 / layers)
+        b.record(stream)
+        b.synchronize()
+        eager.append(a.elapsed_time(b))
+    same_eager = bool(torch.equal(out, ref))
+    # the pass as a graph (no memset nodes: the step's kernels clear what they need)
+    replays, same_graph, graph_error = [], True, None
+    try:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            one_pass()  # warm on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=gs):
+                one_pass()
+        torch.cuda.synchronize()
+        for _ in range(passes):
+            out.zero_()
+            F.fathom_stream_read(flush, flush.numel(), sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+            b.synchronize()
+            replays.append(a.elapsed_time(b))
+            same_graph = same_graph and bool(torch.equal(out, ref))
+        del graph
+    except Exception as e:  # report, keep the eager figures
+        graph_error = f"{type(e).__name__}: {e}"
+        torch.cuda.synchronize()
+    # phases, per layer
+    ph = {name: [] for name in PHASES}
+    for _ in range(passes):
+        F.fathom_stream_read(flush, flush.numel(), sink)
+        evs = []
+        for (sv, qv, Kv, Vv), ov in zip(views, outs):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(F.STEP_PHASES + 1)]
+            F.fathom_step_timed(sv, qv, Kv, Vv, B, k, sm, e, out=ov, ws=ws, stream=stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        for e in evs:
+            for i, name in enumerate(PHASES):
+                ph[name].append(e[i].elapsed_time(e[i + 1]))
+    del flush
+    med = lambda v: round(float(np.median(v)), 4)
+    res = {"layers": layers, "kv_heads_per_layer": per_layer, "passes": passes,
+           "timing": "GPU time of one pass over the layers (one token of one sequence), "
+                     "last-level cache flushed before each pass",
+           "ms_per_token_graph": med(replays) if replays else None,
+           "ms_per_token_eager": med(eager),
+           "us_per_layer_graph": (round(float(np.median(replays)) * 1e3 / layers, 2)
+                                  if replays else None),
+           "graph_error": graph_error,
+           "host_us_per_layer_call": round(float(np.median(host)), 1),
+           "phase_us_per_layer": {nm: round(float(np.mean(v)) * 1e3, 2) for nm, v in ph.items()},
+           "outputs_equal_batched_step": None, "eager_repeatable": same_eager,
+           "graph_replays_equal_eager": same_graph}
+    return res, ref
 
 
 def timed_ms(fn, stream, reps, flush=None, sink=None):
@@ -823,6 +975,44 @@ def host_resident_step(args, L):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     sm = float(np.float32(1.0 / np.sqrt(128)))
+    st_d, st_h, q, K_d, V_d, K_h, V_h = layer_1m_stores(args)
+    planes_h = st_h.planes
+    return host_resident_step_run(args, L, cfg, st_d, st_h, q, K_d, V_d, K_h, V_h, planes_h,
+                                  H, G, n, k, B, dev, stream, sm)
+
+
+def step_1m_kernel(args):
+    """--kernel step_1m_host / step_1m_hbm: the 1M-token layer's decode step launched
+    `reps` times (cold caches before each), store and K/V rows in pinned host memory or
+    in HBM, for profiler runs of its kernels."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS["qwen3_8b_1m_layer_step"]
+    G, k, B = cfg.G, cfg.k, args.budget
+    sm = float(np.float32(1.0 / np.sqrt(128)))
+    st_d, st_h, q, K_d, V_d, K_h, V_h = layer_1m_stores(args)
+    host = args.kernel == "step_1m_host"
+    st, K, V = (st_h, K_h, V_h) if host else (st_d, K_d, V_d)
+    ws = F.step_workspace(st_d, G, k, q.device)
+    out = torch.empty((cfg.H, G, 128), dtype=torch.bfloat16, device=q.device)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
+    sink = torch.zeros(2, dtype=torch.int64, device=q.device)
+    ms = timed_ms(lambda: F.fathom_step(st, q, K, V, B, k, sm, out=out, ws=ws),
+                  torch.cuda.current_stream(), args.reps, flush, sink)
+    return {"kernel": args.kernel, "reps": args.reps, "ms": round(ms, 4),
+            "config": cfg.name, "budget_bits": B}
+
+
+def layer_1m_stores(args):
+    """The 1M-token layer (8 KV heads): store and bf16 K/V rows in HBM, and the same
+    store planes and K/V rows copied to pinned host memory."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS["qwen3_8b_1m_layer_step"]
+    H, G, n = cfg.H, cfg.G, cfg.n
+    dev = torch.device("cuda:0")
     t0 = time.time()
     st_d = F.Store.empty(H, n, dev)
     K_d = torch.empty((H, n, 128), dtype=torch.bfloat16, device=dev)
@@ -842,7 +1032,13 @@ def host_resident_step(args, L):
     st_h = F.Store(planes_h, st_d.scale, st_d.zero, st_d.var, n)
     torch.cuda.synchronize()
     log(f"[bench] host-resident 1M layer ready in {time.time() - t0:.1f}s")
+    return st_d, st_h, q, K_d, V_d, K_h, V_h
 
+
+def host_resident_step_run(args, L, cfg, st_d, st_h, q, K_d, V_d, K_h, V_h, planes_h, H, G,
+                           n, k, B, dev, stream, sm):
+    import torch
+    from bit_plane_kv_amd import fathom as F
     ws = F.step_workspace(st_d, G, k, dev)
     out_d = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
     out_h = torch.empty_like(out_d)
@@ -876,6 +1072,9 @@ def host_resident_step(args, L):
     plane_gbps = plane_bytes / (scan_h * 1e-3) / 1e9
     oracle_check = layer_oracle_check(args, cfg, q, depth_of(st_d, q, B), idx_d, out_d,
                                       K_d, V_d, B, k, sm)
+    oracle_time = None if args.no_cpu_baseline else oracle_layer_time(args, cfg, q, K_d, V_d,
+                                                                      B, k, sm)
+    step_bytes = plane_bytes + H * G * k * 512
     return {
         "workload": cfg.name, "kv_heads": H, "queries_per_kv_head": G, "tokens": n,
         "budget_bits": B, "k": k, "host_equals_hbm": same, "oracle_check": oracle_check,
@@ -887,6 +1086,9 @@ def host_resident_step(args, L):
         "L_GBps": L["L_GBps"], "scan_frac_of_link": round(plane_gbps / L["L_GBps"], 4),
         "scan_gkeys_per_s_host": round(H * n / (scan_h * 1e-3) / 1e9, 2),
         "pinned_host_bytes": int(planes_h.numel() * 4 + 2 * K_h.numel() * 2),
+        "step_link_bytes": int(step_bytes),
+        "step_frac_of_link_bound": round(step_bytes / (L["L_GBps"] * 1e9) / (step_h * 1e-3), 4),
+        "cpu_baseline": oracle_time,
     }
 
 
@@ -925,6 +1127,42 @@ def layer_oracle_check(args, cfg, q, depth, idx, out, K, V, B, k, sm):
     return {"head": h, "plan": bool(np.array_equal(depth[h].cpu().numpy(), ref_depth[0])),
             "score_rel_err": err, "topk": bool(np.array_equal(gi, oracle.topk(got, k))),
             "attn_abs_err": aerr}
+
+
+def oracle_layer_time(args, cfg, q, K, V, B, k, sm, sample_heads=4):
+    """The oracle's time for the decode step of the 1M-token layer (plan + fp64 scores +
+    top-k + attention), measured on the first `sample_heads` of its 8 KV heads (OpenMP
+    over heads) and scaled to the layer and to the 36-layer model: labelled extrapolated."""
+    import torch
+
+    import oracle
+    from bit_plane_kv_amd import synth
+    n, G, H = cfg.n, cfg.G, cfg.H
+    hs = list(range(sample_heads))
+    keys = synth.keys_torch(args.seed, cfg.cfg_id, hs, n, "cuda").cpu().numpy()
+    s, z, codes = oracle.quantize(keys)          # store build: not part of a step
+    del keys
+    var = oracle.channel_var(codes, s)
+    Kh = K[:sample_heads].cpu().view(torch.int16).numpy().view(np.uint16)
+    Vh = V[:sample_heads].cpu().view(torch.int16).numpy().view(np.uint16)
+    qh = q[:sample_heads].cpu().numpy()
+    t0 = time.perf_counter()
+    depth = oracle.plan(qh, var, B)
+    sc = oracle.scores(codes, s, z, depth, qh)
+    idx = oracle.topk(sc.astype(np.float32).reshape(-1, n), k).reshape(sample_heads, G, k)
+    oracle.attention(qh, Kh, Vh, idx, sm)
+    t = time.perf_counter() - t0
+    cores = oracle.threads()
+    used = min(cores, sample_heads)
+    layer_ms = t * 1e3 * (H / sample_heads)
+    return {"kind": "oracle", "cores": used, "cpu_model": cpu_model(),
+            "value": round(H * n / (layer_ms * 1e-3) / 1e9, 6), "unit": "Gkeys/s",
+            "layer_step_ms_extrapolated": round(layer_ms, 1),
+            "model_step_ms_extrapolated": round(layer_ms * 36, 1),
+            "sample": f"{sample_heads} of the layer's {H} KV heads (n={n}, G={G}, B={B}, "
+                      f"k={k}): plan + fp64 scores + top-k + attention in {t:.2f} s wall on "
+                      f"{used} threads (OpenMP over heads); layer = x{H / sample_heads:g}, "
+                      f"model = x36 more, both extrapolated"}
 
 
 def cpu_baseline(cfg, args, st, q_np, K, V, B, k, sm, sample_keys):
