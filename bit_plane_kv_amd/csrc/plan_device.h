@@ -13,8 +13,8 @@
 // number of items before (c, t) in that order.
 //
 // The ranks come from the channels alone.  With the channels sorted by (w descending,
-// c ascending) and pos(X, c) = #{c' : w_c' > X, or w_c' = X and c' < c} (a binary search
-// in that order), item (c', t') comes before (c, t) exactly when channel c' comes
+// c ascending) and pos(X, c) = #{c' : w_c' > X, or w_c' = X and c' < c} (a search in
+// that order), item (c', t') comes before (c, t) exactly when channel c' comes
 // before (X, c) for X = w_c 4^(t' - t) (an exact scaling), except that the items of a
 // channel with w_c = 0 are all equal and ordered by t.  Hence
 //   rank(c, t) = sum over t' = 0..3 of pos(w_c 4^(t' - t), c)  (+ t when w_c = 0),
@@ -60,58 +60,90 @@ __device__ __forceinline__ void plan_load(const float *__restrict__ q,
 
 // Whole plan of head h from the loaded inputs: each channel's depth to cnt[0..127]
 // (LDS); 256 threads; ends with a barrier, so cnt is complete for every thread.
+//
+// Importances are compared by their bit patterns: for non-negative doubles (-0 is made
+// +0) the unsigned 64-bit order of the bits is the numeric order and equal bits are
+// equal values, so each comparison is one integer compare.  The order's tie rule (lower
+// channel first) only matters between equal importances; they are found by counting
+// the channels at each strict rank (the number of larger importances), and only the
+// channels that share one count the lower channels they tie with.
 __device__ __forceinline__ void plan_from(const float (&qp)[FATHOM_MAX_G], float vp, int G,
                                           int B, int *cnt) {
-    struct Entry {  // a channel in sorted order
-        double w;
-        int c, pad;
-    };
-    __shared__ double wsh[kD];
-    __shared__ Entry srt[kD];
+    __shared__ __align__(16) unsigned long long wkey[kD];  // by channel
+    __shared__ __align__(16) unsigned long long skey[kD];  // in (w desc, c asc) order
+    __shared__ int sch[kD];                                // the channel at each place
+    __shared__ int nrank[kD];                              // channels per strict rank
     const int tid = threadIdx.x, c = plan_channel(), half = tid & 1;
-    const double w = plan_importance(qp, vp, G);
-    if (!half) wsh[c] = w;
+    const double w = plan_importance(qp, vp, G) + 0.0;  // -0 -> +0
+    const unsigned long long bw = (unsigned long long)__double_as_longlong(w);
+    if (!half) wkey[c] = bw;
+    else nrank[c] = 0;
     __syncthreads();
-    // the channel's place in (w descending, c ascending): each thread counts half
-    int rank = 0;
-#pragma unroll 8
-    for (int o = 64 * half; o < 64 * half + 64; ++o) {
-        const double x = wsh[o];
-        rank += (x > w) || (x == w && o < c);
-    }
-    rank += __shfl_xor(rank, 1, 64);
-    if (!half) srt[rank] = Entry{w, c, 0};
-    __syncthreads();
-    // pos(w 4^j, c): thread half 0 searches j = -3 .. 0, half 1 j = 1 .. 3 (j = 4 is a
-    // dummy), all four at once: the length of the prefix of the sorted channels that
-    // comes before (X, c), found by steps of 128, 64, .., 1 (0 .. 128 channels)
-    double X[4];
-    int pos[4];
+    // strict rank: each thread counts the larger importances in one half of the channels
+    int r0 = 0, r1 = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        X[s] = ldexp(w, 2 * (half ? s + 1 : s - 3));
+    for (int o = 64 * half; o < 64 * half + 64; o += 2) {
+        const ulonglong2 x = *reinterpret_cast<const ulonglong2 *>(&wkey[o]);
+        r0 += x.x > bw;
+        r1 += x.y > bw;
+    }
+    int strict = r0 + r1;
+    strict += __shfl_xor(strict, 1, 64);
+    if (!half) atomicAdd(&nrank[strict], 1);
+    __syncthreads();
+    int rank = strict;
+    if (nrank[strict] > 1) {  // equal importances: the lower channels come first
+        int before = 0;       // (both threads of the channel take this branch)
+        for (int o = half; o < c; o += 2) before += wkey[o] == bw;
+        rank += before + __shfl_xor(before, 1, 64);
+    }
+    if (!half) {
+        skey[rank] = bw;
+        sch[rank] = c;
+    }
+    __syncthreads();
+    // P[j + 3] = pos(w 4^j, c), j = -3 .. 3.  j = 0 is the channel's own rank; thread
+    // half 0 searches j = -3 .. -1, half 1 j = 1 .. 3.  Channels before (X, c) form a
+    // prefix of the sorted order: its length is found from the last key of each group
+    // of 16 (the same 8 keys for every thread), then by four halving steps inside the
+    // group, then past the channels whose importance equals X and whose index is lower.
+    unsigned long long bx[3];
+    int pos[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const double X = ldexp(w, 2 * (half ? s + 1 : s - 3));
+        bx[s] = (unsigned long long)__double_as_longlong(X);
         pos[s] = 0;
     }
+    constexpr int kSeg = 16;
 #pragma unroll
-    for (int step = kD; step > 0; step >>= 1) {
+    for (int b = 0; b < kD / kSeg; ++b) {
+        const unsigned long long last = skey[kSeg * b + kSeg - 1];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (pos[s] + step <= kD) {
-                const Entry e = srt[pos[s] + step - 1];
-                if (e.w > X[s] || (e.w == X[s] && e.c < c)) pos[s] += step;
-            }
+        for (int s = 0; s < 3; ++s) pos[s] += kSeg * (last > bx[s]);
+    }
+#pragma unroll
+    for (int step = kSeg / 2; step > 0; step >>= 1) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const unsigned long long e = skey[min(pos[s] + step - 1, kD - 1)];
+            if (pos[s] < kD && e > bx[s]) pos[s] += step;
         }
     }
-    // P[j + 3] = pos(w 4^j, c) for j = -3 .. 3, from both threads of the channel
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        if (pos[s] < kD && skey[pos[s]] == bx[s]) {
+            while (pos[s] < kD && skey[pos[s]] == bx[s] && sch[pos[s]] < c) ++pos[s];
+        }
+    }
     int P[7];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 3; ++s) {
         const int other = __shfl_xor(pos[s], 1, 64);
-        const int lo = half ? other : pos[s];   // j = s - 3
-        const int hi = half ? pos[s] : other;   // j = s + 1
-        P[s] = lo;
-        if (s < 3) P[s + 4] = hi;
+        P[s] = half ? other : pos[s];       // j = s - 3
+        P[s + 4] = half ? pos[s] : other;   // j = s + 1
     }
+    P[3] = rank;
     int depth = 0;
 #pragma unroll
     for (int t = 0; t < kPlanes; ++t) {

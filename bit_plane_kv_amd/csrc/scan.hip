@@ -92,14 +92,19 @@ static_assert(kSampleWords == 32, "four waves of 8 sampled words");
 __device__ __forceinline__ void sample_issue(const uint32_t *__restrict__ hp, int W,
                                              int word_stride, const uint32_t *pl, int p0,
                                              int np, uint4 (&v)[kSamplePer]) {
+    uint32_t row[kSamplePer];
+#pragma unroll
+    for (int u = 0; u < kSamplePer; ++u) {  // every list read first (p0 + p < 512 always)
+        const int p = (threadIdx.x + 256 * u) / kSampleRuns;
+        row[u] = pl[p0 + p];
+    }
 #pragma unroll
     for (int u = 0; u < kSamplePer; ++u) {
         const int e = threadIdx.x + 256 * u;
         const int p = e / kSampleRuns, r = e % kSampleRuns;
         const int w0 = sample_run_word(r, W);
-        const uint32_t row = p < np ? pl[p0 + p] : 0u;
         // a run that starts below W lies in the row (word_stride >= 4 * ceil(W / 4))
-        v[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)row * word_stride +
+        v[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)(p < np ? row[u] : 0u) * word_stride +
                                                 (w0 < W ? w0 : 0));
     }
 }
@@ -134,19 +139,33 @@ __device__ __forceinline__ uint32_t rank_top_bits(const uint32_t (&kk)[N], uint3
     return T;
 }
 
+// rank_top_bits of the total (<= 64 N) keys compacted at the front of buf (zero keys
+// count for nothing: every candidate is at least 2^12).
+template <int N>
+__device__ __forceinline__ uint32_t rank_top_bits_buf(const uint32_t *buf, uint32_t total,
+                                                      uint32_t m, int lane) {
+    uint32_t kk[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) kk[e] = (uint32_t)lane + 64u * e < total ? buf[lane + 64 * e] : 0u;
+    return rank_top_bits(kk, m);
+}
+
 // rank_top_bits of the wave's 1024 sampled keys, searched over fewer keys: with L the
-// same search over the 64 lane maxima (m <= 64), at least m keys are >= L, so the
-// m-th largest key is too, and every count the search compares with m is the same over
-// the keys >= L as over all of them (below L both are >= m).  When at most 128 keys
-// are >= L they are compacted into buf (this wave's 128 words of LDS) and searched two
-// a lane; otherwise all 16 a lane are.
+// same search over the two largest keys of each lane (m <= 128), at least m keys are
+// >= L, so the m-th largest key is too, and every count the search compares with m is
+// the same over the keys >= L as over all of them (below L both are >= m).  When at
+// most 256 keys are >= L they are compacted into buf (this wave's 1024 words of LDS)
+// and searched one to four a lane; otherwise all 16 a lane are.
 __device__ __forceinline__ uint32_t sample_quantile(const uint32_t (&kk)[16], uint32_t m,
                                                     int lane, uint32_t *buf) {
-    if (m > 64u) return rank_top_bits(kk, m);
-    uint32_t mx[1] = {kk[0]};
+    if (m > 128u) return rank_top_bits(kk, m);
+    uint32_t top[2] = {0u, 0u};  // the lane's largest and second largest key
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx[0] = max(mx[0], kk[e]);
-    const uint32_t L = rank_top_bits(mx, m);
+    for (int e = 0; e < 16; ++e) {
+        top[1] = max(top[1], min(top[0], kk[e]));
+        top[0] = max(top[0], kk[e]);
+    }
+    const uint32_t L = rank_top_bits(top, m);
     uint32_t c = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) c += kk[e] >= L;
@@ -157,14 +176,14 @@ __device__ __forceinline__ uint32_t sample_quantile(const uint32_t (&kk)[16], ui
         if (lane >= o) inc += t;
     }
     const uint32_t total = (uint32_t)__shfl((int)inc, 63, 64);
-    if (total > 128u) return rank_top_bits(kk, m);
+    if (total > 256u) return rank_top_bits(kk, m);
     uint32_t pos = inc - c;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         if (kk[e] >= L) buf[pos++] = kk[e];
-    const uint32_t two[2] = {(uint32_t)lane < total ? buf[lane] : 0u,
-                             (uint32_t)lane + 64u < total ? buf[lane + 64] : 0u};
-    return rank_top_bits(two, m);
+    if (total <= 64u) return rank_top_bits_buf<1>(buf, total, m, lane);
+    if (total <= 128u) return rank_top_bits_buf<2>(buf, total, m, lane);
+    return rank_top_bits_buf<4>(buf, total, m, lane);
 }
 
 // la: the head's A operand halves [K-block][lane][QS] (8 bytes, as in the records);
@@ -175,7 +194,8 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
                                                   int nplanes, int nkb, const uint32_t *pl,
                                                   const uint4 (&first)[kSamplePer],
                                                   const uint2 *la, const float *C,
-                                                  const float *S, ScanMeta *meta) {
+                                                  const float *S, uint32_t *tk,
+                                                  ScanMeta *meta) {
     constexpr int kST = kSampleWords * 32;  // sampled tokens per query
     // the staged words and, once they are used, the sampled keys share one buffer
     __shared__ __align__(16) uint32_t sbuf[kSamplePlanes * kSampleWords];
@@ -250,7 +270,10 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             for (int e = 0; e < kPerLane; ++e) kk[e] = skey[gq][lane + 64 * e];
             // the wave's own row of skey, now in registers, holds the compacted keys
             const uint32_t T = m > 0u ? sample_quantile(kk, m, lane, skey[gq]) : 0u;
-            if (lane == 0) meta->tkey[4 * set + gq] = T;
+            if (lane == 0) {
+                meta->tkey[4 * set + gq] = T;
+                tk[4 * set + gq] = T;
+            }
         }
     }
 }
@@ -316,6 +339,8 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     __shared__ uint32_t pl[kMaxPlanesPerHead];
     __shared__ double wt[NQ][kMaxPlanesPerHead];
     __shared__ double red[NQ][kD];
+    __shared__ double amx[NQ][kD];
+    __shared__ double csum[NQ];
     __shared__ double inv_unit[NQ];
     __shared__ double unit[NQ];
     __shared__ uint2 la[kMaxKBlocks * 64 * QS];  // A operand halves, as in the records
@@ -353,6 +378,7 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
             const double qv = (double)in.q[g];
             for (int j = 0; j < t; ++j) wt[g][o + j] = (qv * s) * (double)(8 >> j);
             red[g][c] = qv * (z + s * hm);  // this channel's share of C_g
+            amx[g][c] = t > 0 ? fabs((qv * s) * 8.0) : 0.0;  // its largest |weight|
         }
     }
     __syncthreads();
@@ -361,20 +387,20 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     if (k > 0)
         sample_issue(planes + (size_t)h * kMaxPlanesPerHead * word_stride, (n + 31) >> 5,
                      word_stride, pl, 0, min(nplanes, kSamplePlanes), first);
-    for (int s2 = kD / 2; s2 > 0; s2 >>= 1) {  // C_g: fixed-order tree sum over channels
-        if (tid < s2) {
-#pragma unroll
-            for (int g = 0; g < NQ; ++g) red[g][tid] += red[g][tid + s2];
-        }
-        __syncthreads();
-    }
-    // weight unit of each query: one wave per query
+    // C_g (a sum over the channels) and the weight unit of each query (from the largest
+    // |weight|): wave v takes queries v, v + 4.  Lane l first adds channels l and l + 64,
+    // then a butterfly over the lanes halves the distance each step, so lane 0 adds the
+    // same pairs in the same order as a halving tree over the 128 channels.
     for (int g = tid >> 6; g < NQ; g += 4) {
-        double mx = 0.0;
-        for (int p = lane; p < nplanes; p += 64) mx = fmax(mx, fabs(wt[g][p]));
+        double sum = red[g][lane] + red[g][lane + 64];
+        double mx = fmax(amx[g][lane], amx[g][lane + 64]);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+        for (int o = 32; o > 0; o >>= 1) {
+            sum += __shfl_xor(sum, o, 64);
+            mx = fmax(mx, __shfl_xor(mx, o, 64));
+        }
         if (lane == 0) {
+            csum[g] = sum;
             int e = 0;
             frexp(mx, &e);  // mx < 2^e
             unit[g] = mx > 0.0 ? ldexp(1.0, e - 30) : 1.0;
@@ -385,19 +411,39 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     __syncthreads();
     // each weight as an integer count of its query's unit, biased by 128 (1 + 256 +
     // 65536) so that its signed base-256 digits are plain bytes (weight_byte); written
-    // over the weight it comes from
+    // over the weight it comes from.  The same pass sums, per query, |M| and
+    // |D0 + 256 D1| of M's digits (the part of a weight the filter's integer test does
+    // not see): integer sums, exact in any order.  Wave v takes queries v, v + 4.
     long long(*Mu)[kMaxPlanesPerHead] = reinterpret_cast<long long(*)[kMaxPlanesPerHead]>(wt);
-    for (int e = tid; e < NQ * nplanes; e += 256) {
-        const int g = e / nplanes, p = e - g * nplanes;
-        Mu[g][p] = (g < G ? llrint(wt[g][p] * inv_unit[g]) : 0LL) + kDigitBias;
+    __shared__ double rb[NQ], mabs[NQ];
+    for (int g = tid >> 6; g < NQ; g += 4) {
+        long long r = 0, a = 0;
+        for (int p = lane; p < nplanes; p += 64) {
+            const long long u = (g < G ? llrint(wt[g][p] * inv_unit[g]) : 0LL) + kDigitBias;
+            Mu[g][p] = u;
+            const int d0 = (int)(int8_t)(uint8_t)weight_byte(u, 0);
+            const int d1 = (int)(int8_t)(uint8_t)weight_byte(u, 1);
+            const int dl = d0 + 256 * d1;
+            r += dl < 0 ? -dl : dl;
+            a += u >= kDigitBias ? u - kDigitBias : kDigitBias - u;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            r += __shfl_xor(r, o, 64);
+            a += __shfl_xor(a, o, 64);
+        }
+        if (lane == 0) {
+            rb[g] = (double)r;
+            mabs[g] = (double)a;
+        }
     }
     for (int p = tid; p < nplanes; p += 256) meta->plane[p] = pl[p];
     if (tid < FATHOM_MAX_G) {
-        meta->C[tid] = tid < G ? (float)red[tid][0] : 0.0f;
+        meta->C[tid] = tid < G ? (float)csum[tid] : 0.0f;
         meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
     }
     if (tid < NQ) {
-        cf[tid] = tid < G ? (float)red[tid][0] : 0.0f;
+        cf[tid] = tid < G ? (float)csum[tid] : 0.0f;
         sf[tid] = tid < G ? (float)unit[tid] : 0.0f;
     }
     if (tid == 0) {
@@ -442,34 +488,13 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         if (tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
         return;
     }
-    // per query: sum over the planes of |M| and of |D0 + 256 D1| of M's digits (the
-    // part of a weight the filter's integer test does not see), exact in fp64
-    __shared__ double rb[NQ], mabs[NQ];
-    for (int g = tid >> 6; g < NQ; g += 4) {
-        double r = 0.0, a = 0.0;
-        for (int p = lane; p < nplanes; p += 64) {
-            const long long u = Mu[g][p];
-            const int d0 = (int)(int8_t)(uint8_t)weight_byte(u, 0);
-            const int d1 = (int)(int8_t)(uint8_t)weight_byte(u, 1);
-            r += fabs((double)(d0 + 256 * d1));
-            a += fabs((double)(u - kDigitBias));
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            r += __shfl_xor(r, o, 64);
-            a += __shfl_xor(a, o, 64);
-        }
-        if (lane == 0) {
-            rb[g] = r;
-            mabs[g] = a;
-        }
-    }
+    __shared__ uint32_t tk[NQ];
     sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
-                          meta);
+                          tk, meta);
     __syncthreads();  // the thresholds and the sums are complete
     if (tid < NQ * 8) {
         const int g = tid >> 3, m = tid & 7;
-        meta->xthr[g][m] = filter_threshold(g < G, meta->tkey[g], cf[g], sf[g], rb[g], mabs[g], m);
+        meta->xthr[g][m] = filter_threshold(g < G, tk[g], cf[g], sf[g], rb[g], mabs[g], m);
     }
     if (tid >= NQ * 8 && tid < FATHOM_MAX_G * 8) meta->xthr[tid >> 3][tid & 7] = 0;
 }

@@ -109,6 +109,52 @@ def test_scan_topk_matches_full_scan(H, G, n, k, kind):
         assert cnt.max() <= n // 8
 
 
+TKEY_OFFSET = 16 + 2 * 32   # int32 x4, C[8], S[8], then tkey[8]
+
+
+def _order_key(v):
+    """The select's key of an fp32 score: unsigned order equals the scores' order."""
+    b = np.asarray(v, np.float32).view(np.uint32)
+    return np.where(b & 0x80000000, ~b, b ^ 0x80000000).astype(np.uint32)
+
+
+@pytest.mark.parametrize("H,G,n,k,kind", [
+    (2, 4, 32768, 512, "plan92"),     # m = 53: the two-stage search
+    (2, 4, 32768, 512, "b512"),
+    (1, 8, 9000, 300, "plan92"),      # m = 79, two query sets
+    (1, 4, 70000, 2000, "random"),    # m = 71, a ragged last sample run
+    (1, 5, 40000, 16384, "plan92"),   # m = 536 > 128: every key searched
+    (3, 4, 5000, 64, "b0"),           # m = 48, every score equal
+])
+def test_sample_threshold_is_the_sampled_quantile(H, G, n, k, kind):
+    """Each query's threshold key is the m-th largest order key of its scores at the
+    sampled tokens (m = the sample rank, scores as the full scan computes them), with
+    its low 12 bits cleared."""
+    torch = torch_cuda()
+    print(f"[sample threshold] H={H} G={G} n={n} k={k} {kind}", flush=True)
+    keys, q, _, _ = inputs(103, H, G, n)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    depth = _depth(kind, st, q_t, H, n)
+    full = F.fathom_scan(st, q_t, depth).cpu().numpy()
+    ws = F.scan_topk_workspace(st, G, k, "cuda")
+    F.fathom_scan_topk(st, q_t, depth, k, ws=ws)
+    torch.cuda.synchronize()
+    raw = ws[:H * META_BYTES].cpu().numpy().view(np.uint8).reshape(H, META_BYTES)
+    tkey = raw[:, TKEY_OFFSET:TKEY_OFFSET + 32].copy().view(np.uint32)[:, :G]
+    W = (n + 31) // 32
+    toks = (_sample_words(W)[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    toks = toks[toks < n]
+    S = toks.size
+    x = 0.5 * (5.0 + np.sqrt(25.0 + 4.0 * k * S / n))
+    m = int(np.ceil(x * x))
+    assert m <= S
+    for h in range(H):
+        for g in range(G):
+            srt = np.sort(_order_key(full[h, g, toks]))[::-1]
+            assert tkey[h, g] == (srt[m - 1] & np.uint32(0xFFFFF000)), (h, g)
+
+
 def _boost_sampled_tokens(keys, q):
     """Make the tokens the threshold sample reads the best of their rows, so that the
     sampled quantile sits far above the row's k-th score and few tokens clear it."""
