@@ -256,8 +256,9 @@ __device__ __noinline__ void rescore_word_call(const FilterArgs &fa, int h, int 
 
 // kExplicit: input entries carry their own int32 index (candidate levels); otherwise
 // the index is the position in the row.  kCandOut: write (value, index) candidates
-// (at column chunk*kk of the output row) instead of final indices.
-template <bool kExplicit, bool kCandOut, bool kMasked>
+// (at column chunk*kk of the output row) instead of final indices.  kDirect (with
+// kMasked, a row of one chunk): the select runs alone, without the lean select.
+template <bool kExplicit, bool kCandOut, bool kMasked, bool kDirect = false>
 __device__ __forceinline__ void select_chunk(
     int64_t row, int chunk, const float *__restrict__ vals, const int32_t *__restrict__ in_idx,
     int64_t row_len, int64_t in_stride, int k, float *__restrict__ out_val,
@@ -284,7 +285,26 @@ __device__ __forceinline__ void select_chunk(
         const ScanMeta *meta =
             reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
         const int word = chunk * kThreads + tid;
-        if (needs_rescore(meta, g, k)) {
+        if constexpr (!kCandOut && kDirect) {
+            // Run alone (a row of one chunk), the select itself counts the kept keys
+            // that clear the row's threshold exactly (otherwise the lean select did).
+            bool rescore = meta->cnt[g] < (uint32_t)k || ((meta->ovf >> g) & 1u);
+            if (!rescore) {
+                const uint32_t lenmask = vmask;
+                vmask = load_kept(reinterpret_cast<const int2 *>(vals + row * fa.cstride),
+                                  fa.masks + row * fa.W, word, fa.W, vmask, meta->C[g],
+                                  meta->S[g], key);
+                const uint32_t tkey = meta->tkey[g];
+                uint32_t nex = 0u;
+#pragma unroll
+                for (int e = 0; e < kEPT; ++e) nex += ((vmask >> e) & 1u) && key[e] >= tkey;
+                uint32_t total;
+                block_excl_scan(nex, scan_sh, &total);
+                rescore = total < (uint32_t)k;  // a winner may be missing
+                if (rescore) vmask = lenmask;
+            }
+            if (rescore) rescore_word(fa, h, g, word, vmask, hist, key);
+        } else if (needs_rescore(meta, g, k)) {
             if constexpr (kCandOut)
                 rescore_word_call(fa, h, g, word, vmask, hist, key);
             else
@@ -504,42 +524,56 @@ __global__ __launch_bounds__(kThreads, kCandOut ? 8 : 1) void k_topk_redo(
 }
 
 // ---------------------------------------------------------------------------------
-// Filtered select: one 256-thread workgroup per row chunk ranks the chunk's kept
-// candidates in LDS (up to kSelCap of them), so that every row of a decode step runs
-// at once.  A chunk with more candidates, or of a row that kept fewer than k tokens in
-// total, is appended to the redo list for the full select above.
+// Filtered select: one workgroup per row chunk ranks the chunk's kept candidates in
+// LDS (up to kSelCap of them).  With many rows (a batched step) a workgroup has 256
+// threads, so that every row runs at once, and a chunk with more candidates, of a row
+// that kept fewer than k tokens, or of a one-chunk row of which fewer than k candidates
+// clear the threshold exactly, is appended to the redo list for the full select above.
+// With few rows of one chunk (one layer of a decode step: kDirect) a workgroup has 1024
+// threads and finishes such a row itself with the full select, so that no second
+// launch follows.
 // ---------------------------------------------------------------------------------
-constexpr int kSelThreads = 256;
-constexpr int kSelCap = 3840;  // with 8 KB of histogram: 5 workgroups per CU
-constexpr int kSelWords = kTopkChunk / 32 / kSelThreads;  // mask words per thread: 4
-static_assert(kSelWords == 4, "two threads per 8-word block");
+constexpr int kSelCap = 3840;   // with 8 KB of histogram: 5 workgroups of 256 a CU
+constexpr int kSelBins = 2048;  // 11-bit digits: passes over bits 31-21, 20-10, 9-0
 
-// Exclusive prefix over the 256 threads with one barrier: each thread adds the totals
-// of the waves before its own.  sh (4 words) must not be rewritten before every thread
-// has read it: callers alternate between two.
-__device__ __forceinline__ uint32_t block256_prefix(uint32_t v, uint32_t *sh, uint32_t *total) {
+// Exclusive prefix over the NT threads with one barrier: each thread adds the totals
+// of the waves before its own.  sh (NT / 64 words) must not be rewritten before every
+// thread has read it: callers alternate between two.
+template <int NT>
+__device__ __forceinline__ uint32_t block_prefix1(uint32_t v, uint32_t *sh, uint32_t *total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t inc = wave_incl_scan(v, lane);
     if (lane == 63) sh[wave] = inc;
     __syncthreads();
-    const uint32_t a = sh[0], b = sh[1], c = sh[2], d = sh[3];
-    *total = a + b + c + d;
-    return inc - v + (wave > 0 ? a : 0u) + (wave > 1 ? b : 0u) + (wave > 2 ? c : 0u);
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t t = sh[w];
+        before += w < wave ? t : 0u;
+        all += t;
+    }
+    *total = all;
+    return inc - v + before;
 }
 
-constexpr int kSelBins = 2048;  // 11-bit digits: passes over bits 31-21, 20-10, 9-0
-
-template <bool kCandOut>
-__global__ __launch_bounds__(kSelThreads) void k_select_kept(
-    const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
+// The lean select's body for NT threads (256, or 1024 with kDirect).
+template <bool kCandOut, bool kDirect, int NT>
+__device__ __forceinline__ void select_kept(
+    const float *__restrict__ cand, int64_t n, int row0, int k, const FilterArgs &fa,
     uint32_t *__restrict__ list, float *__restrict__ out_val, int32_t *__restrict__ out_idx,
     int64_t out_stride) {
+    constexpr int NW = NT / 64;                 // waves
+    constexpr int WPT = kTopkChunk / 32 / NT;   // mask words a thread: 4 or 1
+    constexpr int BPT = kSelBins / NT;          // histogram bins a thread: 8 or 2
+    constexpr int kPer = (kSelCap + NT - 1) / NT;
+    static_assert(WPT == 4 || WPT == 1, "two threads, or eight, per 8-word block");
+    static_assert(!kDirect || (NT == kThreads && !kCandOut), "the direct select: one chunk");
     __shared__ uint32_t skey[kSelCap];
     __shared__ uint16_t soff[kSelCap];
     __shared__ uint32_t hist[kSelBins];
-    __shared__ uint32_t sh[2][4];
+    __shared__ uint32_t sh[2][NW];
     __shared__ uint32_t pick[2][3];
-    __shared__ uint32_t smm[3][4];  // per-wave min and max key, count clearing the threshold
+    __shared__ uint32_t smm[3][NW];  // per-wave min and max key, count clearing the threshold
     const int tid = threadIdx.x, chunk = blockIdx.x, nch = gridDim.x;
     const int64_t row = (int64_t)row0 + blockIdx.y;
     const int64_t start = (int64_t)chunk * kTopkChunk;
@@ -548,54 +582,75 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     ScanMeta *meta0 = reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws));
     ScanMeta *meta =
         reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws) + (size_t)h * kMetaBytes);
-    // this thread's 4 mask words: chunk words 4 tid .. 4 tid + 3
-    const int wl = kSelWords * tid;
+    // a row chunk that needs the full select: listed for the redo kernel, or (kDirect)
+    // finished here by all NT threads (the condition is the same for every thread)
+    auto hand_over = [&]() {
+        if constexpr (kDirect)
+            select_chunk<false, false, true, true>(row, 0, cand, nullptr, n, n, k, nullptr,
+                                                   out_idx, 0, fa);
+        else if (tid == 0)
+            list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
+    };
+    // this thread's WPT mask words: chunk words WPT tid .. WPT tid + WPT - 1
+    const int wl = WPT * tid;
     const int64_t wg = (int64_t)chunk * (kTopkChunk / 32) + wl;
-    uint32_t mk[kSelWords], c[kSelWords];
+    uint32_t mk[WPT], c[WPT];
     // every load unconditional (a word past the row reads the row's last word, then
     // masked off), so that they are all in flight together
 #pragma unroll
-    for (int j = 0; j < kSelWords; ++j)
+    for (int j = 0; j < WPT; ++j)
         mk[j] = fa.masks[row * fa.W + min(wg + j, (int64_t)fa.W - 1)];
     const uint32_t kept = meta->cnt[g];
 #pragma unroll
-    for (int j = 0; j < kSelWords; ++j) {
+    for (int j = 0; j < WPT; ++j) {
         const int t0 = 32 * (wl + j);  // first chunk token of the word
         const uint32_t lm = t0 >= len ? 0u : (len - t0 >= 32 ? 0xFFFFFFFFu : (1u << (len - t0)) - 1u);
         mk[j] = wg + j < fa.W ? mk[j] & lm : 0u;
     }
     // the row is rescored by the full select
     const bool full = kept < (uint32_t)k || ((meta->ovf >> g) & 1u);
+    uint32_t csum = 0u;
 #pragma unroll
-    for (int j = 0; j < kSelWords; ++j) {
+    for (int j = 0; j < WPT; ++j) {
         if (full) mk[j] = 0u;
         c[j] = (uint32_t)__popc(mk[j]);
+        csum += c[j];
     }
-    for (int b = tid; b < kSelBins; b += kSelThreads) hist[b] = 0u;
+    for (int b = tid; b < kSelBins; b += NT) hist[b] = 0u;
     uint32_t C;
-    const uint32_t pos0 = block256_prefix(c[0] + c[1] + c[2] + c[3], sh[0], &C);
+    const uint32_t pos0 = block_prefix1<NT>(csum, sh[0], &C);
     if (full || C > (uint32_t)kSelCap) {
-        if (tid == 0) list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
+        hand_over();
         return;
     }
-    // Stored order of a block's kept scores: words 0,2,4,6,1,3,5,7.  Thread 2b holds
-    // words 0-3 of block b, thread 2b+1 words 4-7.
-    {
+    // Stored order of a block's kept scores: words 0,2,4,6,1,3,5,7; off[j]: the kept
+    // tokens of the block stored before those of word wl + j.
+    uint32_t off[WPT];
+    if constexpr (WPT == 4) {  // thread 2b: words 0-3 of block b, thread 2b+1 words 4-7
         const uint32_t E = c[0] + c[2], O = c[1] + c[3];
         const uint32_t pE = (uint32_t)__shfl_xor((int)E, 1, 64);
         const uint32_t pO = (uint32_t)__shfl_xor((int)O, 1, 64);
         const bool odd = tid & 1;
         const uint32_t eb = odd ? pE : 0u, ob = odd ? pO : 0u, te = E + pE;
-        uint32_t off[kSelWords];
         off[0] = eb;
         off[2] = eb + c[0];
         off[1] = te + ob;
         off[3] = te + ob + c[1];
-        // first the record index of each kept token in the row, in token order ...
+    } else {  // thread 8b + j: word j of block b
+        const int j = tid & 7, oj = (j & 1) * 4 + (j >> 1);  // its place in the order
+        uint32_t pre = 0u;
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+            const uint32_t co = (uint32_t)__shfl((int)c[0], 2 * (o & 3) + (o >> 2), 8);
+            if (o < oj) pre += co;
+        }
+        off[0] = pre;
+    }
+    {   // first the record index of each kept token in the row, in token order ...
         const uint32_t blk = (uint32_t)((start + 32 * (int64_t)(wl & ~7)) / 2);
         uint32_t pos = pos0;
 #pragma unroll
-        for (int j = 0; j < kSelWords; ++j) {
+        for (int j = 0; j < WPT; ++j) {
             uint32_t m = mk[j], r = blk + off[j];
             while (m) {
                 const int b = __ffs(m) - 1;
@@ -607,14 +662,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         }
     }
     __syncthreads();
-    {   // ... then all the loads at once, each thread up to kSelCap / 256 of them; each
+    {   // ... then all the loads at once, each thread up to kSelCap / NT of them; each
         // record becomes the scan's exact score and its order key
-        constexpr int kPer = kSelCap / kSelThreads;
         const int2 *crow = reinterpret_cast<const int2 *>(cand + row * fa.cstride);
         int2 v[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            const int e = tid + kSelThreads * u;
+            const int e = tid + NT * u;
             v[u] = e < (int)C ? crow[skey[e]] : make_int2(0, 0);
         }
         const float Cg = meta->C[g], Sg = meta->S[g];
@@ -624,7 +678,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nex = 0u;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            const int e = tid + kSelThreads * u;
+            const int e = tid + NT * u;
             if (e < (int)C) {
                 const uint32_t key = order_key(record_score(v[u], soff[e] & 7, Cg, Sg));
                 skey[e] = key;
@@ -646,13 +700,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         }
     }
     __syncthreads();
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     {   // the candidates clearing the threshold exactly: with fewer than k a winner may be
         // missing (rows of one chunk go to the full select; a row of several chunks is
         // judged on its sum over chunks by the redo kernel)
-        const uint32_t nex = smm[2][0] + smm[2][1] + smm[2][2] + smm[2][3];
-        if (tid == 0) atomicAdd(&meta->cnt_exact[g], nex);
+        uint32_t nex = 0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            kmin = min(kmin, smm[0][w]);
+            kmax = max(kmax, smm[1][w]);
+            nex += smm[2][w];
+        }
+        if (!kDirect && tid == 0) atomicAdd(&meta->cnt_exact[g], nex);
         if (!kCandOut && nex < (uint32_t)k) {
-            if (tid == 0) list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
+            hand_over();
             return;
         }
     }
@@ -667,44 +728,42 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     // radix select starts below the bits all of them share (from their min and max), so
     // that its first histogram spreads them over many bins instead of a few contended
     // ones.  Digits of up to 11 bits.
-    const uint32_t kmin = min(min(smm[0][0], smm[0][1]), min(smm[0][2], smm[0][3]));
-    const uint32_t kmax = max(max(smm[1][0], smm[1][1]), max(smm[1][2], smm[1][3]));
     const uint32_t diff = kmin ^ kmax;
     int shift = diff == 0u ? 0 : 32 - __clz(diff);  // bits >= shift: the same in every key
     uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift), need = (uint32_t)kr;
     for (int pass = 0; shift > 0; ++pass) {
         const int sd = max(0, shift - 11), width = shift - sd, nb = 1 << width;
-        for (int i = tid; i < (int)C; i += kSelThreads) {
+        for (int i = tid; i < (int)C; i += NT) {
             const uint32_t key = skey[i];
             if (((uint64_t)key >> shift) == prefix) atomicAdd(&hist[(key >> sd) & (nb - 1)], 1u);
         }
         __syncthreads();
-        // thread t owns bins nb-1-8t .. nb-8-8t (largest first)
-        uint32_t c8[8], local = 0u;
+        // thread t owns bins nb-1-BPT t .. nb-BPT-BPT t (largest first)
+        uint32_t cb[BPT], local = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int bin = nb - 1 - (8 * tid + e);
-            c8[e] = bin >= 0 ? hist[bin] : 0u;
-            local += c8[e];
+        for (int e = 0; e < BPT; ++e) {
+            const int bin = nb - 1 - (BPT * tid + e);
+            cb[e] = bin >= 0 ? hist[bin] : 0u;
+            local += cb[e];
         }
         uint32_t tot;
-        const uint32_t above = block256_prefix(local, sh[(pass + 1) & 1], &tot);
+        const uint32_t above = block_prefix1<NT>(local, sh[(pass + 1) & 1], &tot);
         if (above < need && need <= above + local) {
             uint32_t cum = above;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (cum < need && need <= cum + c8[e]) {
-                    pick[pass & 1][0] = (uint32_t)(nb - 1 - (8 * tid + e));
+            for (int e = 0; e < BPT; ++e) {
+                if (cum < need && need <= cum + cb[e]) {
+                    pick[pass & 1][0] = (uint32_t)(nb - 1 - (BPT * tid + e));
                     pick[pass & 1][1] = cum;
-                    pick[pass & 1][2] = c8[e];
+                    pick[pass & 1][2] = cb[e];
                 }
-                cum += c8[e];
+                cum += cb[e];
             }
         }
         // every thread has read hist: clear it for the next pass
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int bin = nb - 1 - (8 * tid + e);
+        for (int e = 0; e < BPT; ++e) {
+            const int bin = nb - 1 - (BPT * tid + e);
             if (bin >= 0) hist[bin] = 0u;
         }
         __syncthreads();
@@ -716,7 +775,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     }
     // ordered output: greater keys all win; of the keys equal to the prefix, the `need`
     // first in token order
-    const int seg = ((int)C + kSelThreads - 1) / kSelThreads;
+    const int seg = ((int)C + NT - 1) / NT;
     const int b0 = min((int)C, tid * seg), b1 = min((int)C, b0 + seg);
     uint32_t gt = 0u, eq = 0u;
     for (int i = b0; i < b1; ++i) {
@@ -725,7 +784,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
         eq += kv == prefix;
     }
     uint32_t tot;
-    const uint32_t before = block256_prefix(gt | (eq << 16), sh[1], &tot);
+    const uint32_t before = block_prefix1<NT>(gt | (eq << 16), sh[1], &tot);
     const uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
     const uint32_t eq_won_before = min(eqb, need);
     uint32_t take = min(need - eq_won_before, eq);
@@ -753,6 +812,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select_kept(
     if (kCandOut) fill_slots(out_val, out_idx, obase, kr, min(k, len));
 }
 
+template <bool kCandOut>
+__global__ __launch_bounds__(256) void k_select_kept(
+    const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
+    uint32_t *__restrict__ list, float *__restrict__ out_val, int32_t *__restrict__ out_idx,
+    int64_t out_stride) {
+    select_kept<kCandOut, false, 256>(cand, n, row0, k, fa, list, out_val, out_idx, out_stride);
+}
+
+// Like the final select it may use 128 VGPRs, so that it needs no scratch.
+__global__ __launch_bounds__(kThreads, 1) void k_select_direct(
+    const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
+    int32_t *__restrict__ out_idx) {
+    select_kept<false, true, kThreads>(cand, n, row0, k, fa, nullptr, nullptr, out_idx, 0);
+}
+
 template <bool kExplicit, bool kCandOut>
 void launch_level(const float *vals, const int32_t *in_idx, int64_t len, int64_t in_stride,
                   int R, int k, float *out_val, int32_t *out_idx, int64_t out_stride,
@@ -775,7 +849,7 @@ void launch_filtered_level(const float *cand, int64_t n, int R, int k, const Fil
     const int nch = (int)((n + kTopkChunk - 1) / kTopkChunk);
     for (int r0 = 0; r0 < R; r0 += 65535) {
         const int rows = std::min(65535, R - r0);
-        hipLaunchKernelGGL(k_select_kept<kCandOut>, dim3(nch, rows), dim3(kSelThreads), 0, s,
+        hipLaunchKernelGGL(k_select_kept<kCandOut>, dim3(nch, rows), dim3(256), 0, s,
                            cand, n, r0, k, fa, list, out_val, out_idx, out_stride);
     }
     const int grid = (int)std::min<int64_t>((int64_t)R * nch, kRedoGrid);
@@ -783,13 +857,22 @@ void launch_filtered_level(const float *cand, int64_t n, int R, int k, const Fil
                        out_val, out_idx, out_stride, fa, list, nch);
 }
 
+// Rows of one chunk of a filtered select run k_select_direct when there are at most this
+// many (one row a CU); more rows run the lean 256-thread select, then the full select
+// over the chunks it hands over.
+constexpr int kDirectRows = 256;
+
 // Levels over R rows of n entries; the first reads either plain scores or (with a redo
 // list) the filtering scan's candidates.
 hipError_t run_levels(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
                       hipStream_t s, const FilterArgs &fa, uint32_t *list) {
     const TopkLevels L = topk_levels(n, k);
     if (L.n_levels == 0) {
-        if (list)
+        if (list && R <= kDirectRows) {
+            for (int r0 = 0; r0 < R; r0 += 65535)
+                hipLaunchKernelGGL(k_select_direct, dim3(1, std::min(65535, R - r0)),
+                                   dim3(kThreads), 0, s, scores, (int64_t)n, r0, k, fa, idx);
+        } else if (list)
             launch_filtered_level<false>(scores, n, R, k, fa, list, nullptr, idx, 0, s);
         else
             launch_level<false, false>(scores, nullptr, n, n, R, k, nullptr, idx, 0, s);

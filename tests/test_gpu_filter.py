@@ -94,6 +94,8 @@ def _run(keys, q, k, kind):
     (2, 4, 3000, 50, "b0"),           # every score equal: ties to the lower index
     (2, 4, 9000, 300, "b512"),
     (1, 5, 40000, 16384, "plan92"),   # the largest k with several chunks
+    (130, 4, 2048, 64, "plan92"),     # more than 512 one-chunk rows: the lean select
+    (130, 4, 2048, 64, "b512"),       # ... every row rescored by the full select after it
 ])
 def test_scan_topk_matches_full_scan(H, G, n, k, kind):
     print(f"[scan_topk] H={H} G={G} n={n} k={k} {kind}", flush=True)
@@ -170,7 +172,7 @@ def _boost_sampled_tokens(keys, q):
 
 
 @pytest.mark.parametrize("H,G,n,k", [(2, 4, 32768, 512), (1, 2, 70000, 512),
-                                     (1, 8, 9000, 300)])
+                                     (1, 8, 9000, 300), (65, 8, 8192, 64)])
 def test_scan_topk_repairs_rows_that_kept_too_few(H, G, n, k):
     print(f"[scan_topk repair] H={H} G={G} n={n} k={k}", flush=True)
     keys, q, _, _ = inputs(101, H, G, n)
