@@ -2,17 +2,21 @@
 // attention over just those k tokens; reading the values for k tokens).
 //
 // One workgroup per (head, query).  A wave works on 8 winner rows at once, 8 lanes per
-// row, 16 channels (32 bytes of K and of V) per lane; each of the 32 row slots of the
-// workgroup keeps an online softmax (running max, running sum, 128-wide output), and
-// the slots are merged through LDS at the end.  Rows are gathered straight from HBM or
-// from pinned host memory; the gather is memory-bound, so there is no matrix-core use.
+// row, 16 channels (32 bytes of K and of V) per lane; each of the NT / 8 row slots keeps
+// an online softmax (running max, running sum, 128-wide output) over its rows, taken
+// four at a time with every load of the four in flight together.  The slots are merged
+// through LDS at the end in two levels (NT / 128 groups of 16 slots, then the groups).
+// Rows are gathered straight from HBM or from pinned host memory; the gather is
+// memory-bound, so there is no matrix-core use.  With few rows (one layer of a decode
+// step) a workgroup has 1024 threads, so that the 512 winners of a row need one round of
+// index loads and one of K/V loads; with many (a batched step) it has 256, so that
+// several workgroups share a CU and keep HBM busy.
 #include "common.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kSlots = kAttnThreads / 8;  // 32 rows in flight per workgroup
+constexpr int kSmallRows = 256;  // (head, query) rows up to which workgroups have 1024 threads
 
 __device__ __forceinline__ void unpack8(const uint4 u, float *f) {
     f[0] = bf16_bits_to_float(u.x & 0xFFFFu);
@@ -25,12 +29,18 @@ __device__ __forceinline__ void unpack8(const uint4 u, float *f) {
     f[7] = __uint_as_float(u.w & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
+template <int NT>
+__global__ __launch_bounds__(NT) void k_sparse_attn(
     const float *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
     float sm_scale, uint16_t *__restrict__ out) {
+    constexpr int kSlots = NT / 8;              // rows in flight per workgroup
+    constexpr int kParts = NT / kD;             // groups of slots in the merge
+    constexpr int kSlotsPerPart = kSlots / kParts;  // 16
     __shared__ float so[kSlots][kD + 1];
     __shared__ float smax[kSlots], ssum[kSlots];
+    __shared__ float po[kParts][kD];
+    __shared__ float pmax[kParts], psum[kParts];
     const int hg = blockIdx.x, h = hg / G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = wave * 8 + (lane >> 3), sub = lane & 7;
@@ -55,7 +65,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     const uint16_t *Kh = K + (size_t)h * n * kD + sub * 16;
     const uint16_t *Vh = V + (size_t)h * n * kD + sub * 16;
     // four rows a slot at a time: their indices, then their K and V pieces, are loaded
-    // together, so that each batch waits for two memory latencies instead of each row
+    // together (a row past k or out of range reads row 0 and is then skipped), so that
+    // each batch waits for two memory latencies instead of each row
     for (int r0 = slot; r0 < k; r0 += 4 * kSlots) {
         int row[4];
         bool ok[4];
@@ -68,9 +79,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
         uint4 kk[4][2], vv[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (!ok[u]) continue;
-            const uint4 *kp = reinterpret_cast<const uint4 *>(Kh + (size_t)row[u] * kD);
-            const uint4 *vp = reinterpret_cast<const uint4 *>(Vh + (size_t)row[u] * kD);
+            const size_t rr = ok[u] ? (size_t)row[u] : 0;
+            const uint4 *kp = reinterpret_cast<const uint4 *>(Kh + rr * kD);
+            const uint4 *vp = reinterpret_cast<const uint4 *>(Vh + rr * kD);
             kk[u][0] = kp[0];
             kk[u][1] = kp[1];
             vv[u][0] = vp[0];
@@ -107,14 +118,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
         ssum[slot] = l;
     }
     __syncthreads();
-    if (tid < kD) {
+    {   // group p of slots (p, p + kParts, ...): channel c's share of the output
+        const int c = tid & (kD - 1), p = tid >> 7;
         float M = -INFINITY;
-        for (int s2 = 0; s2 < kSlots; ++s2) M = fmaxf(M, smax[s2]);
+#pragma unroll
+        for (int j = 0; j < kSlotsPerPart; ++j) M = fmaxf(M, smax[p + kParts * j]);
         float L = 0.0f, O = 0.0f;
-        for (int s2 = 0; s2 < kSlots; ++s2) {
+#pragma unroll
+        for (int j = 0; j < kSlotsPerPart; ++j) {
+            const int s2 = p + kParts * j;
             const float f = smax[s2] == -INFINITY ? 0.0f : expf(smax[s2] - M);
             L += ssum[s2] * f;
-            O += so[s2][tid] * f;
+            O += so[s2][c] * f;
+        }
+        po[p][c] = O;
+        if (c == 0) {
+            pmax[p] = M;
+            psum[p] = L;
+        }
+    }
+    __syncthreads();
+    if (tid < kD) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) M = fmaxf(M, pmax[p]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) {
+            const float f = pmax[p] == -INFINITY ? 0.0f : expf(pmax[p] - M);
+            L += psum[p] * f;
+            O += po[p][tid] * f;
         }
         const float res = L > 0.0f ? O / L : 0.0f;
         out[(size_t)hg * kD + tid] = float_to_bf16_bits(res);
@@ -161,8 +194,12 @@ __global__ __launch_bounds__(256) void k_stream_runs(const char *__restrict__ sr
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_sparse_attn, dim3(H * G), dim3(kAttnThreads), 0, s, q, K, V, G, n,
-                       idx, k, sm_scale, out);
+    if (H * G <= kSmallRows)
+        hipLaunchKernelGGL(k_sparse_attn<1024>, dim3(H * G), dim3(1024), 0, s, q, K, V, G, n,
+                           idx, k, sm_scale, out);
+    else
+        hipLaunchKernelGGL(k_sparse_attn<256>, dim3(H * G), dim3(256), 0, s, q, K, V, G, n,
+                           idx, k, sm_scale, out);
     return hipGetLastError();
 }
 

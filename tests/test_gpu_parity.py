@@ -257,7 +257,9 @@ def test_topk_matches_oracle(R, n, k, dist):
 # attention
 # ---------------------------------------------------------------------------------
 @pytest.mark.parametrize("H,G,n,k", [(2, 4, 3000, 512), (1, 1, 4096, 64), (2, 3, 100, 100),
-                                     (1, 2, 50, 1), (3, 8, 2000, 77)])
+                                     (1, 2, 50, 1), (3, 8, 2000, 77),
+                                     (1, 2, 3000, 1300),   # several rounds of 512 rows a slot set
+                                     (70, 4, 600, 300)])   # more than 256 rows: 256-thread groups
 def test_sparse_attn_matches_oracle(H, G, n, k):
     torch = torch_cuda()
     keys, q, K, V = inputs(70, H, G, n)
