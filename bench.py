@@ -65,6 +65,9 @@ def parse():
                     help="skip the grouped-store lines (build, append, scan)")
     ap.add_argument("--accuracy-only", action="store_true",
                     help="run only the synthetic accuracy-per-byte sweep")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the per-layer decode passes (36 sequential 8-head steps) "
+                         "and print their line (for profiler runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --kernel: also run a 1 GiB streaming read and a 256 MiB "
                          "copy, whose byte counts scale the profiler's HBM counters")
@@ -132,6 +135,13 @@ def main():
     out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s: H={H} G={G} n={n} B={B} k={k}")
+
+    if args.decode_only:
+        per_layer, _, _ = decode_per_layer(F, st, q, K, V, B, k, sm_scale, dev, stream,
+                                           passes=max(5, min(args.steps, 20)), layers=H // 8)
+        print(json.dumps({"decode_per_layer": per_layer, "config": cfg.name,
+                          "budget_bits": B}), flush=True)
+        return
 
     if args.kernel:
         kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
@@ -222,22 +232,37 @@ def main():
     # ---------------- per-kernel times (cold caches between launches) ----------------
     kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
                         stream, reps=max(10, min(args.steps, 30)))
+    # A scan's algorithmic bytes are the planes it reads, B/8 bytes per key; what it
+    # writes (fp32 scores, or candidate records and kept masks) is the implementation's
+    # and is reported beside them, with the fraction it would give if counted.
     plane_bytes = B / 8 * n * H
     score_bytes = 4 * G * n * H
-    scan_bytes = plane_bytes + score_bytes
     scan_ms = kern["scan_ms"]
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    achieved = plane_bytes / (scan_ms * 1e-3) / 1e9
     roofline_full = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("scan_full"), "kernel": "k_scan_main<1,false,false>",
-                     "algorithmic_bytes_per_launch": int(scan_bytes),
+                     "algorithmic_bytes_per_launch": int(plane_bytes),
+                     "written_bytes_per_launch": int(score_bytes),
+                     "frac_counting_writes": round((plane_bytes + score_bytes) / (scan_ms * 1e-3)
+                                                   / 1e9 / HBM_PEAK_GBS, 4),
                      "timing": "fathom_scan alone, cold caches, mean of its own timed launches"}
+    # the specified design's scan: bit extraction on the vector ALUs, no matrix cores
+    ex_ms = kern.get("scan_extract_ms")
+    roofline_extract = None
+    if ex_ms:
+        gbs = plane_bytes / (ex_ms * 1e-3) / 1e9
+        roofline_extract = {"bound": "alu", "achieved_hbm_GBps": round(gbs, 1),
+                            "hbm_peak": HBM_PEAK_GBS, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "kernel": "k_scan_extract<4>", "ms_per_launch": round(ex_ms, 4),
+                            "algorithmic_bytes_per_launch": int(plane_bytes),
+                            "valu": load_counters("scan_extract"),
+                            "timing": "fathom_scan_extract alone, cold caches"}
     # the step's own kernels, timed live in the phase pass: the scan (filtering form) and
     # the attention; the roofline is the longer one's
     W = (n + 31) // 32
     live = {
-        "scan": ("k_scan_main<1,false,true>", "scan_filter",
-                 plane_bytes + 4 * kept_total + 4 * W * G * H),
+        "scan": ("k_scan_main<1,false,true>", "scan_filter", plane_bytes),
         "attention": ("k_sparse_attn", "attn", H * G * (k * (2 * 128 * 2 + 4) + 128 * 4 + 128 * 2)),
     }
     phase_rooflines = {}
@@ -248,6 +273,12 @@ def main():
                                  "traffic": load_traffic(tkey), "kernel": kname,
                                  "algorithmic_bytes_per_launch": int(nbytes),
                                  "ms_per_launch": phases[name]}
+    # the filtering scan's own writes: 8-byte candidate records and one mask word per
+    # 32 tokens of each row
+    fw = 8 * kept_total + 4 * W * G * H
+    phase_rooflines["scan"]["written_bytes_per_launch"] = int(fw)
+    phase_rooflines["scan"]["frac_counting_writes"] = round(
+        (plane_bytes + fw) / (phases["scan"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     dominant = max(live, key=lambda nm: phases[nm])
     roofline = dict(phase_rooflines[dominant])
     roofline["timing"] = (f"the step's longest kernel ({dominant}), mean over the "
@@ -278,6 +309,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "roofline_full_scan": roofline_full,
+        "roofline_scan_extract": roofline_extract,
         "step_is": "one fathom_step over all 36 x 8 (layer, KV head) pairs: the batched "
                    "form (36 sequences x 1 layer), not one sequence's token; per-layer "
                    "sequential decode is under decode_per_layer",
@@ -288,7 +320,7 @@ def main():
         "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
         "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
         "bytes_per_step": {"planes": int(plane_bytes),
-                           "candidate_scores_written": int(4 * H * G * parity["kept_per_row_mean"]),
+                           "candidate_records_written": int(8 * H * G * parity["kept_per_row_mean"]),
                            "kept_masks_written": int(H * G * ((n + 31) // 32) * 4),
                            "scores_written_by_full_scan": int(score_bytes),
                            "winner_rows": int(H * G * k * 512)},
@@ -457,7 +489,27 @@ TRAFFIC_FILES = {  # kernel -> (counter summary under profiles/, the source it w
     "scan_full": ("scan_traffic.json", "scan.hip"),
     "scan_filter": ("scan_filter_traffic.json", "scan.hip"),
     "attn": ("attn_traffic.json", "attn.hip"),
+    "scan_extract": ("scan_extract_counters.json", "scan_extract.hip"),
 }
+
+
+def load_counters(kernel):
+    """The instruction counters of a kernel from its committed rocprofv3 summary (a JSON
+    object), if the summary was taken on the current source of that kernel; else None."""
+    import hashlib
+    name, srcname = TRAFFIC_FILES[kernel]
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", srcname)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != digest:
+            return None
+        return rec.get("counters")
+    except Exception:
+        return None
 
 
 def load_traffic(kernel):
