@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--kernel", default=None,
                     choices=["plan", "scan_prepare", "scan", "topk", "attn", "scan_fixed136",
                              "scan_extract", "scan_topk", "scan_nibble", "scan_b512",
-                             "step_1m_host", "step_1m_hbm"],
+                             "step_1m_host", "step_1m_hbm", "scan_grouped"],
                     help="set up the workload, time only this kernel (for profiler runs)")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--no-host", action="store_true",
@@ -98,6 +98,9 @@ def main():
 
     if args.kernel in ("step_1m_host", "step_1m_hbm"):
         print(json.dumps(step_1m_kernel(args)), flush=True)
+        return
+    if args.kernel == "scan_grouped":
+        print(json.dumps(grouped_kernel(args)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]
@@ -739,6 +742,108 @@ def grouped_lines(args, kern):
     return res
 
 
+def grouped_store_1m_layer(args, dev):
+    """The grouped store of one 1M-token layer (8 KV heads), built on the GPU, and its
+    per-query plan at the bench budget."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS["qwen3_8b_1m_layer_step"]
+    H, G, n = cfg.H, cfg.G, cfg.n
+    ng = (n + 127) // 128
+    gs = F.GStore.empty(H, n, dev, n=n)
+    keys = synth.keys_torch(args.seed, cfg.cfg_id, range(H), n, dev)
+    F.fathom_quantize_groups(keys, gs, 0, ng)
+    del keys
+    q = torch.from_numpy(synth.queries_np(args.seed, cfg.cfg_id, range(H), G)).to(dev)
+    depth = F.fathom_plan_grouped(gs, q, args.budget)
+    torch.cuda.synchronize()
+    return gs, q, depth, cfg
+
+
+def grouped_host_line(args, L):
+    """The grouped store (68 B per token per KV head) of one 1M-token layer with its
+    planes, fp16 scales and fp16 zeros in pinned host memory, read by the GPU over the
+    host link -- where the blog measures that index ("Where this does not work"): the
+    grouped scan's GPU time from host memory and from HBM (cold caches), the bytes it
+    reads over the link (the planned planes, and every channel's scale and zero of every
+    group) and the fraction of the link bound those bytes give; the scores from host
+    memory must equal those from HBM."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    gs_d, q, depth, cfg = grouped_store_1m_layer(args, dev)
+    H, G, n, B = cfg.H, cfg.G, cfg.n, args.budget
+    ng = (n + 127) // 128
+    planes_h = torch.empty(gs_d.planes.shape, dtype=torch.int32, pin_memory=True)
+    planes_h.copy_(gs_d.planes)
+    s_h = torch.empty(gs_d.scale16.shape, dtype=torch.int16, pin_memory=True)
+    s_h.copy_(gs_d.scale16)
+    z_h = torch.empty(gs_d.zero16.shape, dtype=torch.int16, pin_memory=True)
+    z_h.copy_(gs_d.zero16)
+    gs_h = F.GStore(planes_h, s_h, z_h, gs_d.sums, gs_d.var, gs_d.prefix, gs_d.prefix_groups, n)
+    sc_d = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    sc_h = torch.empty_like(sc_d)
+    F.fathom_scan_grouped(gs_d, q, depth, scores=sc_d)
+    F.fathom_scan_grouped(gs_h, q, depth, scores=sc_h)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(sc_d, sc_h))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    ms_d = timed_ms(lambda: F.fathom_scan_grouped(gs_d, q, depth, scores=sc_d), stream, 5,
+                    flush, sink)
+    ms_h = timed_ms(lambda: F.fathom_scan_grouped(gs_h, q, depth, scores=sc_h), stream, 5,
+                    flush, sink)
+    plane_bytes = H * B * n / 8
+    sz_bytes = H * 128 * ng * 4
+    link_bytes = plane_bytes + sz_bytes
+    bound_ms = link_bytes / (L["L_GBps"] * 1e9) * 1e3
+    res = {"workload": cfg.name, "kv_heads": H, "tokens": n, "queries_per_kv_head": G,
+           "budget_bits": B, "bytes_per_token_per_kv_head": 68,
+           "scan_ms_host": round(ms_h, 4), "scan_ms_hbm": round(ms_d, 4),
+           "link_bytes": int(link_bytes), "plane_bytes": int(plane_bytes),
+           "scale_zero_bytes": int(sz_bytes), "link_GBps": L["L_GBps"],
+           "link_bound_ms": round(bound_ms, 4), "frac_of_link_bound": round(bound_ms / ms_h, 3),
+           "achieved_link_GBps": round(link_bytes / (ms_h * 1e-3) / 1e9, 2),
+           "host_scores_equal_hbm": same,
+           "timing": "fathom_scan_grouped alone, 1 GiB streaming read before each of 5 launches"}
+    log(f"[bench] grouped 1M layer scan: host {ms_h:.3f} ms, HBM {ms_d:.3f} ms, "
+        f"{bound_ms / ms_h:.2f} of the link bound, equal {same}")
+    del gs_d, gs_h, planes_h, s_h, z_h, sc_d, sc_h, flush
+    return res
+
+
+def grouped_kernel(args):
+    """--kernel scan_grouped: the grouped store on the bench workload, its scan alone
+    (for profiler runs)."""
+    import torch
+    from bit_plane_kv_amd import fathom as F
+    from bit_plane_kv_amd import synth
+    cfg = synth.CONFIGS[args.config]
+    H, G, n, B = cfg.H, cfg.G, cfg.n, args.budget
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ng = (n + 127) // 128
+    gs = F.GStore.empty(H, n, dev, n=n)
+    for h0 in range(0, H, 32):
+        h1 = min(H, h0 + 32)
+        keys = synth.keys_torch(args.seed, cfg.cfg_id, range(h0, h1), n, dev)
+        sub = F.GStore(gs.planes[h0:h1], gs.scale16[h0:h1], gs.zero16[h0:h1], gs.sums[h0:h1],
+                       gs.var[h0:h1], gs.prefix[h0:h1], gs.prefix_groups[h0:h1], n)
+        F.fathom_quantize_groups(keys, sub, 0, ng)
+        del keys
+    q = torch.from_numpy(synth.queries_np(args.seed, cfg.cfg_id, range(H), G)).to(dev)
+    depth = F.fathom_plan_grouped(gs, q, B)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    ms = timed_ms(lambda: F.fathom_scan_grouped(gs, q, depth, scores=scores), stream,
+                  args.reps, flush, sink)
+    return {"kernel": "scan_grouped", "reps": args.reps, "ms": round(ms, 4),
+            "config": cfg.name, "budget_bits": B}
+
+
 ACC_BUDGETS = (16, 24, 32, 40, 48, 56, 64, 72, 80, 92, 104, 120, 136, 168, 200, 256, 512)
 
 
@@ -852,6 +957,11 @@ def host_lines(args):
     except Exception as e:
         out["link_run_sweep"] = {"error": f"{type(e).__name__}: {e}"}
     out["layer_1m_step"] = host_resident_step(args, L)
+    try:
+        out["grouped_1m_layer_scan"] = grouped_host_line(args, L)
+    except Exception as e:  # report, do not lose the other lines
+        out["grouped_1m_layer_scan"] = {"error": f"{type(e).__name__}: {e}"}
+    torch.cuda.empty_cache()
     if not args.no_host_models:
         for name in ("qwen3_8b_256k_host", "qwen3_8b_1m_host"):
             try:
