@@ -4,8 +4,10 @@
 // One workgroup per (head, query).  A wave works on 8 winner rows at once, 8 lanes per
 // row, 16 channels (32 bytes of K and of V) per lane; each of the NT / 8 row slots keeps
 // an online softmax (running max, running sum, 128-wide output) over its rows, taken
-// four at a time with every load of the four in flight together.  The slots are merged
-// through LDS at the end in two levels (NT / 128 groups of 16 slots, then the groups).
+// four at a time with every load of the four in flight together and one update of the
+// running max per four rows.  At the end one wave finds the largest running max and each
+// slot's factor; the slots' outputs are summed through LDS in two levels (NT / 128 groups
+// of 16 slots, then the groups).
 // Rows are gathered straight from HBM or from pinned host memory; the gather is
 // memory-bound, so there is no matrix-core use.  With few rows (one layer of a decode
 // step) a workgroup has 1024 threads, so that the 512 winners of a row need one round of
@@ -38,9 +40,9 @@ __global__ __launch_bounds__(NT) void k_sparse_attn(
     constexpr int kParts = NT / kD;             // groups of slots in the merge
     constexpr int kSlotsPerPart = kSlots / kParts;  // 16
     __shared__ float so[kSlots][kD + 1];
-    __shared__ float smax[kSlots], ssum[kSlots];
+    __shared__ float smax[kSlots], ssum[kSlots], sf[kSlots];
     __shared__ float po[kParts][kD];
-    __shared__ float pmax[kParts], psum[kParts];
+    __shared__ float sL;
     const int hg = blockIdx.x, h = hg / G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = wave * 8 + (lane >> 3), sub = lane & 7;
@@ -66,7 +68,8 @@ __global__ __launch_bounds__(NT) void k_sparse_attn(
     const uint16_t *Vh = V + (size_t)h * n * kD + sub * 16;
     // four rows a slot at a time: their indices, then their K and V pieces, are loaded
     // together (a row past k or out of range reads row 0 and is then skipped), so that
-    // each batch waits for two memory latencies instead of each row
+    // each batch waits for two memory latencies instead of each row; the four rows then
+    // update the slot's running softmax once
     for (int r0 = slot; r0 < k; r0 += 4 * kSlots) {
         int row[4];
         bool ok[4];
@@ -87,29 +90,38 @@ __global__ __launch_bounds__(NT) void k_sparse_attn(
             vv[u][0] = vp[0];
             vv[u][1] = vp[1];
         }
+        float sc[4];
+        float mn = m;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (!ok[u]) continue;
-            float kf[16], vf[16];
+            float kf[16];
             unpack8(kk[u][0], kf);
             unpack8(kk[u][1], kf + 8);
-            unpack8(vv[u][0], vf);
-            unpack8(vv[u][1], vf + 8);
             float dot = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], kf[i], dot);
             dot += __shfl_xor(dot, 1, 64);
             dot += __shfl_xor(dot, 2, 64);
             dot += __shfl_xor(dot, 4, 64);
-            const float s = dot * sm_scale;
-            const float mn = fmaxf(m, s);
-            const float a = expf(m - mn);  // 0 while m is still -inf
-            const float b = expf(s - mn);
-            l = l * a + b;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[i] = o[i] * a + b * vf[i];
-            m = mn;
+            sc[u] = ok[u] ? dot * sm_scale : -INFINITY;
+            mn = fmaxf(mn, sc[u]);
         }
+        if (mn == -INFINITY) continue;  // no row of this batch, none before it
+        const float a = expf(m - mn);   // 0 while m is still -inf
+        l *= a;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] *= a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float b = expf(sc[u] - mn);  // 0 for a skipped row
+            float vf[16];
+            unpack8(vv[u][0], vf);
+            unpack8(vv[u][1], vf + 8);
+            l += b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] = fmaf(b, vf[i], o[i]);
+        }
+        m = mn;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) so[slot][sub * 16 + i] = o[i];
@@ -118,37 +130,38 @@ __global__ __launch_bounds__(NT) void k_sparse_attn(
         ssum[slot] = l;
     }
     __syncthreads();
+    if (wave == 0) {  // the largest running max M, each slot's factor e^(m - M), and L
+        float mx = -INFINITY;
+        for (int s2 = lane; s2 < kSlots; s2 += 64) mx = fmaxf(mx, smax[s2]);
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
+        float L = 0.0f;
+        for (int s2 = lane; s2 < kSlots; s2 += 64) {
+            const float f = smax[s2] == -INFINITY ? 0.0f : expf(smax[s2] - mx);
+            sf[s2] = f;
+            L += ssum[s2] * f;
+        }
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) L += __shfl_xor(L, o2, 64);
+        if (lane == 0) sL = L;
+    }
+    __syncthreads();
     {   // group p of slots (p, p + kParts, ...): channel c's share of the output
         const int c = tid & (kD - 1), p = tid >> 7;
-        float M = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kSlotsPerPart; ++j) M = fmaxf(M, smax[p + kParts * j]);
-        float L = 0.0f, O = 0.0f;
+        float O = 0.0f;
 #pragma unroll
         for (int j = 0; j < kSlotsPerPart; ++j) {
             const int s2 = p + kParts * j;
-            const float f = smax[s2] == -INFINITY ? 0.0f : expf(smax[s2] - M);
-            L += ssum[s2] * f;
-            O += so[s2][c] * f;
+            O = fmaf(sf[s2], so[s2][c], O);
         }
         po[p][c] = O;
-        if (c == 0) {
-            pmax[p] = M;
-            psum[p] = L;
-        }
     }
     __syncthreads();
     if (tid < kD) {
-        float M = -INFINITY;
+        float O = 0.0f;
 #pragma unroll
-        for (int p = 0; p < kParts; ++p) M = fmaxf(M, pmax[p]);
-        float L = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int p = 0; p < kParts; ++p) {
-            const float f = pmax[p] == -INFINITY ? 0.0f : expf(pmax[p] - M);
-            L += psum[p] * f;
-            O += po[p][tid] * f;
-        }
+        for (int p = 0; p < kParts; ++p) O += po[p][tid];
+        const float L = sL;
         const float res = L > 0.0f ? O / L : 0.0f;
         out[(size_t)hg * kD + tid] = float_to_bf16_bits(res);
     }
