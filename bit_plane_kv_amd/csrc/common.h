@@ -8,6 +8,15 @@
 
 #include "fathom.h"
 
+// Whole-wave reductions of the device library (DPP row operations, the result in every
+// lane): cheaper than a butterfly of cross-lane shuffles.
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_add_u32(unsigned int);
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_min_u32(unsigned int);
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_max_u32(unsigned int);
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_add_u64(
+    unsigned long long);
+extern "C" __device__ __attribute__((const)) double __ockl_wfred_max_f64(double);
+
 namespace fathom {
 
 constexpr int kD = FATHOM_D;                 // channels per head

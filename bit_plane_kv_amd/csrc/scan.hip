@@ -304,7 +304,7 @@ __device__ __forceinline__ int32_t filter_threshold(bool live, uint32_t tkey, fl
     return (int32_t)t;
 }
 
-// Inputs of the prepare step a thread reads (threads 0..127: channel tid): the head's
+// Inputs of the prepare step a thread reads (thread t: channel t mod 128): the head's
 // queries, scale and zero, loaded together at the start of a kernel.
 template <int QS>
 struct PrepIn {
@@ -318,7 +318,7 @@ __device__ __forceinline__ void load_prep_in(const float *__restrict__ q,
                                              PrepIn<QS> &in) {
     // unconditional loads (channel and query clamped) so that all are in flight
     // together; the values a thread does not need are never used or zeroed
-    const int c = min((int)threadIdx.x, kD - 1);
+    const int c = (int)threadIdx.x & (kD - 1);
 #pragma unroll
     for (int g = 0; g < 4 * QS; ++g) in.q[g] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
     in.s = scale[(size_t)h * kD + c];
@@ -367,14 +367,16 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     const int ngroups = (nplanes + kGroupBits - 1) / kGroupBits;
     // at least one K-block, so that a head with no planes still writes its constants
     const int nkb = max(1, (ngroups + kKBlockGroups - 1) / kKBlockGroups);
-    if (tid < kD) {
-        const int c = tid, t = tc[c], o = off[c];
+    {   // thread t: channel t mod 128, queries t / 128, t / 128 + 2, ...
+        const int c = tid & (kD - 1), half = tid >> 7, t = tc[c], o = off[c];
         const double s = (double)in.s;
         const double z = (double)in.z;
         const double hm = (double)((16 >> t) - 1) * 0.5;  // bin-midpoint offset h(t)
-        for (int j = 0; j < t; ++j) pl[o + j] = (uint32_t)(c * kPlanes + j);
+        if (!half)
+            for (int j = 0; j < t; ++j) pl[o + j] = (uint32_t)(c * kPlanes + j);
 #pragma unroll
         for (int g = 0; g < NQ; ++g) {
+            if ((g & 1) != half) continue;
             const double qv = (double)in.q[g];
             for (int j = 0; j < t; ++j) wt[g][o + j] = (qv * s) * (double)(8 >> j);
             red[g][c] = qv * (z + s * hm);  // this channel's share of C_g
@@ -395,10 +397,8 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         double sum = red[g][lane] + red[g][lane + 64];
         double mx = fmax(amx[g][lane], amx[g][lane + 64]);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            sum += __shfl_xor(sum, o, 64);
-            mx = fmax(mx, __shfl_xor(mx, o, 64));
-        }
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        mx = __ockl_wfred_max_f64(mx);
         if (lane == 0) {
             csum[g] = sum;
             int e = 0;
@@ -427,11 +427,8 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
             r += dl < 0 ? -dl : dl;
             a += u >= kDigitBias ? u - kDigitBias : kDigitBias - u;
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            r += __shfl_xor(r, o, 64);
-            a += __shfl_xor(a, o, 64);
-        }
+        r = (long long)__ockl_wfred_add_u64((unsigned long long)r);  // both sums are >= 0
+        a = (long long)__ockl_wfred_add_u64((unsigned long long)a);
         if (lane == 0) {
             rb[g] = (double)r;
             mabs[g] = (double)a;

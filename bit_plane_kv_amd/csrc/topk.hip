@@ -687,12 +687,9 @@ __device__ __forceinline__ void select_kept(
                 nex += key >= tkey;
             }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-            nex += (uint32_t)__shfl_xor((int)nex, o, 64);
-        }
+        kmin = __ockl_wfred_min_u32(kmin);
+        kmax = __ockl_wfred_max_u32(kmax);
+        nex = __ockl_wfred_add_u32(nex);
         if ((tid & 63) == 0) {
             smm[0][tid >> 6] = kmin;
             smm[1][tid >> 6] = kmax;
