@@ -726,7 +726,8 @@ def grouped_lines(args, kern):
     ref = oracle.scores_grouped(codes, s16, z16, ref_depth, q[h:h + 1].cpu().numpy())
     got = scores[h:h + 1].cpu().numpy()
     rel = float((np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
-    ok = bool(np.array_equal(gs.scale16[h:h + 1, :, :ng].cpu().numpy().view(np.uint16), s16)
+    ok = bool(np.array_equal(gs.scale16[h:h + 1, :ng].cpu().numpy().view(np.uint16)
+                             .transpose(0, 2, 1), s16)
               and np.array_equal(depth[h:h + 1].cpu().numpy(), ref_depth) and rel <= 1e-5)
     res = {"bytes_per_token_per_kv_head": 64 + 4, "group_tokens": 128,
            "build_ms": round(build_ms, 3), "append_one_token_ms": round(append_ms, 4),

@@ -40,6 +40,17 @@ int check_visible(const void *p) {
     return FATHOM_ERR_NOT_MAPPED;
 }
 
+// p is pinned host memory mapped for the GPU (read over the host link).
+bool is_pinned_host(const void *p) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeHost;
+}
+
 int check_all(std::initializer_list<const void *> ptrs) {
     for (const void *p : ptrs) {
         if (!p) continue;
@@ -261,7 +272,7 @@ static int check_gstore(const fathom_gstore *gs) {
     const int ng = (gs->n_tokens + FATHOM_GROUP - 1) / FATHOM_GROUP;
     if (gs->word_stride < 4 * ng || (gs->word_stride & 3) || gs->group_stride < ng)
         return FATHOM_ERR_INVALID_ARG;
-    if (!aligned(gs->planes, 16) || !aligned(gs->scale16, 2) || !aligned(gs->zero16, 2) ||
+    if (!aligned(gs->planes, 16) || !aligned(gs->scale16, 8) || !aligned(gs->zero16, 8) ||
         !aligned(gs->sums, 8) || !aligned(gs->var, 4) || !aligned(gs->prefix, 16) ||
         !aligned(gs->prefix_groups, 4))
         return FATHOM_ERR_INVALID_ARG;
@@ -307,7 +318,8 @@ int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const ui
     if (!q || !depth || !scores || !aligned(q, 4) || !aligned(scores, 4))
         return FATHOM_ERR_INVALID_ARG;
     FATHOM_TRY(check_all({q, depth, scores}));
-    return hip_status(launch_scan_grouped(*gs, q, depth, G, scores, as_stream(stream)));
+    return hip_status(launch_scan_grouped(*gs, q, depth, G, scores, is_pinned_host(gs->planes),
+                                          as_stream(stream)));
 }
 
 int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream) {

@@ -171,8 +171,9 @@ hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,
 hipError_t launch_pack_nibbles(const fathom_store &st, uint8_t *nib, hipStream_t s);
 hipError_t launch_quantize_groups(const float *keys, int64_t head_stride,
                                   const fathom_gstore &gs, int g0, int g1, hipStream_t s);
+// host_planes: the planes are pinned host memory (longer reads per tile)
 hipError_t launch_scan_grouped(const fathom_gstore &gs, const float *q, const uint8_t *depth,
-                               int G, float *scores, hipStream_t s);
+                               int G, float *scores, bool host_planes, hipStream_t s);
 hipError_t launch_scan_nibble(const uint8_t *nib, const float *scale, const float *zero, int H,
                               int n, const float *q, int G, float *scores, hipStream_t s);
 hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,

@@ -106,9 +106,10 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_groups(
     ps2[w][c] = s2;
     __syncthreads();
     if (w == 0) {
+        const size_t tg = ((size_t)h * gs.group_stride + G) * kD + c;  // tables: group-major
+        gs.scale16[tg] = __half_as_ushort(sh);
+        gs.zero16[tg] = __half_as_ushort(zh);
         const size_t t = ((size_t)h * kD + c) * gs.group_stride + G;
-        gs.scale16[t] = __half_as_ushort(sh);
-        gs.zero16[t] = __half_as_ushort(zh);
         gs.sums[2 * t] = ps1[0][c] + ps1[1][c] + ps1[2][c] + ps1[3][c];
         gs.sums[2 * t + 1] = ps2[0][c] + ps2[1][c] + ps2[2][c] + ps2[3][c];
     }
@@ -138,8 +139,9 @@ __global__ __launch_bounds__(kD) void k_var_groups(fathom_gstore gs, int g0) {
             gs.prefix[2 * hc + 1] = Q;
             gs.prefix_groups[hc] = G;
         }
-        const double zf = (double)__half2float(__ushort_as_half(gs.zero16[base + G]));
-        const double sf = (double)__half2float(__ushort_as_half(gs.scale16[base + G]));
+        const size_t tg = ((size_t)h * gs.group_stride + G) * kD + c;
+        const double zf = (double)__half2float(__ushort_as_half(gs.zero16[tg]));
+        const double sf = (double)__half2float(__ushort_as_half(gs.scale16[tg]));
         const int2 s12 = *reinterpret_cast<const int2 *>(gs.sums + 2 * (base + G));
         const double s1 = (double)s12.x, s2 = (double)s12.y;
         const double nG = (double)(min(n, (G + 1) * kGroup) - G * kGroup);
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kD) void k_var_groups(fathom_gstore gs, int g0) {
 // product of a token-by-plane bit matrix and a plane-by-query weight matrix, except
 // that the weights change every 128-token group.  So each 16-column MFMA block must lie
 // in one group: wave v of a workgroup scores words 8v .. 8v+7 (groups 2v and 2v+1 of a
-// 32-word tile), and lane 16 q + 4 w + s reads word 8v + 4 pos + w of planes s and s+4
+// 64-word tile), and lane 16 q + 4 w + s reads word 8v + 4 pos + w of planes s and s+4
 // of plane groups q and q+4 of the K-pair, so that pos picks the group.  The A operand
 // (16 rows = 4 queries x 4 digits, K = 64 planes) of each (K-pair, group) is built in
 // registers: each weight becomes an integer count of a per-(query, group) power-of-two
@@ -169,25 +171,29 @@ __global__ __launch_bounds__(kD) void k_var_groups(fathom_gstore gs, int g0) {
 // exact; each score is C + S (D0 + 256 D1 + 65536 (D2 + 256 D3)) / 2^m in fp32 as in the
 // per-channel scan, C_gG = sum_c q_gc (zf_cG + sf_cG h(t_c)) in fp64 rounded once.
 // ---------------------------------------------------------------------------------
-constexpr int kMThreads = 256;                     // 4 waves
-constexpr int kMWords = 32;                        // words per tile: 8 per wave
-constexpr int kMGroups = kMWords / kGroupWords;    // 8 groups per tile, 2 per wave
+// A tile is TW words, 8 per wave.  From HBM TW = 32 (4 waves: less lock-step, 150 us
+// against 185 us for 64 on the bench cache); from pinned host memory TW = 64, so that each
+// plane row is read in 256-byte runs and a tile's fp16 scales and zeros (group-major) in
+// 4 KiB runs -- the link loses most of its rate on shorter runs (1M-token layer: 0.96 of
+// the link bound against 0.26 with 128-byte row runs and 16-byte table pieces).
 constexpr int kMBatch = 128;                       // planes staged at once: two K-pairs
-constexpr int kMRowPad = kMWords + 4;              // 16-byte aligned LDS rows
 
-// Four waves per SIMD for one query set (117 registers, no spills: each tile's chain of
-// loads and barriers is hidden by more resident tiles; five spill to scratch and run
-// slower), two for two sets (198 registers; three spill).
-template <int QS>
-__global__ __launch_bounds__(kMThreads)
+// Four waves per SIMD for one query set (five spill to scratch and run slower), two for
+// two sets.
+template <int QS, int TW>
+__global__ __launch_bounds__(TW * 8)
 __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
     fathom_gstore gs, const float *__restrict__ q, const uint8_t *__restrict__ depth, int G,
     float *__restrict__ scores, int tiles_per_head) {
+    constexpr int kMThreads = TW * 8;               // TW / 8 waves
+    constexpr int kMWords = TW;                     // words per tile
+    constexpr int kMGroups = kMWords / kGroupWords; // groups per tile, 2 per wave
+    constexpr int kMRowPad = kMWords + 4;           // 16-byte aligned LDS rows
     constexpr int NQ = 4 * QS;
     __shared__ __align__(16) uint32_t words[kMBatch][kMRowPad];
     __shared__ float qs[NQ][kD];
-    __shared__ __half sgrp[kD][kMGroups];
-    __shared__ __half zgrp[kD][kMGroups];
+    __shared__ __align__(8) __half sgrp[kMGroups][kD];  // group-major, as in the store
+    __shared__ __align__(8) __half zgrp[kMGroups][kD];
     __shared__ float cg[kMGroups][NQ];
     __shared__ int tc[kD];
     __shared__ int off[kD + 1];
@@ -200,8 +206,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
 
     // inputs: every load unconditional (indices clamped into the head's tables) and
     // issued before any is used, so that they are all in flight together
-    constexpr int kQPer = NQ * kD / kMThreads;       // 2 or 4
-    constexpr int kSPer = kD * kMGroups / kMThreads;  // 4
+    constexpr int kQPer = NQ * kD / kMThreads;       // 1 or 2
+    static_assert(kD * kMGroups == 4 * kMThreads, "one 8-byte load per table a thread");
     const int tdep = depth[(size_t)h * kD + min(tid, kD - 1)];
     float qv[kQPer];
 #pragma unroll
@@ -209,26 +215,20 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
         const int e = tid + kMThreads * u, g = e / kD, c = e - g * kD;
         qv[u] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
     }
-    uint16_t sv[kSPer], zv[kSPer];
-#pragma unroll
-    for (int u = 0; u < kSPer; ++u) {
-        const int e = tid + kMThreads * u, c = e / kMGroups, gg = e - c * kMGroups;
-        const size_t t = ((size_t)h * kD + c) * gs.group_stride + min(gb + gg, ng - 1);
-        sv[u] = gs.scale16[t];
-        zv[u] = gs.zero16[t];
-    }
+    // the tile's scales and zeros: thread t takes channels 4 (t % 32) .. + 3 of group
+    // t / 32 (groups past the head's last are its last group's)
+    const int sgg = tid / (kD / 4), sc0 = 4 * (tid % (kD / 4));
+    const size_t st0 = ((size_t)h * gs.group_stride + min(gb + sgg, ng - 1)) * kD + sc0;
+    const uint2 sv = *reinterpret_cast<const uint2 *>(gs.scale16 + st0);
+    const uint2 zv = *reinterpret_cast<const uint2 *>(gs.zero16 + st0);
     if (tid < kD) tc[tid] = min(tdep, kPlanes);
 #pragma unroll
     for (int u = 0; u < kQPer; ++u) {
         const int e = tid + kMThreads * u, g = e / kD, c = e - g * kD;
         qs[g][c] = g < G ? qv[u] : 0.0f;
     }
-#pragma unroll
-    for (int u = 0; u < kSPer; ++u) {
-        const int e = tid + kMThreads * u, c = e / kMGroups, gg = e - c * kMGroups;
-        sgrp[c][gg] = __ushort_as_half(sv[u]);
-        zgrp[c][gg] = __ushort_as_half(zv[u]);
-    }
+    *reinterpret_cast<uint2 *>(&sgrp[sgg][sc0]) = sv;
+    *reinterpret_cast<uint2 *>(&zgrp[sgg][sc0]) = zv;
     __syncthreads();
     if (tid < 64) {  // exclusive prefix sum of the depths, 2 channels a lane
         const int a = tc[2 * lane], b = tc[2 * lane + 1];
@@ -251,8 +251,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
         double acc = 0.0;
 #pragma unroll
         for (int c = c0; c < c0 + 16; ++c) {
-            const double zf = (double)__half2float(zgrp[c][gg]);
-            const double sf = (double)__half2float(sgrp[c][gg]);
+            const double zf = (double)__half2float(zgrp[gg][c]);
+            const double sf = (double)__half2float(sgrp[gg][c]);
             const double hm = (double)((16 >> tc[c]) - 1) * 0.5;
             acc += (double)qs[g][c] * (zf + sf * hm);
         }
@@ -285,7 +285,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int c = lane + 64 * cc;
-                if (tc[c] > 0) mx = fmaxf(mx, fabsf(qs[g][c] * __half2float(sgrp[c][gr])) * 8.0f);
+                if (tc[c] > 0) mx = fmaxf(mx, fabsf(qs[g][c] * __half2float(sgrp[gr][c])) * 8.0f);
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -309,7 +309,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
             uint4 x[kBPer];
 #pragma unroll
             for (int u = 0; u < kBPer; ++u) {
-                const int e = tid + kMThreads * u, r = e >> 3, v = e & 7;
+                const int e = tid + kMThreads * u, r = e / (kMWords / 4), v = e % (kMWords / 4);
                 const int wv = w0 + 4 * v;
                 const int row = pl[p0 + min(r, np - 1)];
                 x[u] = *reinterpret_cast<const uint4 *>(hp + (size_t)row * gs.word_stride +
@@ -317,7 +317,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
             }
 #pragma unroll
             for (int u = 0; u < kBPer; ++u) {
-                const int e = tid + kMThreads * u, r = e >> 3, v = e & 7;
+                const int e = tid + kMThreads * u, r = e / (kMWords / 4), v = e % (kMWords / 4);
                 if (r < np)
                     *reinterpret_cast<uint4 *>(&words[r][4 * v]) =
                         w0 + 4 * v < gs.word_stride ? x[u] : make_uint4(0u, 0u, 0u, 0u);
@@ -345,7 +345,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
                         int M = 0;
                         if (P < nplanes) {
                             const int row = pl[P], c = row >> 2, j = row & 3;
-                            const float w = qs[g][c] * __half2float(sgrp[c][gr]);
+                            const float w = qs[g][c] * __half2float(sgrp[gr][c]);
                             // w 2^(3-j) / 2^(e-30), an exact power-of-two scaling
                             M = (int)rintf(ldexpf(w, 33 - j - eu[pos][g]));
                         }
@@ -427,13 +427,13 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
     }
 }
 
-template <int QS>
+template <int QS, int TW>
 void launch_scan_mma(const fathom_gstore &gs, const float *q, const uint8_t *depth, int G,
                      float *scores, hipStream_t s) {
     const int W = (gs.n_tokens + 31) >> 5;
-    const int tiles = (W + kMWords - 1) / kMWords;
-    hipLaunchKernelGGL(k_scan_grouped_mma<QS>, dim3(gs.n_heads * tiles), dim3(kMThreads), 0, s,
-                       gs, q, depth, G, scores, tiles);
+    const int tiles = (W + TW - 1) / TW;
+    hipLaunchKernelGGL((k_scan_grouped_mma<QS, TW>), dim3(gs.n_heads * tiles), dim3(TW * 8), 0,
+                       s, gs, q, depth, G, scores, tiles);
 }
 
 }  // namespace
@@ -447,9 +447,14 @@ hipError_t launch_quantize_groups(const float *keys, int64_t head_stride,
 }
 
 hipError_t launch_scan_grouped(const fathom_gstore &gs, const float *q, const uint8_t *depth,
-                               int G, float *scores, hipStream_t s) {
-    if (query_sets(G) == 1) launch_scan_mma<1>(gs, q, depth, G, scores, s);
-    else launch_scan_mma<2>(gs, q, depth, G, scores, s);
+                               int G, float *scores, bool host_planes, hipStream_t s) {
+    if (query_sets(G) == 1) {
+        if (host_planes) launch_scan_mma<1, 64>(gs, q, depth, G, scores, s);
+        else launch_scan_mma<1, 32>(gs, q, depth, G, scores, s);
+    } else {
+        if (host_planes) launch_scan_mma<2, 64>(gs, q, depth, G, scores, s);
+        else launch_scan_mma<2, 32>(gs, q, depth, G, scores, s);
+    }
     return hipGetLastError();
 }
 

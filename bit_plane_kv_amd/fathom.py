@@ -196,7 +196,7 @@ class GStore:
     """Grouped store: planes as in Store, fp16 scale/zero and int32 code sums per
     (channel, 128-token group), fp32 var.  Capacity: n_max tokens."""
     planes: object        # int32 [H][d][4][word_stride]
-    scale16: object       # int16 (fp16 bits) [H][d][group_stride]
+    scale16: object       # int16 (fp16 bits) [H][group_stride][d]
     zero16: object
     sums: object          # int32 [H][d][group_stride][2]
     var: object           # fp32 [H][d]
@@ -210,7 +210,7 @@ class GStore:
 
     def descriptor(self) -> fathom_gstore:
         return fathom_gstore(self.n_heads, self.n_tokens, D, int(self.planes.shape[-1]),
-                             int(self.scale16.shape[-1]), 0, _ptr(self.planes),
+                             int(self.scale16.shape[1]), 0, _ptr(self.planes),
                              _ptr(self.scale16), _ptr(self.zero16), _ptr(self.sums),
                              _ptr(self.var), _ptr(self.prefix), _ptr(self.prefix_groups))
 
@@ -221,8 +221,8 @@ class GStore:
         i32 = dict(dtype=torch.int32, device=device)
         ws = int(lib().fathom_word_stride(GROUP * ng))  # >= 4 ng words, whole groups
         return GStore(torch.zeros((H, D, PLANES, ws), **i32),
-                      torch.zeros((H, D, ng), dtype=torch.int16, device=device),
-                      torch.zeros((H, D, ng), dtype=torch.int16, device=device),
+                      torch.zeros((H, ng, D), dtype=torch.int16, device=device),
+                      torch.zeros((H, ng, D), dtype=torch.int16, device=device),
                       torch.zeros((H, D, ng, 2), **i32),
                       torch.zeros((H, D), dtype=torch.float32, device=device),
                       torch.zeros((H, D, 2), dtype=torch.float64, device=device),

@@ -91,13 +91,16 @@ typedef struct fathom_store {
  * and one fp16 zero per channel per 128-token group give).  Caller-owned buffers:
  *   planes [H][d][4][word_stride] uint32, as in fathom_store; word_stride >=
  *          4*ceil(n/128) and a multiple of 4 (whole groups of 4 words).
- *   scale16, zero16 [H][d][group_stride] fp16 bits: group G of channel c of head h.
+ *   scale16, zero16 [H][group_stride][d] fp16 bits: group G of channel c of head h
+ *          (group-major, so that one group's 128 channels are 256 contiguous bytes);
+ *          8-byte aligned.
  *   sums [H][d][group_stride][2] int32: the group's sum of codes and of squared codes.
  *   var [H][d] fp32: variance of the group-dequantized channel over all n tokens.
  *   prefix [H][d][2] fp64 and prefix_groups [H][d] int32: the variance's running sums
  *          (S, Q below) over the first prefix_groups groups, kept so that an append
  *          adds only the groups it changed.  Zero them before the first call.
- * group_stride >= ceil(n/128).  All device memory except planes (HBM or pinned host).
+ * group_stride >= ceil(n/128).  All device memory except planes, scale16 and zero16
+ * (HBM or pinned host).
  */
 typedef struct fathom_gstore {
     int32_t n_heads;      /* H */

@@ -29,8 +29,9 @@ def _check_against_oracle(gs, keys):
     planes = gs.planes.cpu().numpy().view(np.uint32)
     assert np.array_equal(planes[..., :(n + 31) // 32], oracle.pack_planes(codes))
     assert not planes[..., (n + 31) // 32:4 * ng].any()      # words past n are zero
-    assert np.array_equal(gs.scale16.cpu().numpy().view(np.uint16)[..., :ng], s16)
-    assert np.array_equal(gs.zero16.cpu().numpy().view(np.uint16)[..., :ng], z16)
+    # the store's tables are group-major [H][group][channel]; the oracle's [H][channel][group]
+    assert np.array_equal(gs.scale16.cpu().numpy().view(np.uint16)[:, :ng].transpose(0, 2, 1), s16)
+    assert np.array_equal(gs.zero16.cpu().numpy().view(np.uint16)[:, :ng].transpose(0, 2, 1), z16)
     assert np.array_equal(gs.var.cpu().numpy(), oracle.var_grouped(codes, s16, z16))
     return s16, z16, codes
 
@@ -100,3 +101,29 @@ def test_grouped_plan_and_scan_match_oracle(H, G, n, kind):
     torch.cuda.synchronize()
     ref = oracle.scores_grouped(codes, s16, z16, ref_depth, q)
     check_rows(got.cpu().numpy(), ref)
+
+
+def test_grouped_scan_from_pinned_host_memory_equals_hbm():
+    """The grouped scan reads planes, fp16 scales and fp16 zeros in place from pinned host
+    memory (the blog's setting for this index): the same scores as from HBM, bit for bit,
+    over several 2048-token tiles and a ragged last one."""
+    torch = torch_cuda()
+    H, G, n = 2, 4, 5000
+    print(f"[grouped host] H={H} G={G} n={n}", flush=True)
+    keys, q, _, _ = inputs(123, H, G, n)
+    gs = _build(keys)
+    q_t = to_dev(q)
+    depth = F.fathom_plan_grouped(gs, q_t, 92)
+    ref = F.fathom_scan_grouped(gs, q_t, depth)
+    host = {}
+    for name in ("planes", "scale16", "zero16"):
+        t = getattr(gs, name)
+        host[name] = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        host[name].copy_(t)
+    gh = F.GStore(host["planes"], host["scale16"], host["zero16"], gs.sums, gs.var, gs.prefix,
+                  gs.prefix_groups, n)
+    got = F.fathom_scan_grouped(gh, q_t, depth)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    s16, z16, codes = oracle.quantize_grouped(keys)
+    check_rows(got.cpu().numpy(), oracle.scores_grouped(codes, s16, z16, depth.cpu().numpy(), q))
