@@ -463,6 +463,14 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     } else {  // the filtering scan keeps the candidates only
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
         FATHOM_TRY(mark(2));
+        if (filtered_attend_applies(H * G, n, k)) {
+            // few rows of one chunk (a layer of a decode step): select and attention in one
+            // kernel; its time falls in the select phase, the attention phase is empty
+            FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k,
+                                                              idx, q, K, V, sm_scale, out, s)));
+            FATHOM_TRY(mark(3));
+            return mark(4);
+        }
         FATHOM_TRY(hip_status(
             launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
     }

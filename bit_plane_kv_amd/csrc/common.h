@@ -183,6 +183,14 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
 hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand,
                                 const uint32_t *masks, void *scan_ws, uint32_t *redo_list,
                                 int k, int32_t *idx, void *ws, hipStream_t s);
+// the same select fused with the attention of each row (rows of one chunk, few rows, small
+// k: filtered_attend_applies); idx still receives the winners
+bool filtered_attend_applies(int R, int n, int k);
+hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,
+                                       const uint32_t *masks, void *scan_ws, int k,
+                                       int32_t *idx, const float *q, const uint16_t *K,
+                                       const uint16_t *V, float sm_scale, uint16_t *out,
+                                       hipStream_t s);
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s);

@@ -9,6 +9,7 @@
 // the lowest positions.  Rows longer than a chunk are cut into chunks whose top
 // min(k, chunk) survive as (value, index) candidates, in index order, for the next
 // level, until one chunk remains.
+#include "attn_device.h"
 #include "common.h"
 
 namespace fathom {
@@ -86,14 +87,18 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t *total) {
 __device__ __forceinline__ void find_bin(uint32_t *hist, uint32_t *scan_sh, uint32_t *pick,
                                          int nb, uint32_t need) {
     const int tid = threadIdx.x;
-    uint32_t c4[4];
-    uint32_t local = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int b = nb - 1 - (4 * tid + e);  // thread t owns 4 bins, highest first
-        c4[e] = b >= 0 ? hist[b] : 0u;
-        local += c4[e];
+    uint32_t c4[4] = {0u, 0u, 0u, 0u};
+    // thread t owns bins nb-1-4t .. nb-4-4t, highest first: one aligned 16-byte piece
+    // (word by word, lanes 16 bytes apart conflict 4-way on the banks)
+    const int lo = nb - 4 - 4 * tid;
+    if (lo >= 0) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(&hist[lo]);
+        c4[0] = x.w;
+        c4[1] = x.z;
+        c4[2] = x.y;
+        c4[3] = x.x;
     }
+    const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
     uint32_t total;
     const uint32_t above = block_excl_scan(local, scan_sh, &total);
     if (above < need && need <= above + local) {
@@ -262,8 +267,9 @@ template <bool kExplicit, bool kCandOut, bool kMasked, bool kDirect = false>
 __device__ __forceinline__ void select_chunk(
     int64_t row, int chunk, const float *__restrict__ vals, const int32_t *__restrict__ in_idx,
     int64_t row_len, int64_t in_stride, int k, float *__restrict__ out_val,
-    int32_t *__restrict__ out_idx, int64_t out_stride, const FilterArgs &fa) {
-    __shared__ uint32_t hist[4096];
+    int32_t *__restrict__ out_idx, int64_t out_stride, const FilterArgs &fa,
+    int32_t *lds_idx = nullptr) {
+    __shared__ __align__(16) uint32_t hist[4096];
     __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t scan_sh[17];
     __shared__ uint32_t pick[3];
@@ -447,6 +453,7 @@ __device__ __forceinline__ void select_chunk(
                 out_idx[o] = index;
             } else {
                 out_idx[row * (int64_t)k + slot] = index;
+                if (lds_idx) lds_idx[slot] = index;  // the winners, also for this workgroup
             }
         }
         ++slot;
@@ -561,7 +568,7 @@ template <bool kCandOut, bool kDirect, int NT>
 __device__ __forceinline__ void select_kept(
     const float *__restrict__ cand, int64_t n, int row0, int k, const FilterArgs &fa,
     uint32_t *__restrict__ list, float *__restrict__ out_val, int32_t *__restrict__ out_idx,
-    int64_t out_stride) {
+    int64_t out_stride, int32_t *lds_idx = nullptr) {
     constexpr int NW = NT / 64;                 // waves
     constexpr int WPT = kTopkChunk / 32 / NT;   // mask words a thread: 4 or 1
     constexpr int BPT = kSelBins / NT;          // histogram bins a thread: 8 or 2
@@ -570,7 +577,7 @@ __device__ __forceinline__ void select_kept(
     static_assert(!kDirect || (NT == kThreads && !kCandOut), "the direct select: one chunk");
     __shared__ uint32_t skey[kSelCap];
     __shared__ uint16_t soff[kSelCap];
-    __shared__ uint32_t hist[kSelBins];
+    __shared__ __align__(16) uint32_t hist[kSelBins];
     __shared__ uint32_t sh[2][NW];
     __shared__ uint32_t pick[2][3];
     __shared__ uint32_t smm[3][NW];  // per-wave min and max key, count clearing the threshold
@@ -587,7 +594,7 @@ __device__ __forceinline__ void select_kept(
     auto hand_over = [&]() {
         if constexpr (kDirect)
             select_chunk<false, false, true, true>(row, 0, cand, nullptr, n, n, k, nullptr,
-                                                   out_idx, 0, fa);
+                                                   out_idx, 0, fa, lds_idx);
         else if (tid == 0)
             list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
     };
@@ -735,14 +742,37 @@ __device__ __forceinline__ void select_kept(
             if (((uint64_t)key >> shift) == prefix) atomicAdd(&hist[(key >> sd) & (nb - 1)], 1u);
         }
         __syncthreads();
-        // thread t owns bins nb-1-BPT t .. nb-BPT-BPT t (largest first)
+        // thread t owns bins nb-1-BPT t .. nb-BPT-BPT t (largest first); when all of
+        // them exist they are one aligned run, read as 16-byte pieces (lanes 4 BPT bytes
+        // apart: word by word that is a BPT-way bank conflict)
         uint32_t cb[BPT], local = 0u;
+        const int lo = nb - BPT - BPT * tid;  // the thread's lowest bin
+        if constexpr (BPT % 4 == 0) {
+            if (lo >= 0) {
 #pragma unroll
-        for (int e = 0; e < BPT; ++e) {
-            const int bin = nb - 1 - (BPT * tid + e);
-            cb[e] = bin >= 0 ? hist[bin] : 0u;
-            local += cb[e];
+                for (int v = 0; v < BPT / 4; ++v) {
+                    const uint4 x = *reinterpret_cast<const uint4 *>(&hist[lo + 4 * v]);
+                    cb[BPT - 1 - 4 * v] = x.x;
+                    cb[BPT - 2 - 4 * v] = x.y;
+                    cb[BPT - 3 - 4 * v] = x.z;
+                    cb[BPT - 4 - 4 * v] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < BPT; ++e) {
+                    const int bin = nb - 1 - (BPT * tid + e);
+                    cb[e] = bin >= 0 ? hist[bin] : 0u;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < BPT; ++e) {
+                const int bin = nb - 1 - (BPT * tid + e);
+                cb[e] = bin >= 0 ? hist[bin] : 0u;
+            }
         }
+#pragma unroll
+        for (int e = 0; e < BPT; ++e) local += cb[e];
         uint32_t tot;
         const uint32_t above = block_prefix1<NT>(local, sh[(pass + 1) & 1], &tot);
         if (above < need && need <= above + local) {
@@ -758,10 +788,16 @@ __device__ __forceinline__ void select_kept(
             }
         }
         // every thread has read hist: clear it for the next pass
+        if (BPT % 4 == 0 && lo >= 0) {
 #pragma unroll
-        for (int e = 0; e < BPT; ++e) {
-            const int bin = nb - 1 - (BPT * tid + e);
-            if (bin >= 0) hist[bin] = 0u;
+            for (int v = 0; v < BPT / 4; ++v)
+                *reinterpret_cast<uint4 *>(&hist[lo + 4 * v]) = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < BPT; ++e) {
+                const int bin = nb - 1 - (BPT * tid + e);
+                if (bin >= 0) hist[bin] = 0u;
+            }
         }
         __syncthreads();
         prefix = (prefix << width) | pick[pass & 1][0];
@@ -801,6 +837,7 @@ __device__ __forceinline__ void select_kept(
                     out_idx[obase + slot] = index;
                 } else {
                     out_idx[row * (int64_t)k + slot] = index;
+                    if (lds_idx) lds_idx[slot] = index;
                 }
             }
             ++slot;
@@ -822,6 +859,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_select_direct(
     const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
     int32_t *__restrict__ out_idx) {
     select_kept<false, true, kThreads>(cand, n, row0, k, fa, nullptr, nullptr, out_idx, 0);
+}
+
+// The direct select and the attention of its row in one workgroup (one layer of a decode
+// step): the winners pass to the attention in LDS, so no index round trip through memory
+// and no second launch.  k <= kFusedMaxK.
+constexpr int kFusedMaxK = 1024;
+__global__ __launch_bounds__(kThreads, 1) void k_select_attend(
+    const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
+    int32_t *__restrict__ out_idx, const float *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, float sm_scale, uint16_t *__restrict__ out) {
+    __shared__ int32_t widx[kFusedMaxK];
+    select_kept<false, true, kThreads>(cand, n, row0, k, fa, nullptr, nullptr, out_idx, 0,
+                                       widx);
+    __syncthreads();  // every winner is in widx
+    attend_row<kThreads>(q, K, V, fa.G, (int)n, [](int r) { return widx[r]; }, k, sm_scale,
+                         out, row0 + (int)blockIdx.y);
 }
 
 template <bool kExplicit, bool kCandOut>
@@ -904,6 +957,31 @@ hipError_t run_levels(const float *scores, int R, int n, int k, int32_t *idx, vo
 hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, void *ws,
                        hipStream_t s) {
     return run_levels(scores, R, n, k, idx, ws, s, FilterArgs{}, nullptr);
+}
+
+bool filtered_attend_applies(int R, int n, int k) {
+    return topk_levels(n, k).n_levels == 0 && R <= kDirectRows && k <= kFusedMaxK;
+}
+
+hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,
+                                       const uint32_t *masks, void *scan_ws, int k,
+                                       int32_t *idx, const float *q, const uint16_t *K,
+                                       const uint16_t *V, float sm_scale, uint16_t *out,
+                                       hipStream_t s) {
+    FilterArgs fa;
+    fa.masks = masks;
+    fa.scan_ws = static_cast<const char *>(scan_ws);
+    fa.planes = st.planes;
+    fa.word_stride = st.word_stride;
+    fa.W = (st.n_tokens + 31) / 32;
+    fa.cstride = cand_stride(st.n_tokens);
+    fa.G = G;
+    fa.H = st.n_heads;
+    fa.qs = query_sets(G);
+    const int R = st.n_heads * G;
+    hipLaunchKernelGGL(k_select_attend, dim3(1, R), dim3(kThreads), 0, s, cand,
+                       (int64_t)st.n_tokens, 0, k, fa, idx, q, K, V, sm_scale, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand,

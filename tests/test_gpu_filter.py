@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 from bit_plane_kv_amd import fathom as F
+from bit_plane_kv_amd import synth
 
 from gpu_util import bf16_to_f32, inputs, store_from_keys, to_dev, torch_cuda
 
@@ -181,11 +182,22 @@ def test_scan_topk_repairs_rows_that_kept_too_few(H, G, n, k):
     assert (cnt < k).any()   # the repair ran on at least one row
 
 
-def test_step_filtered_equals_step_full():
+@pytest.mark.parametrize("H,G,n,k,boost", [
+    (4, 4, 20000, 256, False),   # one layer's shape: select and attention in one kernel
+    (2, 4, 32768, 512, True),    # ... and rows it must rescore (the sample boosted)
+    (1, 4, 32768, 1024, False),  # the largest k of the fused kernel
+    (70, 4, 3000, 64, False),    # more than 256 rows: select, redo, then attention
+])
+def test_step_filtered_equals_step_full(H, G, n, k, boost):
+    """The filtered step (scan with the keep test, select, attention) against the full
+    step (every score written, full top-k, attention): the same winners and outputs."""
     torch = torch_cuda()
-    H, G, n, B, k = 4, 4, 20000, 92, 256
-    print(f"[step filtered] H={H} G={G} n={n} B={B} k={k}", flush=True)
+    B = 92
+    print(f"[step filtered] H={H} G={G} n={n} B={B} k={k} boost={boost}", flush=True)
     keys, q, K, V = inputs(102, H, G, n)
+    if boost:
+        keys = _boost_sampled_tokens(keys, q)
+        K = synth.bf16_bits(keys)
     st, _ = store_from_keys(keys)
     q_t = to_dev(q)
     Kd = to_dev(K).view(torch.bfloat16)
