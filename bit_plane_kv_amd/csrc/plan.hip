@@ -11,8 +11,8 @@ __global__ __launch_bounds__(256) void k_plan(const float *__restrict__ q,
     __shared__ int cnt[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
     float qp[FATHOM_MAX_G], vp;
-    plan_load(q, var, G, h, qp, vp);
-    plan_from(qp, vp, G, B, cnt);
+    plan_load<256>(q, var, G, h, qp, vp);
+    plan_from<256>(qp, vp, G, B, cnt);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)cnt[tid];
 }
 

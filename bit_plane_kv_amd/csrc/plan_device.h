@@ -41,16 +41,18 @@ __device__ __forceinline__ double plan_importance(const float (&qc)[FATHOM_MAX_G
     return sq * (double)v;
 }
 
-// The channel a thread plans: two threads per channel.
-__device__ __forceinline__ int plan_channel() { return (int)(threadIdx.x >> 1); }
+// The channel a thread plans: NT / 128 threads per channel (NT = 256 or 512).
+template <int NT>
+__device__ __forceinline__ int plan_channel() { return (int)threadIdx.x / (NT / kD); }
 
 // Loads the plan's inputs of this thread's channel: its G queries and its variance.
 // Every load is unconditional (query clamped to a real one) so that all of them are in
 // flight together; the unused values are zeroed afterwards.
+template <int NT>
 __device__ __forceinline__ void plan_load(const float *__restrict__ q,
                                           const float *__restrict__ var, int G, int h,
                                           float (&qp)[FATHOM_MAX_G], float &vp) {
-    const int c = plan_channel();
+    const int c = plan_channel<NT>();
 #pragma unroll
     for (int g = 0; g < FATHOM_MAX_G; ++g) qp[g] = q[((size_t)h * G + min(g, G - 1)) * kD + c];
     vp = var[(size_t)h * kD + c];
@@ -59,7 +61,8 @@ __device__ __forceinline__ void plan_load(const float *__restrict__ q,
 }
 
 // Whole plan of head h from the loaded inputs: each channel's depth to cnt[0..127]
-// (LDS); 256 threads; ends with a barrier, so cnt is complete for every thread.
+// (LDS); NT threads (256 or 512: 2 or 4 a channel); ends with a barrier, so cnt is
+// complete for every thread.
 //
 // Importances are compared by their bit patterns: for non-negative doubles (-0 is made
 // +0) the unsigned 64-bit order of the bits is the numeric order and equal bits are
@@ -67,83 +70,108 @@ __device__ __forceinline__ void plan_load(const float *__restrict__ q,
 // channel first) only matters between equal importances; they are found by counting
 // the channels at each strict rank (the number of larger importances), and only the
 // channels that share one count the lower channels they tie with.
+template <int NT>
 __device__ __forceinline__ void plan_from(const float (&qp)[FATHOM_MAX_G], float vp, int G,
                                           int B, int *cnt) {
+    constexpr int TPC = NT / kD;  // threads per channel: 2 or 4
+    static_assert(TPC == 2 || TPC == 4, "2 or 4 threads a channel");
     __shared__ __align__(16) unsigned long long wkey[kD];  // by channel
     __shared__ __align__(16) unsigned long long skey[kD];  // in (w desc, c asc) order
     __shared__ int sch[kD];                                // the channel at each place
     __shared__ int nrank[kD];                              // channels per strict rank
-    const int tid = threadIdx.x, c = plan_channel(), half = tid & 1;
+    const int tid = threadIdx.x, c = plan_channel<NT>(), part = tid % TPC;
     const double w = plan_importance(qp, vp, G) + 0.0;  // -0 -> +0
     const unsigned long long bw = (unsigned long long)__double_as_longlong(w);
-    if (!half) wkey[c] = bw;
-    else nrank[c] = 0;
+    if (part == 0) wkey[c] = bw;
+    else if (part == 1) nrank[c] = 0;
     __syncthreads();
-    // strict rank: each thread counts the larger importances in one half of the channels
+    // strict rank: each of the channel's threads counts the larger importances in its
+    // share of the channels
+    constexpr int kShare = kD / TPC;
     int r0 = 0, r1 = 0;
 #pragma unroll
-    for (int o = 64 * half; o < 64 * half + 64; o += 2) {
+    for (int o = kShare * part; o < kShare * part + kShare; o += 2) {
         const ulonglong2 x = *reinterpret_cast<const ulonglong2 *>(&wkey[o]);
         r0 += x.x > bw;
         r1 += x.y > bw;
     }
     int strict = r0 + r1;
-    strict += __shfl_xor(strict, 1, 64);
-    if (!half) atomicAdd(&nrank[strict], 1);
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1) strict += __shfl_xor(strict, o, 64);
+    if (part == 0) atomicAdd(&nrank[strict], 1);
     __syncthreads();
     int rank = strict;
     if (nrank[strict] > 1) {  // equal importances: the lower channels come first
-        int before = 0;       // (both threads of the channel take this branch)
-        for (int o = half; o < c; o += 2) before += wkey[o] == bw;
-        rank += before + __shfl_xor(before, 1, 64);
+        int before = 0;       // (all threads of the channel take this branch)
+        for (int o = part; o < c; o += TPC) before += wkey[o] == bw;
+#pragma unroll
+        for (int o = 1; o < TPC; o <<= 1) before += __shfl_xor(before, o, 64);
+        rank += before;
     }
-    if (!half) {
+    if (part == 0) {
         skey[rank] = bw;
         sch[rank] = c;
     }
     __syncthreads();
-    // P[j + 3] = pos(w 4^j, c), j = -3 .. 3.  j = 0 is the channel's own rank; thread
-    // half 0 searches j = -3 .. -1, half 1 j = 1 .. 3.  Channels before (X, c) form a
-    // prefix of the sorted order: its length is found from the last key of each group
-    // of 16 (the same 8 keys for every thread), then by four halving steps inside the
-    // group, then past the channels whose importance equals X and whose index is lower.
-    unsigned long long bx[3];
-    int pos[3];
+    // P[j + 3] = pos(w 4^j, c), j = -3 .. 3.  j = 0 is the channel's own rank; the other
+    // six are shared by the channel's threads (2 threads: j = -3..-1 and 1..3; 4 threads:
+    // -3, -2 | -1 | 1 | 2, 3).  Channels before (X, c) form a prefix of the sorted order:
+    // its length is found from the last key of each group of 16 (the same 8 keys for
+    // every thread), then by four halving steps inside the group, then past the channels
+    // whose importance equals X and whose index is lower.
+    constexpr int NS = 6 / TPC + (TPC == 4 ? 1 : 0);  // searches a thread: 3 or 2
+    int js[NS];
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const double X = ldexp(w, 2 * (half ? s + 1 : s - 3));
-        bx[s] = (unsigned long long)__double_as_longlong(X);
-        pos[s] = 0;
+    for (int i = 0; i < NS; ++i) {
+        if (TPC == 2) js[i] = part ? i + 1 : i - 3;
+        else js[i] = part == 0 ? i - 3 : part == 3 ? i + 2 : (i == 0 ? (part == 1 ? -1 : 1) : 0);
+    }
+    unsigned long long bx[NS];
+    int pos[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const double X = ldexp(w, 2 * js[i]);
+        bx[i] = (unsigned long long)__double_as_longlong(X);
+        pos[i] = 0;
     }
     constexpr int kSeg = 16;
 #pragma unroll
     for (int b = 0; b < kD / kSeg; ++b) {
         const unsigned long long last = skey[kSeg * b + kSeg - 1];
 #pragma unroll
-        for (int s = 0; s < 3; ++s) pos[s] += kSeg * (last > bx[s]);
+        for (int i = 0; i < NS; ++i) pos[i] += kSeg * (last > bx[i]);
     }
 #pragma unroll
     for (int step = kSeg / 2; step > 0; step >>= 1) {
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-            const unsigned long long e = skey[min(pos[s] + step - 1, kD - 1)];
-            if (pos[s] < kD && e > bx[s]) pos[s] += step;
+        for (int i = 0; i < NS; ++i) {
+            const unsigned long long e = skey[min(pos[i] + step - 1, kD - 1)];
+            if (pos[i] < kD && e > bx[i]) pos[i] += step;
         }
     }
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        if (pos[s] < kD && skey[pos[s]] == bx[s]) {
-            while (pos[s] < kD && skey[pos[s]] == bx[s] && sch[pos[s]] < c) ++pos[s];
+    for (int i = 0; i < NS; ++i) {
+        if (pos[i] < kD && skey[pos[i]] == bx[i]) {
+            while (pos[i] < kD && skey[pos[i]] == bx[i] && sch[pos[i]] < c) ++pos[i];
         }
     }
     int P[7];
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const int other = __shfl_xor(pos[s], 1, 64);
-        P[s] = half ? other : pos[s];       // j = s - 3
-        P[s + 4] = half ? pos[s] : other;   // j = s + 1
-    }
     P[3] = rank;
+    const int base = (int)(threadIdx.x & 63) & ~(TPC - 1);  // the channel's first lane
+    if (TPC == 2) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            P[i] = __shfl(pos[i], base, 64);          // j = i - 3
+            P[i + 4] = __shfl(pos[i], base + 1, 64);  // j = i + 1
+        }
+    } else {
+        P[0] = __shfl(pos[0], base, 64);      // -3
+        P[1] = __shfl(pos[1], base, 64);      // -2
+        P[2] = __shfl(pos[0], base + 1, 64);  // -1
+        P[4] = __shfl(pos[0], base + 2, 64);  // 1
+        P[5] = __shfl(pos[0], base + 3, 64);  // 2
+        P[6] = __shfl(pos[1], base + 3, 64);  // 3
+    }
     int depth = 0;
 #pragma unroll
     for (int t = 0; t < kPlanes; ++t) {
@@ -152,7 +180,7 @@ __device__ __forceinline__ void plan_from(const float (&qp)[FATHOM_MAX_G], float
         for (int tp = 0; tp < kPlanes; ++tp) r += P[tp - t + 3];
         depth += r < B;
     }
-    if (!half) cnt[c] = depth;
+    if (part == 0) cnt[c] = depth;
     __syncthreads();
 }
 

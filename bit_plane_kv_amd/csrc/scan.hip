@@ -36,12 +36,12 @@ namespace {
 // One K-pair: w[h][p][pos] = word pos of plane s (p = 0) / s+4 (p = 1) of group q + 4h.
 // kHi: the upper 4 groups exist; without them their operand bytes are zero and their
 // words are neither transposed nor masked.
-template <int QS, bool kFirst, bool kHi>
-__device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4i (&A)[QS],
-                                          int s, bool hi, v4i (&acc)[2][8][QS]) {
+template <int QS, bool kFirst, bool kHi, int NP = 2>
+__device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][NP], const v4i (&A)[QS],
+                                          int s, bool hi, v4i (&acc)[NP][8][QS]) {
     const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int pos = 0; pos < 2; ++pos) {
+    for (int pos = 0; pos < NP; ++pos) {
         uint32_t x[2][2];  // [half][planes 0-3 / 4-7]
 #pragma unroll
         for (int h = 0; h < (kHi ? 2 : 1); ++h) {
@@ -64,14 +64,15 @@ __device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][2], const v4
     }
 }
 
-template <int QS>
-__device__ __forceinline__ void mma_item(const uint32_t (&w)[2][2][2], const v4i (&A)[QS], int s,
-                                         bool first, bool hi, v4i (&acc)[2][8][QS]) {
-    if (first) mma_kpair<QS, true, true>(w, A, s, hi, acc);
-    else mma_kpair<QS, false, true>(w, A, s, hi, acc);
+// NP words per lane (2 in the scan; 1 in the threshold sample of a 512-thread prepare)
+template <int QS, int NP = 2>
+__device__ __forceinline__ void mma_item(const uint32_t (&w)[2][2][NP], const v4i (&A)[QS], int s,
+                                         bool first, bool hi, v4i (&acc)[NP][8][QS]) {
+    if (first) mma_kpair<QS, true, true, NP>(w, A, s, hi, acc);
+    else mma_kpair<QS, false, true, NP>(w, A, s, hi, acc);
 }
 
-// Candidate thresholds of one head (256 threads).  A guess of each query's score
+// Candidate thresholds of one head (NT threads: 256 or 512).  A guess of each query's score
 // quantile from a sample of the head's tokens (sample_run_word): the sampled tokens are
 // scored exactly as the scan scores them -- the same operand records, matrix-core digit
 // sums and fp32 combine -- and the sample_rank-th largest sampled key is the threshold,
@@ -79,28 +80,33 @@ __device__ __forceinline__ void mma_item(const uint32_t (&w)[2][2][2], const v4i
 // Only the count of kept tokens decides correctness, and the select checks it.  The
 // sampled words of up to 128 planes (two K-pairs) at a time are staged in LDS, 16 bytes
 // per (plane, run), all in flight together (those of the first 128 planes are loaded by
-// sample_issue as soon as the plane list is known); wave v then takes sampled words
-// 8v .. 8v+7 the way a scan wave takes its 8 words of a super-step.
+// sample_issue as soon as the plane list is known); each wave then takes its share of
+// the sampled words (8 of 4 waves, 4 of 8) the way a scan wave takes its 8 words of a
+// super-step.
 constexpr int kSamplePlanes = 128;
-constexpr int kSamplePer = kSamplePlanes * kSampleRuns / 256;  // 16-byte loads a thread
-static_assert(kSampleWords == 32, "four waves of 8 sampled words");
+static_assert(kSampleWords == 32, "32 sampled words: 8 a wave of 4, 4 a wave of 8");
 
-// Loads (plane p0 + e / 8, run e % 8), e = tid + 256 u, of the head's plane list pl
+// Loads (plane p0 + e / 8, run e % 8), e = tid + NT u, of the head's plane list pl
 // (np planes from p0).  Every load is unconditional -- a plane past the list reads the
 // store's row 0, a run past a short row the row's first 16 bytes -- so that the
 // compiler keeps them all in flight; sample_stage drops those values.
+template <int NT>
+constexpr int sample_per() { return kSamplePlanes * kSampleRuns / NT; }  // loads a thread
+
+template <int NT>
 __device__ __forceinline__ void sample_issue(const uint32_t *__restrict__ hp, int W,
                                              int word_stride, const uint32_t *pl, int p0,
-                                             int np, uint4 (&v)[kSamplePer]) {
-    uint32_t row[kSamplePer];
+                                             int np, uint4 (&v)[sample_per<NT>()]) {
+    constexpr int SP = sample_per<NT>();
+    uint32_t row[SP];
 #pragma unroll
-    for (int u = 0; u < kSamplePer; ++u) {  // every list read first (p0 + p < 512 always)
-        const int p = (threadIdx.x + 256 * u) / kSampleRuns;
+    for (int u = 0; u < SP; ++u) {  // every list read first (p0 + p < 512 always)
+        const int p = (threadIdx.x + NT * u) / kSampleRuns;
         row[u] = pl[p0 + p];
     }
 #pragma unroll
-    for (int u = 0; u < kSamplePer; ++u) {
-        const int e = threadIdx.x + 256 * u;
+    for (int u = 0; u < SP; ++u) {
+        const int e = threadIdx.x + NT * u;
         const int p = e / kSampleRuns, r = e % kSampleRuns;
         const int w0 = sample_run_word(r, W);
         // a run that starts below W lies in the row (word_stride >= 4 * ceil(W / 4))
@@ -110,11 +116,12 @@ __device__ __forceinline__ void sample_issue(const uint32_t *__restrict__ hp, in
 }
 // Writes the loaded values of real (plane, run) pairs to sw; a run past a short row is
 // zero.  Rows of sw past np keep whatever they hold: their planes have zero weights.
-__device__ __forceinline__ void sample_stage(const uint4 (&v)[kSamplePer], int W, int np,
+template <int NT>
+__device__ __forceinline__ void sample_stage(const uint4 (&v)[sample_per<NT>()], int W, int np,
                                              uint32_t (*sw)[kSampleWords]) {
 #pragma unroll
-    for (int u = 0; u < kSamplePer; ++u) {
-        const int e = threadIdx.x + 256 * u;
+    for (int u = 0; u < sample_per<NT>(); ++u) {
+        const int e = threadIdx.x + NT * u;
         const int p = e / kSampleRuns, r = e % kSampleRuns;
         const bool live = sample_run_word(r, W) < W;
         if (p < np)
@@ -188,11 +195,11 @@ __device__ __forceinline__ uint32_t sample_quantile(const uint32_t (&kk)[16], ui
 
 // la: the head's A operand halves [K-block][lane][QS] (8 bytes, as in the records);
 // C, S: each query's constant term and weight unit as the scan reads them.
-template <int QS>
+template <int QS, int NT>
 __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ planes, int n,
                                                   int word_stride, int k, int h,
                                                   int nplanes, int nkb, const uint32_t *pl,
-                                                  const uint4 (&first)[kSamplePer],
+                                                  const uint4 (&first)[sample_per<NT>()],
                                                   const uint2 *la, const float *C,
                                                   const float *S, uint32_t *tk,
                                                   ScanMeta *meta) {
@@ -208,17 +215,19 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
     const uint32_t m = (uint32_t)sample_rank(n, k);
     const uint32_t *hp = planes + (size_t)h * kMaxPlanesPerHead * word_stride;
     const int npr = (nkb + 1) >> 1;  // K-pairs (nkb >= 1)
-    v4i acc[2][8][QS];
+    constexpr int WPW = kSampleWords / (NT / 64);  // sampled words a wave: 8 or 4
+    constexpr int NP = WPW / 4;                    // words a lane: 2 or 1
+    v4i acc[NP][8][QS];
     for (int kp0 = 0; kp0 < npr; kp0 += 2) {  // batches of two K-pairs (128 planes)
         const int p0 = 64 * kp0;
         const int np = max(0, min(kSamplePlanes, nplanes - p0));
         if (kp0) __syncthreads();  // the previous batch is no longer read
         if (kp0 == 0) {
-            sample_stage(first, W, np, sw);
+            sample_stage<NT>(first, W, np, sw);
         } else {
-            uint4 v[kSamplePer];
-            sample_issue(hp, W, word_stride, pl, p0, np, v);
-            sample_stage(v, W, np, sw);
+            uint4 v[sample_per<NT>()];
+            sample_issue<NT>(hp, W, word_stride, pl, p0, np, v);
+            sample_stage<NT>(v, W, np, sw);
         }
         __syncthreads();
 #pragma unroll
@@ -226,15 +235,15 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             const int kp = kp0 + kk;
             if (kp >= npr) break;
             const bool hi = 2 * kp + 1 < nkb;  // upper 4 groups of the K-pair exist
-            uint32_t w[2][2][2];
+            uint32_t w[2][2][NP];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-                    for (int pos = 0; pos < 2; ++pos)
+                    for (int pos = 0; pos < NP; ++pos)
                         w[hh][pp][pos] =
-                            sw[64 * kk + 8 * (jq + 4 * hh) + s + 4 * pp][8 * wave + 2 * wq + pos];
+                            sw[64 * kk + 8 * (jq + 4 * hh) + s + 4 * pp][WPW * wave + NP * wq + pos];
             v4i A[QS];
 #pragma unroll
             for (int set = 0; set < QS; ++set) {
@@ -242,7 +251,7 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
                 const uint2 ahi = hi ? la[((2 * kp + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
                 A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
             }
-            mma_item<QS>(w, A, s, kp == 0, hi, acc);
+            mma_item<QS, NP>(w, A, s, kp == 0, hi, acc);
         }
     }
     const bool small = nkb < kMaxKBlocks;
@@ -251,8 +260,8 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
         __syncthreads();  // the staged words (or the previous set's keys) are no longer read
         const int g = 4 * set + jq;
 #pragma unroll
-        for (int pos = 0; pos < 2; ++pos) {
-            const int i = 8 * wave + 2 * wq + pos;  // sampled word
+        for (int pos = 0; pos < NP; ++pos) {
+            const int i = WPW * wave + NP * wq + pos;  // sampled word
             const int word = sample_run_word(i / kSampleRunWords, W) + i % kSampleRunWords;
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) {
@@ -262,7 +271,7 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             }
         }
         __syncthreads();
-        {   // wave gq: the m-th largest sampled key of query 4*set + gq
+        if (wave < 4) {  // wave gq: the m-th largest sampled key of query 4*set + gq
             const int gq = wave;
             constexpr int kPerLane = kST / 64;
             uint32_t kk[kPerLane];
@@ -328,13 +337,16 @@ __device__ __forceinline__ void load_prep_in(const float *__restrict__ q,
 }
 
 // Body of the prepare step for head h; tc[c] (LDS, complete) holds the channel depths.
-// 256 threads.
-template <int QS>
+// NT threads: 512 for one query set, 256 for two (whose registers allow no more).
+template <int QS, int NT>
 __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc, int H,
                                              int G, const uint32_t *__restrict__ planes, int n,
                                              int word_stride, int k, char *__restrict__ ws,
                                              int h) {
     constexpr int NQ = 4 * QS;
+    constexpr int NW = NT / 64;                       // waves
+    constexpr int QT = NT / kD;                       // threads per channel
+    constexpr int WPQ = NW / NQ > 1 ? NW / NQ : 1;    // waves per query in the weight pass
     __shared__ int off[kD + 1];
     __shared__ uint32_t pl[kMaxPlanesPerHead];
     __shared__ double wt[NQ][kMaxPlanesPerHead];
@@ -349,6 +361,8 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     ScanMeta *meta = reinterpret_cast<ScanMeta *>(ws + (size_t)h * kMetaBytes);
     uint32_t *rec = reinterpret_cast<uint32_t *>(ws + (size_t)H * kMetaBytes +
                                                  (size_t)h * kMaxKBlocks * 64 * 16 * QS);
+    __shared__ unsigned long long rbi[NQ], mai[NQ];  // digit-sum bounds, summed by waves
+    if (tid < NQ) rbi[tid] = mai[tid] = 0ull;
     if (tid < 64) {  // one wave: exclusive prefix sum of the depths, 2 channels a lane
         const int a = tc[2 * lane], b = tc[2 * lane + 1];
         int inc = a + b;
@@ -367,7 +381,7 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     const int ngroups = (nplanes + kGroupBits - 1) / kGroupBits;
     // at least one K-block, so that a head with no planes still writes its constants
     const int nkb = max(1, (ngroups + kKBlockGroups - 1) / kKBlockGroups);
-    {   // thread t: channel t mod 128, queries t / 128, t / 128 + 2, ...
+    {   // thread t: channel t mod 128, queries t / 128, t / 128 + QT, ...
         const int c = tid & (kD - 1), half = tid >> 7, t = tc[c], o = off[c];
         const double s = (double)in.s;
         const double z = (double)in.z;
@@ -376,7 +390,7 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
             for (int j = 0; j < t; ++j) pl[o + j] = (uint32_t)(c * kPlanes + j);
 #pragma unroll
         for (int g = 0; g < NQ; ++g) {
-            if ((g & 1) != half) continue;
+            if (g % QT != half) continue;
             const double qv = (double)in.q[g];
             for (int j = 0; j < t; ++j) wt[g][o + j] = (qv * s) * (double)(8 >> j);
             red[g][c] = qv * (z + s * hm);  // this channel's share of C_g
@@ -385,15 +399,15 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     }
     __syncthreads();
     // the threshold sample's first loads go out now and land during the work below
-    uint4 first[kSamplePer];
+    uint4 first[sample_per<NT>()];
     if (k > 0)
-        sample_issue(planes + (size_t)h * kMaxPlanesPerHead * word_stride, (n + 31) >> 5,
-                     word_stride, pl, 0, min(nplanes, kSamplePlanes), first);
+        sample_issue<NT>(planes + (size_t)h * kMaxPlanesPerHead * word_stride, (n + 31) >> 5,
+                         word_stride, pl, 0, min(nplanes, kSamplePlanes), first);
     // C_g (a sum over the channels) and the weight unit of each query (from the largest
     // |weight|): wave v takes queries v, v + 4.  Lane l first adds channels l and l + 64,
     // then a butterfly over the lanes halves the distance each step, so lane 0 adds the
     // same pairs in the same order as a halving tree over the 128 channels.
-    for (int g = tid >> 6; g < NQ; g += 4) {
+    for (int g = tid >> 6; g < NQ; g += NW) {
         double sum = red[g][lane] + red[g][lane + 64];
         double mx = fmax(amx[g][lane], amx[g][lane + 64]);
 #pragma unroll
@@ -413,12 +427,12 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     // 65536) so that its signed base-256 digits are plain bytes (weight_byte); written
     // over the weight it comes from.  The same pass sums, per query, |M| and
     // |D0 + 256 D1| of M's digits (the part of a weight the filter's integer test does
-    // not see): integer sums, exact in any order.  Wave v takes queries v, v + 4.
+    // not see): integer sums, exact in any order.  WPQ waves share a query's planes.
     long long(*Mu)[kMaxPlanesPerHead] = reinterpret_cast<long long(*)[kMaxPlanesPerHead]>(wt);
-    __shared__ double rb[NQ], mabs[NQ];
-    for (int g = tid >> 6; g < NQ; g += 4) {
+    for (int gw = tid >> 6; gw < NQ * WPQ; gw += NW) {
+        const int g = gw % NQ, wp = gw / NQ;
         long long r = 0, a = 0;
-        for (int p = lane; p < nplanes; p += 64) {
+        for (int p = lane + 64 * wp; p < nplanes; p += 64 * WPQ) {
             const long long u = (g < G ? llrint(wt[g][p] * inv_unit[g]) : 0LL) + kDigitBias;
             Mu[g][p] = u;
             const int d0 = (int)(int8_t)(uint8_t)weight_byte(u, 0);
@@ -430,11 +444,11 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         r = (long long)__ockl_wfred_add_u64((unsigned long long)r);  // both sums are >= 0
         a = (long long)__ockl_wfred_add_u64((unsigned long long)a);
         if (lane == 0) {
-            rb[g] = (double)r;
-            mabs[g] = (double)a;
+            atomicAdd(&rbi[g], (unsigned long long)r);
+            atomicAdd(&mai[g], (unsigned long long)a);
         }
     }
-    for (int p = tid; p < nplanes; p += 256) meta->plane[p] = pl[p];
+    for (int p = tid; p < nplanes; p += NT) meta->plane[p] = pl[p];
     if (tid < FATHOM_MAX_G) {
         meta->C[tid] = tid < G ? (float)csum[tid] : 0.0f;
         meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
@@ -451,7 +465,7 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
     }
     __syncthreads();
     // operand records: lane ln of K-block kbl serves group 4*kbl + (ln >> 4)
-    for (int e = tid; e < nkb * 64; e += 256) {
+    for (int e = tid; e < nkb * 64; e += NT) {
         const int kbl = e >> 6, ln = e & 63;
         const int grp = kbl * kKBlockGroups + (ln >> 4);
         const int s = ln & 3, r = ln & 15;
@@ -486,18 +500,24 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         return;
     }
     __shared__ uint32_t tk[NQ];
-    sample_thresholds<QS>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
-                          tk, meta);
+    sample_thresholds<QS, NT>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
+                              tk, meta);
     __syncthreads();  // the thresholds and the sums are complete
     if (tid < NQ * 8) {
         const int g = tid >> 3, m = tid & 7;
-        meta->xthr[g][m] = filter_threshold(g < G, tk[g], cf[g], sf[g], rb[g], mabs[g], m);
+        meta->xthr[g][m] = filter_threshold(g < G, tk[g], cf[g], sf[g], (double)rbi[g],
+                                            (double)mai[g], m);
     }
     if (tid >= NQ * 8 && tid < FATHOM_MAX_G * 8) meta->xthr[tid >> 3][tid & 7] = 0;
 }
 
+// Threads of a prepare workgroup: 512 for one query set (its 212 registers allow two
+// waves a SIMD), 256 for two.
 template <int QS>
-__global__ __launch_bounds__(256) void k_scan_prepare(
+constexpr int prep_threads() { return QS == 1 ? 512 : 256; }
+
+template <int QS>
+__global__ __launch_bounds__(prep_threads<QS>()) void k_scan_prepare(
     const float *__restrict__ q, const uint8_t *__restrict__ depth,
     const float *__restrict__ scale, const float *__restrict__ zero, int H, int G,
     const uint32_t *__restrict__ planes, int n, int word_stride, int k,
@@ -509,13 +529,13 @@ __global__ __launch_bounds__(256) void k_scan_prepare(
     const int t = depth[(size_t)h * kD + min(tid, kD - 1)];
     if (tid < kD) tc[tid] = min(t, kPlanes);
     __syncthreads();
-    prepare_head<QS>(in, tc, H, G, planes, n, word_stride, k, ws, h);
+    prepare_head<QS, prep_threads<QS>()>(in, tc, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // A decode step's plan and prepare in one kernel: the depths stay in LDS between them
 // (and are also written to `depth`).  Every input of both is loaded up front.
 template <int QS>
-__global__ __launch_bounds__(256) void k_plan_prepare(
+__global__ __launch_bounds__(prep_threads<QS>()) void k_plan_prepare(
     const float *__restrict__ q, const float *__restrict__ var,
     const float *__restrict__ scale, const float *__restrict__ zero, int H, int G, int B,
     const uint32_t *__restrict__ planes, int n, int word_stride, int k,
@@ -525,10 +545,11 @@ __global__ __launch_bounds__(256) void k_plan_prepare(
     PrepIn<QS> in;
     load_prep_in<QS>(q, scale, zero, G, h, in);
     float qp[FATHOM_MAX_G], vp;
-    plan_load(q, var, G, h, qp, vp);
-    plan_from(qp, vp, G, B, tc);
+    constexpr int NT = prep_threads<QS>();
+    plan_load<NT>(q, var, G, h, qp, vp);
+    plan_from<NT>(qp, vp, G, B, tc);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];
-    prepare_head<QS>(in, tc, H, G, planes, n, word_stride, k, ws, h);
+    prepare_head<QS, NT>(in, tc, H, G, planes, n, word_stride, k, ws, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1079,28 +1100,30 @@ hipError_t launch_main_q(const fathom_store &st, int G, float *scores, const cha
 hipError_t launch_scan_prepare(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, int k, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
-    const dim3 grid(st.n_heads), block(256);
+    const dim3 grid(st.n_heads);
     if (query_sets(G) == 1)
-        hipLaunchKernelGGL(k_scan_prepare<1>, grid, block, 0, s, q, depth, st.scale, st.zero,
-                           st.n_heads, G, st.planes, st.n_tokens, st.word_stride, k, w);
+        hipLaunchKernelGGL(k_scan_prepare<1>, grid, dim3(prep_threads<1>()), 0, s, q, depth,
+                           st.scale, st.zero, st.n_heads, G, st.planes, st.n_tokens,
+                           st.word_stride, k, w);
     else
-        hipLaunchKernelGGL(k_scan_prepare<2>, grid, block, 0, s, q, depth, st.scale, st.zero,
-                           st.n_heads, G, st.planes, st.n_tokens, st.word_stride, k, w);
+        hipLaunchKernelGGL(k_scan_prepare<2>, grid, dim3(prep_threads<2>()), 0, s, q, depth,
+                           st.scale, st.zero, st.n_heads, G, st.planes, st.n_tokens,
+                           st.word_stride, k, w);
     return hipGetLastError();
 }
 
 hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, int B, int k,
                                uint8_t *depth, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
-    const dim3 grid(st.n_heads), block(256);
+    const dim3 grid(st.n_heads);
     if (query_sets(G) == 1)
-        hipLaunchKernelGGL(k_plan_prepare<1>, grid, block, 0, s, q, st.var, st.scale, st.zero,
-                           st.n_heads, G, B, st.planes, st.n_tokens, st.word_stride, k,
-                           depth, w);
+        hipLaunchKernelGGL(k_plan_prepare<1>, grid, dim3(prep_threads<1>()), 0, s, q, st.var,
+                           st.scale, st.zero, st.n_heads, G, B, st.planes, st.n_tokens,
+                           st.word_stride, k, depth, w);
     else
-        hipLaunchKernelGGL(k_plan_prepare<2>, grid, block, 0, s, q, st.var, st.scale, st.zero,
-                           st.n_heads, G, B, st.planes, st.n_tokens, st.word_stride, k,
-                           depth, w);
+        hipLaunchKernelGGL(k_plan_prepare<2>, grid, dim3(prep_threads<2>()), 0, s, q, st.var,
+                           st.scale, st.zero, st.n_heads, G, B, st.planes, st.n_tokens,
+                           st.word_stride, k, depth, w);
     return hipGetLastError();
 }
 
