@@ -488,27 +488,34 @@ def kernel_times(F, st, q, K, V, B, k, sm, depth, scores, idx, out, dev, stream,
     return res
 
 
-TRAFFIC_FILES = {  # kernel -> (counter summary under profiles/, the source it was taken on)
-    "scan_full": ("scan_traffic.json", "scan.hip"),
-    "scan_filter": ("scan_filter_traffic.json", "scan.hip"),
-    "attn": ("attn_traffic.json", "attn.hip"),
-    "scan_extract": ("scan_extract_counters.json", "scan_extract.hip"),
+TRAFFIC_FILES = {  # kernel -> (counter summary under profiles/, the sources it was taken on)
+    "scan_full": ("scan_traffic.json", ("scan.hip",)),
+    "scan_filter": ("scan_filter_traffic.json", ("scan.hip",)),
+    "attn": ("attn_traffic.json", ("attn.hip", "attn_device.h")),
+    "scan_extract": ("scan_extract_counters.json", ("scan_extract.hip",)),
 }
+
+
+def sources_sha256(names):
+    """sha256 of the named sources under bit_plane_kv_amd/csrc, concatenated in order (one
+    file: that file's own sha256)."""
+    import hashlib
+    h = hashlib.sha256()
+    for nm in names:
+        h.update(open(os.path.join(ROOT, "bit_plane_kv_amd", "csrc", nm), "rb").read())
+    return h.hexdigest()
 
 
 def load_counters(kernel):
     """The instruction counters of a kernel from its committed rocprofv3 summary (a JSON
     object), if the summary was taken on the current source of that kernel; else None."""
-    import hashlib
-    name, srcname = TRAFFIC_FILES[kernel]
+    name, srcs = TRAFFIC_FILES[kernel]
     path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", srcname)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != digest:
+        if rec.get("source_sha256") != sources_sha256(srcs):
             return None
         return rec.get("counters")
     except Exception:
@@ -518,16 +525,13 @@ def load_counters(kernel):
 def load_traffic(kernel):
     """HBM bytes per launch of a kernel from its committed rocprofv3 counter summary, if
     the summary was taken on the current source of that kernel; else None."""
-    import hashlib
-    name, srcname = TRAFFIC_FILES[kernel]
+    name, srcs = TRAFFIC_FILES[kernel]
     path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "bit_plane_kv_amd", "csrc", srcname)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256", rec.get("scan_hip_sha256")) != digest:
+        if rec.get("source_sha256") != sources_sha256(srcs):
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:
