@@ -80,7 +80,8 @@ inline size_t scan_ws_bytes(int H, int G) {
 // low part R = D0 + 256 D1 (int32: heads of more than 480 planes, where that sum could
 // overflow, keep no records and have all their rows rescored) -- goes, in token order, to the
 // front of its 256-token block of a [H][G][cand_stride(n)] area of 4-byte words (at
-// most kBlockRecords records a block; a block with more sets the row's ovf bit), and
+// most kBlockRecords records a block, 64 when a head has at most 4 queries; a block with
+// more sets the row's ovf bit), and
 // bit i of word w of a [H][G][ceil(n/32)] uint32 mask marks token 32w + i as kept.
 // The select turns each record into the scan's exact fp32 score and counts the
 // candidates whose score is >= T: with at least k of them the row's k-th largest score

@@ -64,6 +64,25 @@ __device__ __forceinline__ void mma_kpair(const uint32_t (&w)[2][2][NP], const v
     }
 }
 
+// One pass of a K-pair of the scan from operand dwords read with the LDS transpose read:
+// x[h][p] = byte s (8 tokens) of planes 4p .. 4p+3 of group q + 4h.
+template <int QS, bool kFirst>
+__device__ __forceinline__ void mma_pass_x(const uint32_t (&x)[2][2], const v4i (&A)[QS],
+                                           uint32_t hi_mask, v4i (&acc)[8][QS]) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint32_t mask = 0x01010101u << m;
+        const uint32_t mhi = mask & hi_mask;
+        const v4i b = v4i{(int)(x[0][0] & mask), (int)(x[0][1] & mask), (int)(x[1][0] & mhi),
+                          (int)(x[1][1] & mhi)};
+#pragma unroll
+        for (int set = 0; set < QS; ++set) {
+            const v4i c = kFirst ? v4i{0, 0, 0, 0} : acc[m][set];
+            acc[m][set] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[set], b, c, 0, 0, 0);
+        }
+    }
+}
+
 // NP words per lane (2 in the scan; 1 in the threshold sample of a 512-thread prepare)
 template <int QS, int NP = 2>
 __device__ __forceinline__ void mma_item(const uint32_t (&w)[2][2][NP], const v4i (&A)[QS], int s,
@@ -560,24 +579,27 @@ __global__ __launch_bounds__(prep_threads<QS>()) void k_plan_prepare(
 // the K of one 16x16x64 i8 MFMA.  For each K-pair the waves copy its 64 plane rows,
 // 32*kWaves contiguous bytes (whole cache lines) each, straight from global memory
 // into an LDS tile, 16 bytes a lane; after a barrier, wave v takes words 8v .. 8v+7 of
-// all 64 rows from the tile: lane 16*q + 4*w + s reads words 8v+2w and 8v+2w+1 of
-// planes s and s+4 of groups q and q+4.  A byte transpose across the quad gives lane s
-// byte s (8 tokens) of a group's 8 planes, so bit m of byte i is plane i's bit of token
-// 8s + m; masking bit m of every byte makes the MFMA column of token 8s + m (byte values
-// 0 / 2^m, and -128 for m = 7, divided out in the combine).  The MFMA output lane
-// 16*j + 4*w + s then holds query j's 4 digit sums for that token.  kTiles tiles
-// rotate, so the copies of the next K-pairs are in flight while one is used.
+// all 64 rows from the tile in two passes t of 4 words.  One LDS transpose read
+// (ds_read_b64_tr_b8: within each 16 lanes, lane i < 8 receives byte i of the 8 bytes
+// each even lane 2j read, lane 8 + i byte i of those of the odd lanes 2j + 1) per pass
+// and K-block half h: lane 16*q + 2*j + p of the 16 reads 8 bytes (2 words) of plane j of
+// group q + 4h, words 8v + 4t + 2p and the next, so that lane 16*q + 4*w + s receives
+// byte s of word 8v + 4t + w of the group's 8 planes -- bit m of byte i is plane i's bit
+// of token 8s + m of that word.  Masking bit m of every byte makes the MFMA column of that
+// token (byte values 0 / 2^m, and -128 for m = 7, divided out in the combine).  The MFMA
+// output lane 16*j + 4*w + s then holds query j's 4 digit sums for that token.  kTiles
+// tiles rotate, so the copies of the next K-pairs are in flight while one is used.
 #ifndef FATHOM_SCAN_WAVES
 #define FATHOM_SCAN_WAVES 8
 #endif
-constexpr int kWaves = FATHOM_SCAN_WAVES;     // waves per workgroup (4, 8 or 16)
-static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "workgroup shape");
+constexpr int kWaves = FATHOM_SCAN_WAVES;     // waves per workgroup (8 or 16)
+static_assert(kWaves == 8 || kWaves == 16, "workgroup shape: rows of at least 16 chunks");
 constexpr int kScanThreads = 64 * kWaves;
 constexpr int kSuperWords = 8 * kWaves;       // words per super-step
 constexpr int kRowChunks = kSuperWords / 4;   // 16-byte chunks of a row per super-step
 constexpr int kCopyRows = 64 / kRowChunks;    // rows one copy instruction moves
-constexpr int kGroupBytes = 8 * 16 * kRowChunks + 128;  // a group's 8 rows; the extra
-                                      // 128 bytes start odd groups half-way round the banks
+constexpr int kRowBytes = 16 * kRowChunks;    // one row of a super-step in the tile
+constexpr int kGroupBytes = 8 * kRowBytes;    // a group's 8 rows
 constexpr int kTileBytes = 8 * kGroupBytes;   // one K-pair
 #ifndef FATHOM_SCAN_TILES
 #define FATHOM_SCAN_TILES 3
@@ -591,12 +613,19 @@ constexpr int kTileBytes = 8 * kGroupBytes;   // one K-pair
 constexpr int kTiles = FATHOM_SCAN_TILES;
 static_assert(kTiles >= 2 && kTiles <= 6, "tile ring");
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+// Filter records a 256-token block may hold, and the LDS a wave stages them in beyond
+// the tile ring (the filtering combine below).
+template <int QS>
+constexpr int block_records() { return QS == 1 ? 64 : kBlockRecords; }
+constexpr uint32_t kRunOvf = 0x80000000u;  // a run's kept count: the row overflowed
+template <int QS>
+constexpr size_t stage_bytes_per_wave() { return QS == 1 ? 0 : (size_t)4 * QS * kBlockRecords * 8; }
 
-// 16-byte LDS slot of row i (0..7), chunk c in a group's region; the xor spreads the
-// operand reads (chunk 2v + w/2 of rows s = 0..3) over all banks.
-__device__ __forceinline__ int tile_slot(int i, int c) {
-    return kRowChunks * i + (c ^ (2 * (i & 3)));
-}
+// Chunk c of row i of group g sits in 16-byte slot c ^ tile_swz(g, i) of the row: one
+// transpose read takes chunk 2v + t of the 8 rows of groups g and g + 1 (lanes 0-31; g
+// even) or g + 2 and g + 3, and the xor puts those 16 chunks of each half-wave on 16
+// different slots, i.e. all banks once.
+__device__ __forceinline__ int tile_swz(int g, int i) { return 8 * (g & 1) + i; }
 
 // LDS per head slot: A operand halves [K-block of 4 groups][lane][QS] (8 bytes); the
 // rows the copies read, [K-pair][row r of a K-block half][half] (kWide: row index or
@@ -613,7 +642,8 @@ constexpr size_t lds_head_bytes() {
 }
 template <int QS>
 constexpr size_t scan_lds_bytes() {
-    return 2 * lds_head_bytes<QS>() + (size_t)kTiles * kTileBytes;
+    return 2 * lds_head_bytes<QS>() + (size_t)kTiles * kTileBytes + (size_t)kScanThreads * 8 +
+           (size_t)kWaves * stage_bytes_per_wave<QS>();
 }
 
 // score = C + (D0 + 256 D1 + 65536 (D2 + 256 D3)) * S / (byte value of bit m); the
@@ -641,7 +671,7 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
                                          : Sq[set] * (-1.0f / 128.0f);
                 v[m] = fmaf(f, mult, Cq[set]);
             }
-            const int tok = (wi + pos) * 32 + 8 * s;
+            const int tok = (wi + 4 * pos) * 32 + 8 * s;
             if ((n & 3) == 0 && tok + 8 <= n) {
                 *reinterpret_cast<float4 *>(row + tok) = make_float4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<float4 *>(row + tok + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -658,32 +688,49 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
 // integer test X = D2 + 256 D3 against the row's threshold for its bit m, then the
 // records of the tokens that pass go to the front of the wave's 256-token block (words
 // wb .. wb+7) of the row's record area, with the block's 8 mask words; the row's count
-// of kept tokens grows by the block's.  Within a block the records are ordered by word
-// in the order wb, wb+2, wb+4, wb+6, wb+1, wb+3, wb+5, wb+7 (pos, then w: lane 4w + s of
-// a query's 16 holds byte s of words wb + 2w + pos), and by token within a word.  A
-// block with more than kBlockRecords candidates sets the row's ovf bit (its records are
+// of kept tokens grows by the block's.  Within a block the records are in token order
+// (pass pos, then w: lane 4w + s of a query's 16 holds byte s of word wb + 4 pos + w).  A
+// block with more than block_records<QS>() candidates sets the row's ovf bit (its records are
 // then incomplete and the row is rescored), as does every row of a head of more than
 // 480 planes (!small: R would not fit int32).  xt: the lane's query's thresholds (keep
 // none for a query past G); ragged: the super-step reaches past token n.  kWide: 64-bit
-// record addresses; otherwise 32-bit byte offsets from hcand.
+// record addresses; otherwise 32-bit byte offsets from hcand.  The lane's row's kept count
+// and ovf bit (kRunOvf) are accumulated in cnt (per query set) and added to the row by
+// the caller at the end of its run; the return value is the number of store instructions
+// issued (wave-uniform: each counted store runs with at least one lane active), which
+// lets the caller's next wait for its copies leave exactly those stores pending.
+// The records are first gathered in LDS, block by block (query block b = 4 set + j: the
+// first 2 QS blocks at stage_lo, the others at stage_hi): every lane writes one 8-byte
+// record per token without
+// a branch, a kept token's to its place in the block and the others to the lane's own
+// slot `dummy`; then each query's 16 lanes copy their block out, 16 records a store, so
+// that a few stores of whole runs replace one store per kept token position.  With one
+// query set the stage is the wave's two 1 KiB areas of the tile its next copies will
+// fill, 64 records a block; with two, an 8 KiB area of its own, 128 a block (the two-set
+// scan runs one workgroup per CU, so the LDS is there).
 template <int QS, bool kWide>
-__device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const int (&xt)[QS][8],
+__device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const int (&xt)[QS][8],
                                                bool ragged, bool small, int G, int jq, int s,
                                                int wq, int lane, int wi, int n, int64_t cstride,
-                                               char *hcand, uint32_t *hmask, uint32_t *hcnt,
-                                               uint32_t *hovf, uint32_t, uint32_t) {
+                                               char *hcand, uint32_t *hmask, uint32_t (&cnt)[QS],
+                                               lds_char *stage_lo, lds_char *stage_hi,
+                                               lds_char *dummy) {
+    constexpr int kStage = block_records<QS>();
     const int W = (n + 31) >> 5;
-    const int wb = wi - 2 * wq;   // first word of the block
+    int stores = 0;  // store instructions issued (each wave-uniform)
+    const int wb = wi - wq;       // first word of the block
     const uint32_t below = (1u << (8 * s)) - 1u;  // bits of the quad's lower lanes
 #pragma unroll
     for (int set = 0; set < QS; ++set) {
         const int g = 4 * set + jq;
         const bool live = g < G;  // the same for a query's 16 lanes
         if (!small) {
-            if (live && (lane & 15) == 0) atomicOr(hovf, 1u << g);
+            cnt[set] |= kRunOvf;
             continue;
         }
         const size_t blk_bytes = ((size_t)g * cstride + (size_t)wb * 32) * 4;
+        const int sb = set * 4 + jq;  // this lane's query block
+        lds_char *stage = (sb < 2 * QS ? stage_lo : stage_hi) + (sb % (2 * QS)) * kStage * 8;
         uint32_t base = 0u;       // records of the block's earlier words
 #pragma unroll
         for (int pos = 0; pos < 2; ++pos) {
@@ -691,7 +738,7 @@ __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const
 #pragma unroll
             for (int m = 0; m < 8; ++m) xp[m] = xt[set][m];
             if (ragged) {  // tokens >= n keep nothing
-                const int left = n - ((wi + pos) * 32 + 8 * s);
+                const int left = n - ((wi + 4 * pos) * 32 + 8 * s);
 #pragma unroll
                 for (int m = 0; m < 8; ++m)
                     if (m >= left) xp[m] = m < 7 ? INT32_MAX : INT32_MIN;
@@ -718,38 +765,54 @@ __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const
             suf += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)suf, 0x108, 0xF, 0xF, true);
             const uint32_t r = base + inc - t + (uint32_t)__popc(x & below);
             base += inc + suf - t;
+            const bool mask_out = live && s == 0 && wi + 4 * pos < W;
+            stores += __builtin_amdgcn_ballot_w64(mask_out) != 0 ? 1 : 0;
+            if (mask_out) hmask[(size_t)g * W + wi + 4 * pos] = x;
             if (live) {
-                if (s == 0 && wi + pos < W) hmask[(size_t)g * W + wi + pos] = x;
-                if (base <= (uint32_t)kBlockRecords) {
-                    if constexpr (kWide) {
-                        int2 *rec = reinterpret_cast<int2 *>(hcand + blk_bytes) + r;
+                {
+                    uint32_t k = r;  // record index in the block
 #pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            if (keep[m]) {
-                                const v4i d = acc[pos][m][set];
-                                *rec++ = make_int2(d[2] + d[3] * 256, d[0] + d[1] * 256);
-                            }
-                        }
-                    } else {
-                        uint32_t off = (uint32_t)blk_bytes + 8u * r;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            if (keep[m]) {
-                                const v4i d = acc[pos][m][set];
-                                *reinterpret_cast<int2 *>(hcand + off) =
-                                    make_int2(d[2] + d[3] * 256, d[0] + d[1] * 256);
-                                off += 8u;
-                            }
-                        }
+                    for (int m = 0; m < 8; ++m) {
+                        const v4i d = acc[pos][m][set];
+                        lds_char *a = keep[m] && k < (uint32_t)kStage ? stage + 8u * k : dummy;
+                        *reinterpret_cast<lds_v2i *>(a) = v2i{d[2] + d[3] * 256, d[0] + d[1] * 256};
+                        k += keep[m] ? 1u : 0u;
                     }
                 }
             }
         }
-        if (live && (lane & 15) == 0) {
-            if (base > (uint32_t)kBlockRecords) atomicOr(hovf, 1u << g);
-            if (base) atomicAdd(hcnt + g, base);
+        // the staged records out: lane i of the query's 16 copies records i, i + 16, ...
+        const uint32_t staged = live && base <= (uint32_t)kStage ? base : 0u;
+        for (uint32_t k = (uint32_t)(lane & 15); __builtin_amdgcn_ballot_w64(k < staged) != 0;
+             k += 16u) {
+            ++stores;
+            if (k < staged) {
+                const v2i sv = *reinterpret_cast<const lds_v2i *>(stage + 8u * k);
+                const int2 rv = make_int2(sv.x, sv.y);
+                if constexpr (kWide) reinterpret_cast<int2 *>(hcand + blk_bytes)[k] = rv;
+                else *reinterpret_cast<int2 *>(hcand + ((uint32_t)blk_bytes + 8u * k)) = rv;
+            }
         }
+        cnt[set] += base | (base > (uint32_t)kStage ? kRunOvf : 0u);
     }
+    return stores;
+}
+
+// s_waitcnt vmcnt(min(n, 31)) (expcnt and lgkmcnt not waited for): a smaller count only
+// waits for more.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define FATHOM_VM(i) \
+    case i: __builtin_amdgcn_s_waitcnt(0x0F70 | ((i) & 15) | (((i) >> 4) << 14)); break;
+    switch (n < 31 ? n : 31) {
+        FATHOM_VM(0) FATHOM_VM(1) FATHOM_VM(2) FATHOM_VM(3) FATHOM_VM(4) FATHOM_VM(5)
+        FATHOM_VM(6) FATHOM_VM(7) FATHOM_VM(8) FATHOM_VM(9) FATHOM_VM(10) FATHOM_VM(11)
+        FATHOM_VM(12) FATHOM_VM(13) FATHOM_VM(14) FATHOM_VM(15) FATHOM_VM(16) FATHOM_VM(17)
+        FATHOM_VM(18) FATHOM_VM(19) FATHOM_VM(20) FATHOM_VM(21) FATHOM_VM(22) FATHOM_VM(23)
+        FATHOM_VM(24) FATHOM_VM(25) FATHOM_VM(26) FATHOM_VM(27) FATHOM_VM(28) FATHOM_VM(29)
+        FATHOM_VM(30)
+        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15 | (1 << 14)); break;
+    }
+#undef FATHOM_VM
 }
 
 // Global -> LDS copy of 16 bytes a lane: lane l's bytes land at LDS byte address
@@ -810,6 +873,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const char *__restrict__ ws, float *__restrict__ scores, uint32_t *__restrict__ masks) {
     extern __shared__ uint4 lds_u4[];
     char *lds = reinterpret_cast<char *>(lds_u4);
+    lds_char *lds3 = (lds_char *)lds_u4;
     constexpr size_t kHeadBytes = lds_head_bytes<QS>();
     constexpr size_t kRowsOff = lds_rows_off<QS>();
     constexpr size_t kXthrOff = lds_xthr_off<QS>();
@@ -895,7 +959,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     // moves chunk c of row r of the half: r = 8*cgrp + crow, c = cchunk
     const int cgrp = wave / (kWaves / 4);
     const int crow = (wave % (kWaves / 4)) * kCopyRows + lane / kRowChunks;
-    const int cchunk = (lane % kRowChunks) ^ (2 * (crow & 3));
+    const int cchunk = (lane % kRowChunks) ^ tile_swz(cgrp, crow);
     const int crr = 8 * cgrp + crow;  // row of a K-block half
     const uint32_t cdst = (uint32_t)(cgrp * kGroupBytes +
                                      (wave % (kWaves / 4)) * kCopyRows * kRowChunks * 16);
@@ -937,25 +1001,29 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
 
     v4i acc[2][8][QS];
     int pss = 0, ppr = 0;  // item being used
-    const int rchunk = 2 * wave + (wq >> 1);  // operand chunk and half of this lane
-    const int rhalf = 8 * (wq & 1);
+    // this lane's transpose-read source: plane j of group q (+ 4h), words 4t + 2p and
+    // 4t + 2p + 1 of the wave's 8, i.e. the low or high 8 bytes of chunk 2v + t
     const int qgrp = lane >> 4;               // operand group q (and q + 4)
+    const int trj = (lane & 15) >> 1;
+    const uint32_t trsrc0 = (uint32_t)(qgrp * kGroupBytes + trj * kRowBytes + 8 * (lane & 1));
     // A super-step's scores are combined after the barrier of the next item, before
     // that item's copies are issued: its stores then precede the newest copies in the
     // wave's memory-instruction order, and the wait for the next tile (vmcnt(2): all but
     // the newest copies) covers them rather than copies just issued.  pk: head slot of
     // the pending combine (-1: none), pss_c: its super-step in the run.
     int pk = -1, pss_c = 0;
+    int pstores = 0;  // store instructions of the last combine (filter)
+    uint32_t cnt0[QS], cnt1[QS];  // per head slot: kept counts and kRunOvf
+#pragma unroll
+    for (int set = 0; set < QS; ++set) cnt0[set] = cnt1[set] = 0u;
     uint32_t ptile = 0u;  // LDS address of the tile of the pending super-step's last item
     auto combine = [&]() {
         const int k = pk;
         const int hh = k ? h1 : h0;
         const int nk = k ? nkb1 : nkb0;
         const int ssh = k ? pss_c - h1rel : ss0 + pss_c;  // super-step within the head
-        const int wi = (ssh * kWaves + wave) * 8 + 2 * wq;
+        const int wi = (ssh * kWaves + wave) * 8 + wq;  // this lane's word of pass 0
         if constexpr (kFilter) {
-            ScanMeta *mh =
-                reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) + (size_t)hh * kMetaBytes);
             // this lane's queries' thresholds, from the head's LDS slot
             const int32_t *lx = reinterpret_cast<const int32_t *>(lds + k * kHeadBytes + kXthrOff);
             int xt[QS][8];
@@ -970,11 +1038,27 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
             const bool ragged = (ssh + 1) * kSuperWords * 32 > n;
             // stage and dummy slots: this wave's two 1 KiB copy areas of the tile its
             // next copies will fill (every wave is done reading that tile)
-            const uint32_t mine = ptile + cdst;
-            combine_filter<QS, kWide>(acc, xt, ragged, nk < kMaxKBlocks, G, jq, s, wq, lane, wi,
-                                      n, cs, reinterpret_cast<char *>(scores + (size_t)hh * G * cs),
-                                      masks + (size_t)hh * G * ((n + 31) >> 5), mh->cnt,
-                                      &mh->ovf, mine, mine + (uint32_t)(4 * kGroupBytes) + 8u * lane);
+            // the stage: with one query set this wave's two 1 KiB copy areas of the tile
+            // its next copies will fill (every wave is done reading it); with two, its
+            // own area after the lanes' dummy slots
+            lds_char *tiles_end = lds3 + (tiles_base - lds_base) + kTiles * kTileBytes;
+            lds_char *stage = QS == 1 ? lds3 + (ptile - lds_base) + cdst
+                                      : tiles_end + kScanThreads * 8 + wave * stage_bytes_per_wave<QS>();
+            lds_char *stage_hi = stage + (QS == 1 ? 4 * kGroupBytes : 4096);
+            uint32_t c[QS];
+#pragma unroll
+            for (int set = 0; set < QS; ++set) c[set] = 0u;
+            pstores = combine_filter<QS, kWide>(
+                acc, xt, ragged, nk < kMaxKBlocks, G, jq, s, wq, lane, wi, n, cs,
+                reinterpret_cast<char *>(scores + (size_t)hh * G * cs),
+                masks + (size_t)hh * G * ((n + 31) >> 5), c, stage, stage_hi, tiles_end + 8 * tid);
+#pragma unroll
+            for (int set = 0; set < QS; ++set) {  // count bits stay below kRunOvf
+                cnt0[set] |= k ? 0u : c[set] & kRunOvf;
+                cnt0[set] += k ? 0u : c[set] & ~kRunOvf;
+                cnt1[set] |= k ? c[set] & kRunOvf : 0u;
+                cnt1[set] += k ? c[set] & ~kRunOvf : 0u;
+            }
         } else {
             // the head's constants, picked element by element: choosing between the two
             // arrays as a whole made them addressable, i.e. scratch memory
@@ -989,16 +1073,12 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         pk = -1;
     };
     for (int f = 0; f < nitems; ++f) {
-        // this wave's copies of item f have landed (2 copies per later item in flight)
-        if (fi - f - 1 == kTiles - 2) {
-            if constexpr (kTiles == 2) __builtin_amdgcn_s_waitcnt(0x0F70);
-            if constexpr (kTiles == 3) __builtin_amdgcn_s_waitcnt(0x0F72);
-            if constexpr (kTiles == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-            if constexpr (kTiles == 5) __builtin_amdgcn_s_waitcnt(0x0F76);
-            if constexpr (kTiles == 6) __builtin_amdgcn_s_waitcnt(0x0F78);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
+        // this wave's copies of item f have landed: left pending are the copies of the
+        // later items already issued (2 each) and, with the filter, the stores of the
+        // combines that were issued after item f's copies (the one of the previous
+        // iteration; with the full scores those are waited for too)
+        wait_vmcnt(2 * (fi - f - 1) + (kFilter ? pstores : 0));
+        pstores = 0;
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // ... and every wave's; tile f-1 is free again
         __asm__ volatile("" ::: "memory");
@@ -1007,18 +1087,8 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         const int k = pss >= h1rel ? 1 : 0;
         const int nk = k ? nkb1 : nkb0;
         const bool hi = 2 * ppr + 1 < nk;  // upper 4 groups of the K-pair exist
-        const char *t = lds + 2 * kHeadBytes + (f % kTiles) * kTileBytes + qgrp * kGroupBytes;
-        uint32_t w[2][2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const char *tg = t + h * 4 * kGroupBytes;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(tg + 16 * tile_slot(s, rchunk) + rhalf);
-            const uint2 up = *reinterpret_cast<const uint2 *>(tg + 16 * tile_slot(s + 4, rchunk) + rhalf);
-            w[h][0][0] = lo.x;
-            w[h][0][1] = lo.y;
-            w[h][1][0] = up.x;
-            w[h][1][1] = up.y;
-        }
+        char *t = lds + 2 * kHeadBytes + (f % kTiles) * kTileBytes + trsrc0;
+        const uint32_t hi_mask = hi ? 0xFFFFFFFFu : 0u;
         const uint2 *la = reinterpret_cast<const uint2 *>(lds + k * kHeadBytes);
         v4i A[QS];
 #pragma unroll
@@ -1027,7 +1097,20 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
             const uint2 ahi = hi ? la[((2 * ppr + 1) * 64 + lane) * QS + set] : make_uint2(0u, 0u);
             A[set] = v4i{(int)alo.x, (int)alo.y, (int)ahi.x, (int)ahi.y};
         }
-        mma_item<QS>(w, A, s, ppr == 0, hi, acc);
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            const int slot = (2 * wave + tp) ^ tile_swz(qgrp, trj);  // groups q and q + 4 alike
+            uint32_t x[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i *)(t + h * 4 * kGroupBytes + 16 * slot));
+                x[h][0] = (uint32_t)r.x;
+                x[h][1] = (uint32_t)r.y;
+            }
+            if (ppr == 0) mma_pass_x<QS, true>(x, A, hi_mask, acc[tp]);
+            else mma_pass_x<QS, false>(x, A, hi_mask, acc[tp]);
+        }
         if (++ppr == (k ? npr1 : npr0)) {
             pk = k;
             pss_c = pss;
@@ -1037,6 +1120,23 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         }
     }
     if (pk >= 0) combine();
+    if constexpr (kFilter) {  // the run's kept counts and overflow bits into its rows
+        if ((lane & 15) == 0) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (k && h1 == h0) break;
+                ScanMeta *mh = reinterpret_cast<ScanMeta *>(const_cast<char *>(ws) +
+                                                            (size_t)(k ? h1 : h0) * kMetaBytes);
+#pragma unroll
+                for (int set = 0; set < QS; ++set) {
+                    const int g = 4 * set + jq;
+                    const uint32_t c = k ? cnt1[set] : cnt0[set];
+                    if (g < G && (c & ~kRunOvf)) atomicAdd(mh->cnt + g, c & ~kRunOvf);
+                    if (g < G && (c & kRunOvf)) atomicOr(&mh->ovf, 1u << g);
+                }
+            }
+        }
+    }
 }
 
 // Resident workgroups of a kernel instance over the device (asked once per device).

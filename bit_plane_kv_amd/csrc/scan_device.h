@@ -15,6 +15,9 @@
 namespace fathom {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;   // LDS pointers
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 // Signed base-256 digits of M: M = sum_d 256^d digit_d, digits 0..2 in [-128, 127];
 // for |M| <= 2^30 the top digit lies in [-64, 64].  With u = M + kDigitBias, bits

@@ -159,20 +159,18 @@ __device__ __forceinline__ void fill_slots(float *out_val, int32_t *out_idx, int
 }
 
 // Kept-candidate keys of this thread's word (tokens 32*word .. +31): the block's
-// records lie at the front of its 256-token region, words in the order 0,2,4,6,1,3,5,7
-// of the block, tokens ascending within a word.  Returns the mask.
+// records lie at the front of its 256-token region in token order.  Returns the mask.
 __device__ __forceinline__ uint32_t load_kept(const int2 *row_rec, const uint32_t *row_mask,
                                               int word, int W, uint32_t lenmask, float C,
                                               float S, uint32_t (&key)[kEPT]) {
     const uint32_t mk = (word < W ? row_mask[word] : 0u) & lenmask;
     const uint32_t c = (uint32_t)__popc(mk);
     const int j = threadIdx.x & 7;  // word within the block (blocks are 8 threads)
-    const int oj = (j & 1) * 4 + (j >> 1);
     uint32_t pre = 0u;
 #pragma unroll
-    for (int o = 0; o < 8; ++o) {  // words stored before this one
-        const uint32_t co = (uint32_t)__shfl((int)c, 2 * (o & 3) + (o >> 2), 8);
-        if (o < oj) pre += co;
+    for (int o = 0; o < 7; ++o) {  // words stored before this one
+        const uint32_t co = (uint32_t)__shfl((int)c, o, 8);
+        if (o < j) pre += co;
     }
     const int2 *src = row_rec + (size_t)(word & ~7) * 16 + pre;
     uint32_t r = 0u;
@@ -630,26 +628,23 @@ __device__ __forceinline__ void select_kept(
         hand_over();
         return;
     }
-    // Stored order of a block's kept scores: words 0,2,4,6,1,3,5,7; off[j]: the kept
-    // tokens of the block stored before those of word wl + j.
+    // A block's kept scores are stored in token order; off[j]: the kept tokens of the
+    // block stored before those of word wl + j.
     uint32_t off[WPT];
     if constexpr (WPT == 4) {  // thread 2b: words 0-3 of block b, thread 2b+1 words 4-7
-        const uint32_t E = c[0] + c[2], O = c[1] + c[3];
+        const uint32_t E = c[0] + c[1] + c[2] + c[3];
         const uint32_t pE = (uint32_t)__shfl_xor((int)E, 1, 64);
-        const uint32_t pO = (uint32_t)__shfl_xor((int)O, 1, 64);
-        const bool odd = tid & 1;
-        const uint32_t eb = odd ? pE : 0u, ob = odd ? pO : 0u, te = E + pE;
-        off[0] = eb;
-        off[2] = eb + c[0];
-        off[1] = te + ob;
-        off[3] = te + ob + c[1];
+        off[0] = (tid & 1) ? pE : 0u;
+        off[1] = off[0] + c[0];
+        off[2] = off[1] + c[1];
+        off[3] = off[2] + c[2];
     } else {  // thread 8b + j: word j of block b
-        const int j = tid & 7, oj = (j & 1) * 4 + (j >> 1);  // its place in the order
+        const int j = tid & 7;
         uint32_t pre = 0u;
 #pragma unroll
-        for (int o = 0; o < 8; ++o) {
-            const uint32_t co = (uint32_t)__shfl((int)c[0], 2 * (o & 3) + (o >> 2), 8);
-            if (o < oj) pre += co;
+        for (int o = 0; o < 7; ++o) {
+            const uint32_t co = (uint32_t)__shfl((int)c[0], o, 8);
+            if (o < j) pre += co;
         }
         off[0] = pre;
     }
