@@ -696,9 +696,7 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
 // none for a query past G); ragged: the super-step reaches past token n.  kWide: 64-bit
 // record addresses; otherwise 32-bit byte offsets from hcand.  The lane's row's kept count
 // and ovf bit (kRunOvf) are accumulated in cnt (per query set) and added to the row by
-// the caller at the end of its run; the return value is the number of store instructions
-// issued (wave-uniform: each counted store runs with at least one lane active), which
-// lets the caller's next wait for its copies leave exactly those stores pending.
+// the caller at the end of its run.
 // The records are first gathered in LDS, block by block (query block b = 4 set + j: the
 // first 2 QS blocks at stage_lo, the others at stage_hi): every lane writes one 8-byte
 // record per token without
@@ -709,7 +707,7 @@ __device__ __forceinline__ void combine_store(const v4i (&acc)[2][8][QS], const 
 // fill, 64 records a block; with two, an 8 KiB area of its own, 128 a block (the two-set
 // scan runs one workgroup per CU, so the LDS is there).
 template <int QS, bool kWide>
-__device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const int (&xt)[QS][8],
+__device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const int (&xt)[QS][8],
                                                bool ragged, bool small, int G, int jq, int s,
                                                int wq, int lane, int wi, int n, int64_t cstride,
                                                char *hcand, uint32_t *hmask, uint32_t (&cnt)[QS],
@@ -717,7 +715,6 @@ __device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const 
                                                lds_char *dummy) {
     constexpr int kStage = block_records<QS>();
     const int W = (n + 31) >> 5;
-    int stores = 0;  // store instructions issued (each wave-uniform)
     const int wb = wi - wq;       // first word of the block
     const uint32_t below = (1u << (8 * s)) - 1u;  // bits of the quad's lower lanes
 #pragma unroll
@@ -765,9 +762,7 @@ __device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const 
             suf += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)suf, 0x108, 0xF, 0xF, true);
             const uint32_t r = base + inc - t + (uint32_t)__popc(x & below);
             base += inc + suf - t;
-            const bool mask_out = live && s == 0 && wi + 4 * pos < W;
-            stores += __builtin_amdgcn_ballot_w64(mask_out) != 0 ? 1 : 0;
-            if (mask_out) hmask[(size_t)g * W + wi + 4 * pos] = x;
+            if (live && s == 0 && wi + 4 * pos < W) hmask[(size_t)g * W + wi + 4 * pos] = x;
             if (live) {
                 {
                     uint32_t k = r;  // record index in the block
@@ -785,7 +780,6 @@ __device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const 
         const uint32_t staged = live && base <= (uint32_t)kStage ? base : 0u;
         for (uint32_t k = (uint32_t)(lane & 15); __builtin_amdgcn_ballot_w64(k < staged) != 0;
              k += 16u) {
-            ++stores;
             if (k < staged) {
                 const v2i sv = *reinterpret_cast<const lds_v2i *>(stage + 8u * k);
                 const int2 rv = make_int2(sv.x, sv.y);
@@ -795,24 +789,6 @@ __device__ __forceinline__ int combine_filter(const v4i (&acc)[2][8][QS], const 
         }
         cnt[set] += base | (base > (uint32_t)kStage ? kRunOvf : 0u);
     }
-    return stores;
-}
-
-// s_waitcnt vmcnt(min(n, 31)) (expcnt and lgkmcnt not waited for): a smaller count only
-// waits for more.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-#define FATHOM_VM(i) \
-    case i: __builtin_amdgcn_s_waitcnt(0x0F70 | ((i) & 15) | (((i) >> 4) << 14)); break;
-    switch (n < 31 ? n : 31) {
-        FATHOM_VM(0) FATHOM_VM(1) FATHOM_VM(2) FATHOM_VM(3) FATHOM_VM(4) FATHOM_VM(5)
-        FATHOM_VM(6) FATHOM_VM(7) FATHOM_VM(8) FATHOM_VM(9) FATHOM_VM(10) FATHOM_VM(11)
-        FATHOM_VM(12) FATHOM_VM(13) FATHOM_VM(14) FATHOM_VM(15) FATHOM_VM(16) FATHOM_VM(17)
-        FATHOM_VM(18) FATHOM_VM(19) FATHOM_VM(20) FATHOM_VM(21) FATHOM_VM(22) FATHOM_VM(23)
-        FATHOM_VM(24) FATHOM_VM(25) FATHOM_VM(26) FATHOM_VM(27) FATHOM_VM(28) FATHOM_VM(29)
-        FATHOM_VM(30)
-        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15 | (1 << 14)); break;
-    }
-#undef FATHOM_VM
 }
 
 // Global -> LDS copy of 16 bytes a lane: lane l's bytes land at LDS byte address
@@ -1012,7 +988,6 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     // the newest copies) covers them rather than copies just issued.  pk: head slot of
     // the pending combine (-1: none), pss_c: its super-step in the run.
     int pk = -1, pss_c = 0;
-    int pstores = 0;  // store instructions of the last combine (filter)
     uint32_t cnt0[QS], cnt1[QS];  // per head slot: kept counts and kRunOvf
 #pragma unroll
     for (int set = 0; set < QS; ++set) cnt0[set] = cnt1[set] = 0u;
@@ -1048,7 +1023,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
             uint32_t c[QS];
 #pragma unroll
             for (int set = 0; set < QS; ++set) c[set] = 0u;
-            pstores = combine_filter<QS, kWide>(
+            combine_filter<QS, kWide>(
                 acc, xt, ragged, nk < kMaxKBlocks, G, jq, s, wq, lane, wi, n, cs,
                 reinterpret_cast<char *>(scores + (size_t)hh * G * cs),
                 masks + (size_t)hh * G * ((n + 31) >> 5), c, stage, stage_hi, tiles_end + 8 * tid);
@@ -1073,12 +1048,17 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         pk = -1;
     };
     for (int f = 0; f < nitems; ++f) {
-        // this wave's copies of item f have landed: left pending are the copies of the
-        // later items already issued (2 each) and, with the filter, the stores of the
-        // combines that were issued after item f's copies (the one of the previous
-        // iteration; with the full scores those are waited for too)
-        wait_vmcnt(2 * (fi - f - 1) + (kFilter ? pstores : 0));
-        pstores = 0;
+        // this wave's copies of item f have landed (2 copies per later item in flight;
+        // the stores of a combine, issued before the newest copies, are waited for too)
+        if (fi - f - 1 == kTiles - 2) {
+            if constexpr (kTiles == 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+            if constexpr (kTiles == 3) __builtin_amdgcn_s_waitcnt(0x0F72);
+            if constexpr (kTiles == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+            if constexpr (kTiles == 5) __builtin_amdgcn_s_waitcnt(0x0F76);
+            if constexpr (kTiles == 6) __builtin_amdgcn_s_waitcnt(0x0F78);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // ... and every wave's; tile f-1 is free again
         __asm__ volatile("" ::: "memory");
