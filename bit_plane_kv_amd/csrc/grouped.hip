@@ -374,15 +374,22 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? 4 : 2))) void k_scan_grouped_mma(
                     }
                     A[set] = v4i{(int)bytes[0], (int)bytes[1], (int)bytes[2], (int)bytes[3]};
                 }
-                // B operand: planes s, s+4 of plane groups jq, jq+4 at word 8v + 4 pos + wq
+                // B operand: byte s of word 8v + 4 pos + wq of the 8 planes of plane groups
+                // jq and jq + 4, by the LDS transpose read (within each 16 lanes, lane i < 8
+                // receives byte i of the 8 bytes each even lane read, lane 8 + i those of
+                // the odd lanes): lane 16 jq + 2 j + p reads words 8v + 4 pos + 2p and the
+                // next of plane j.  The rows' 144- or 272-byte stride puts each half-wave's
+                // 32 reads on distinct banks.
                 uint32_t x[2][2];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp)
-                        x[hh][pp] = quad_byte_transpose(
-                            words[64 * kk + 8 * (jq + 4 * hh) + s + 4 * pp][8 * wave + 4 * pos + wq],
-                            s);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int trj = (lane & 15) >> 1, trp = lane & 1;
+                    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i *)&words[64 * kk + 8 * (jq + 4 * hh) + trj]
+                                                                       [8 * wave + 4 * pos + 2 * trp]);
+                    x[hh][0] = (uint32_t)r.x;
+                    x[hh][1] = (uint32_t)r.y;
+                }
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const uint32_t mask = 0x01010101u << m;
