@@ -642,6 +642,7 @@ constexpr size_t lds_head_bytes() {
 }
 template <int QS>
 constexpr size_t scan_lds_bytes() {
+    static_assert(kMaxKBlocks * 64 % kScanThreads == 0, "records a thread");
     return 2 * lds_head_bytes<QS>() + (size_t)kTiles * kTileBytes + (size_t)kScanThreads * 8 +
            (size_t)kWaves * stage_bytes_per_wave<QS>();
 }
@@ -874,45 +875,59 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);  // 4-group K-blocks
     const int nkb1 = min(max(meta1->n_kblocks, 1), kMaxKBlocks);
     const int tid = threadIdx.x;
+    // The head slots' LDS from the operand records.  Every record of the kMaxKBlocks a
+    // head may have is loaded, unconditionally and in the same round as the K-block counts
+    // above (the ones past a head's count are dropped), so that one memory latency, not
+    // two, precedes the first copies.  Record e = 64 kb + ln holds in its first two words
+    // the rows of planes s and s + 4 of group 4 kb + (ln >> 4), s = ln & 3, when
+    // (ln & 15) < 4: row r = 8 (ln >> 4) + s and r + 4 of K-block kb.
+    constexpr int kRecPer = kMaxKBlocks * 64 / kScanThreads;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         if (k && h1 == h0) break;
         const int hk = k ? h1 : h0, nk = k ? nkb1 : nkb0;
         const uint4 *grec = reinterpret_cast<const uint4 *>(
             ws + (size_t)H * kMetaBytes + (size_t)hk * kMaxKBlocks * 64 * 16 * QS);
-        const uint32_t *grec32 = reinterpret_cast<const uint32_t *>(grec);
+        uint4 rec[kRecPer][QS];
+#pragma unroll
+        for (int u = 0; u < kRecPer; ++u)
+#pragma unroll
+            for (int set = 0; set < QS; ++set)
+                rec[u][set] = grec[(size_t)(tid + kScanThreads * u) * QS + set];
+        const uint32_t first_row = reinterpret_cast<const uint32_t *>(grec)[0];
+        int32_t xk = 0;
+        if constexpr (kFilter) {
+            const ScanMeta *mk = k ? meta1 : meta0;
+            if (tid < FATHOM_MAX_G * 8) xk = mk->xthr[tid >> 3][tid & 7];
+        }
         uint2 *la = reinterpret_cast<uint2 *>(lds + k * kHeadBytes);
         uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + k * kHeadBytes + kRowsOff);
-        for (int e = tid; e < nk * 64; e += kScanThreads) {
-            const uint4 r = grec[(size_t)e * QS];
-            la[e * QS] = make_uint2(r.z, r.w);
-            if constexpr (QS == 2) {
-                const uint4 r2 = grec[(size_t)e * QS + 1];
-                la[e * QS + 1] = make_uint2(r2.x, r2.y);
-            }
-        }
-        // row r of K-block kb: plane (r & 7) of group 4 kb + (r >> 3), whose record lane
-        // is 16 (r >> 3) + (r & 3), word 0 (planes 0-3) or 1 (planes 4-7)
-        const uint32_t first_row = grec32[0];
         const uint32_t dead = kWide ? kNoRow
                                     : (first_row < (uint32_t)kMaxPlanesPerHead
                                            ? first_row * (uint32_t)word_stride * 4u : 0u);
         const int nk2 = 2 * ((nk + 1) >> 1);
-        for (int e = tid; e < nk2 * 32; e += kScanThreads) {
-            const int kb = e >> 5, r = e & 31;
-            uint32_t v = dead;
+#pragma unroll
+        for (int u = 0; u < kRecPer; ++u) {
+            const int e = tid + kScanThreads * u, kb = e >> 6, ln = e & 63;
             if (kb < nk) {
-                const uint32_t p =
-                    grec32[((size_t)kb * 64 + 16 * (r >> 3) + (r & 3)) * 4 * QS + ((r >> 2) & 1)];
-                if (p < (uint32_t)kMaxPlanesPerHead)
-                    v = kWide ? p : p * (uint32_t)word_stride * 4u;
+                la[e * QS] = make_uint2(rec[u][0].z, rec[u][0].w);
+                if constexpr (QS == 2) la[e * QS + 1] = make_uint2(rec[u][1].x, rec[u][1].y);
             }
-            lrow[((kb >> 1) * 32 + r) * 2 + (kb & 1)] = v;
+            if (kb < nk2 && (ln & 15) < 4) {
+                const int r = 8 * (ln >> 4) + (ln & 3);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const uint32_t p = hf ? rec[u][0].y : rec[u][0].x;
+                    uint32_t v = dead;
+                    if (kb < nk && p < (uint32_t)kMaxPlanesPerHead)
+                        v = kWide ? p : p * (uint32_t)word_stride * 4u;
+                    lrow[((kb >> 1) * 32 + r + 4 * hf) * 2 + (kb & 1)] = v;
+                }
+            }
         }
         if constexpr (kFilter) {
-            const ScanMeta *mk = k ? meta1 : meta0;
             int32_t *lx = reinterpret_cast<int32_t *>(lds + k * kHeadBytes + kXthrOff);
-            if (tid < FATHOM_MAX_G * 8) lx[tid] = mk->xthr[tid >> 3][tid & 7];
+            if (tid < FATHOM_MAX_G * 8) lx[tid] = xk;
         }
     }
     __syncthreads();
