@@ -453,6 +453,19 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     // 480 planes (the filter keeps no records for them): scan all, then select
     const bool full = scores_out || sample_rank(n, k) == 0 || B == 0 || B > 480;
     FATHOM_TRY(mark(0));
+    if (!full && filtered_attend_applies(H * G, n, k) && front_fused_applies(*st, G)) {
+        // few heads of one-chunk rows (a layer of a decode step): plan, prepare and the
+        // filtering scan in one kernel, then select and attention in one; the plan-prepare
+        // phase holds the first, the scan phase is empty
+        FATHOM_TRY(hip_status(
+            launch_front_fused(*st, q, G, B, k, depth, scan_ws, scores, masks, s)));
+        FATHOM_TRY(mark(1));
+        FATHOM_TRY(mark(2));
+        FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k, idx,
+                                                          q, K, V, sm_scale, out, s)));
+        FATHOM_TRY(mark(3));
+        return mark(4);
+    }
     FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, full ? 0 : k, depth, scan_ws, s)));
     FATHOM_TRY(mark(1));
     if (full) {

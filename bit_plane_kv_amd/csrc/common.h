@@ -167,6 +167,14 @@ hipError_t launch_plan_prepare(const fathom_store &st, const float *q, int G, in
 // masks == nullptr: every score to `scores`; else the candidate filter (see above)
 hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *ws,
                             hipStream_t s, uint32_t *masks = nullptr);
+// A decode step's plan, prepare and filtering scan in one kernel (k_front_fused): when the
+// heads have one query set, rows of one top-k chunk and at most 256 (head, super-step)
+// pairs.  The same outputs as launch_plan_prepare + launch_scan_main with the filter,
+// except that the rows' kept counts and overflow bits in the workspace are not set.
+bool front_fused_applies(const fathom_store &st, int G);
+hipError_t launch_front_fused(const fathom_store &st, const float *q, int G, int B, int k,
+                              uint8_t *depth, void *ws, float *cand, uint32_t *masks,
+                              hipStream_t s);
 hipError_t launch_scan_extract(const fathom_store &st, const float *q, int G,
                                const uint8_t *depth, float *scores, hipStream_t s);
 hipError_t launch_pack_nibbles(const fathom_store &st, uint8_t *nib, hipStream_t s);

@@ -299,7 +299,7 @@ __device__ __forceinline__ void sample_thresholds(const uint32_t *__restrict__ p
             // the wave's own row of skey, now in registers, holds the compacted keys
             const uint32_t T = m > 0u ? sample_quantile(kk, m, lane, skey[gq]) : 0u;
             if (lane == 0) {
-                meta->tkey[4 * set + gq] = T;
+                if (meta) meta->tkey[4 * set + gq] = T;
                 tk[4 * set + gq] = T;
             }
         }
@@ -356,25 +356,28 @@ __device__ __forceinline__ void load_prep_in(const float *__restrict__ q,
 }
 
 // Body of the prepare step for head h; tc[c] (LDS, complete) holds the channel depths.
-// NT threads: 512 for one query set, 256 for two (whose registers allow no more).
+// NT threads: 512 for one query set, 256 for two (whose registers allow no more).  pl
+// (kMaxPlanesPerHead words) and la (the A operands, kMaxKBlocks * 64 * QS) are LDS the
+// caller provides; they hold the plane list and the operand halves on return, xthr_lds
+// (if given) the filter thresholds [query][m].  Only a writer stores the head's meta
+// block and records.  Returns the head's number of planes.
 template <int QS, int NT>
-__device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc, int H,
-                                             int G, const uint32_t *__restrict__ planes, int n,
-                                             int word_stride, int k, char *__restrict__ ws,
-                                             int h) {
+__device__ __forceinline__ int prepare_head(const PrepIn<QS> &in, const int *tc, int H,
+                                            int G, const uint32_t *__restrict__ planes, int n,
+                                            int word_stride, int k, char *__restrict__ ws,
+                                            int h, uint32_t *pl, uint2 *la,
+                                            int32_t *xthr_lds, bool writer) {
     constexpr int NQ = 4 * QS;
     constexpr int NW = NT / 64;                       // waves
     constexpr int QT = NT / kD;                       // threads per channel
     constexpr int WPQ = NW / NQ > 1 ? NW / NQ : 1;    // waves per query in the weight pass
     __shared__ int off[kD + 1];
-    __shared__ uint32_t pl[kMaxPlanesPerHead];
     __shared__ double wt[NQ][kMaxPlanesPerHead];
     __shared__ double red[NQ][kD];
     __shared__ double amx[NQ][kD];
     __shared__ double csum[NQ];
     __shared__ double inv_unit[NQ];
     __shared__ double unit[NQ];
-    __shared__ uint2 la[kMaxKBlocks * 64 * QS];  // A operand halves, as in the records
     __shared__ float cf[NQ], sf[NQ];             // C_g and S_g as the scan reads them
     const int tid = threadIdx.x, lane = tid & 63;
     ScanMeta *meta = reinterpret_cast<ScanMeta *>(ws + (size_t)h * kMetaBytes);
@@ -467,16 +470,18 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
             atomicAdd(&mai[g], (unsigned long long)a);
         }
     }
-    for (int p = tid; p < nplanes; p += NT) meta->plane[p] = pl[p];
-    if (tid < FATHOM_MAX_G) {
-        meta->C[tid] = tid < G ? (float)csum[tid] : 0.0f;
-        meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
+    if (writer) {
+        for (int p = tid; p < nplanes; p += NT) meta->plane[p] = pl[p];
+        if (tid < FATHOM_MAX_G) {
+            meta->C[tid] = tid < G ? (float)csum[tid] : 0.0f;
+            meta->S[tid] = tid < G ? (float)unit[tid] : 0.0f;
+        }
     }
     if (tid < NQ) {
         cf[tid] = tid < G ? (float)csum[tid] : 0.0f;
         sf[tid] = tid < G ? (float)unit[tid] : 0.0f;
     }
-    if (tid == 0) {
+    if (writer && tid == 0) {
         meta->n_planes = nplanes;
         meta->n_groups = ngroups;
         meta->n_kblocks = nkb;
@@ -490,8 +495,10 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
         const int s = ln & 3, r = ln & 15;
         const int p0 = grp * kGroupBits + s, p1 = p0 + 4;
         uint32_t *dst = rec + (size_t)e * 4 * QS;
-        dst[0] = p0 < nplanes ? pl[p0] : kSkipRow;
-        dst[1] = p1 < nplanes ? pl[p1] : kSkipRow;
+        if (writer) {
+            dst[0] = p0 < nplanes ? pl[p0] : kSkipRow;
+            dst[1] = p1 < nplanes ? pl[p1] : kSkipRow;
+        }
 #pragma unroll
         for (int set = 0; set < QS; ++set) {
             const int g = 4 * set + (r >> 2), dg = r & 3;
@@ -503,31 +510,38 @@ __device__ __forceinline__ void prepare_head(const PrepIn<QS> &in, const int *tc
                 if (i < 4) wlo |= byte << (8 * i);
                 else whi |= byte << (8 * (i - 4));
             }
-            dst[2 + 2 * set] = wlo;
-            dst[3 + 2 * set] = whi;
+            if (writer) {
+                dst[2 + 2 * set] = wlo;
+                dst[3 + 2 * set] = whi;
+            }
             la[e * QS + set] = make_uint2(wlo, whi);
         }
-        if (QS == 2) dst[6] = dst[7] = 0;
+        if (QS == 2 && writer) dst[6] = dst[7] = 0;
     }
-    if (tid < FATHOM_MAX_G) {
-        meta->cnt[tid] = 0u;
-        meta->cnt_exact[tid] = 0u;
+    if (writer) {
+        if (tid < FATHOM_MAX_G) {
+            meta->cnt[tid] = 0u;
+            meta->cnt_exact[tid] = 0u;
+        }
+        if (tid == 0) meta->ovf = 0u;
     }
-    if (tid == 0) meta->ovf = 0u;
     if (k <= 0) {
-        if (tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
-        return;
+        if (writer && tid < FATHOM_MAX_G) meta->tkey[tid] = 0u;
+        return nplanes;
     }
     __shared__ uint32_t tk[NQ];
     sample_thresholds<QS, NT>(planes, n, word_stride, k, h, nplanes, nkb, pl, first, la, cf, sf,
-                              tk, meta);
+                              tk, writer ? meta : nullptr);
     __syncthreads();  // the thresholds and the sums are complete
     if (tid < NQ * 8) {
         const int g = tid >> 3, m = tid & 7;
-        meta->xthr[g][m] = filter_threshold(g < G, tk[g], cf[g], sf[g], (double)rbi[g],
-                                            (double)mai[g], m);
+        const int32_t x = filter_threshold(g < G, tk[g], cf[g], sf[g], (double)rbi[g],
+                                           (double)mai[g], m);
+        if (writer) meta->xthr[g][m] = x;
+        if (xthr_lds) xthr_lds[tid] = x;
     }
-    if (tid >= NQ * 8 && tid < FATHOM_MAX_G * 8) meta->xthr[tid >> 3][tid & 7] = 0;
+    if (writer && tid >= NQ * 8 && tid < FATHOM_MAX_G * 8) meta->xthr[tid >> 3][tid & 7] = 0;
+    return nplanes;
 }
 
 // Threads of a prepare workgroup: 512 for one query set (its 212 registers allow two
@@ -548,7 +562,10 @@ __global__ __launch_bounds__(prep_threads<QS>()) void k_scan_prepare(
     const int t = depth[(size_t)h * kD + min(tid, kD - 1)];
     if (tid < kD) tc[tid] = min(t, kPlanes);
     __syncthreads();
-    prepare_head<QS, prep_threads<QS>()>(in, tc, H, G, planes, n, word_stride, k, ws, h);
+    __shared__ uint32_t pl[kMaxPlanesPerHead];
+    __shared__ uint2 la[kMaxKBlocks * 64 * QS];
+    prepare_head<QS, prep_threads<QS>()>(in, tc, H, G, planes, n, word_stride, k, ws, h, pl, la,
+                                         nullptr, true);
 }
 
 // A decode step's plan and prepare in one kernel: the depths stay in LDS between them
@@ -568,7 +585,9 @@ __global__ __launch_bounds__(prep_threads<QS>()) void k_plan_prepare(
     plan_load<NT>(q, var, G, h, qp, vp);
     plan_from<NT>(qp, vp, G, B, tc);
     if (tid < kD) depth[(size_t)h * kD + tid] = (uint8_t)tc[tid];
-    prepare_head<QS, NT>(in, tc, H, G, planes, n, word_stride, k, ws, h);
+    __shared__ uint32_t pl[kMaxPlanesPerHead];
+    __shared__ uint2 la[kMaxKBlocks * 64 * QS];
+    prepare_head<QS, NT>(in, tc, H, G, planes, n, word_stride, k, ws, h, pl, la, nullptr, true);
 }
 
 // ---------------------------------------------------------------------------------
@@ -841,13 +860,27 @@ __device__ __forceinline__ void load_head_consts(const ScanMeta *meta, int G, in
     }
 }
 
-// kWide: a head's 512 rows span 4 GiB or more, so the copies take 64-bit addresses
-// per lane; otherwise 32-bit byte offsets from the head's first row.
-template <int QS, bool kWide, bool kFilter>
-__global__ __launch_bounds__(kScanThreads)
-__attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) void k_scan_main(
+// The plan and prepare inputs of the fused front (k_front_fused).
+struct FrontIn {
+    const float *q, *var, *scale, *zero;
+    int B, k;
+    uint8_t *depth;  // the plan, written by each head's first workgroup
+};
+
+// Body of the scan kernels.  kWide: a head's 512 rows span 4 GiB or more, so the copies
+// take 64-bit addresses per lane; otherwise 32-bit byte offsets from the head's first row.
+// kFused (k_front_fused): the workgroup first plans and prepares its head itself (every
+// workgroup of a head computes the same plan, records and thresholds; the head's first
+// one also stores them for the select) and builds its LDS from that instead of loading
+// the records; its run is one super-step, and it adds no kept counts to the rows (the
+// select of one-chunk rows takes them from the masks).
+template <int QS, bool kWide, bool kFilter, bool kFused>
+__device__ __forceinline__ void scan_body(
     const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H, ScanSplit sp,
-    const char *__restrict__ ws, float *__restrict__ scores, uint32_t *__restrict__ masks) {
+    const char *__restrict__ ws, float *__restrict__ scores, uint32_t *__restrict__ masks,
+    const FrontIn &fz) {
+    static_assert(!kFused || (QS == 1 && kFilter && !kWide && kScanThreads == 512),
+                  "the fused front: one query set, filtering, 512 threads");
     extern __shared__ uint4 lds_u4[];
     char *lds = reinterpret_cast<char *>(lds_u4);
     lds_char *lds3 = (lds_char *)lds_u4;
@@ -871,10 +904,42 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
     const int h1 = (int)((b - 1) / nss);  // h0 or h0 + 1
     const ScanMeta *meta0 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h0 * kMetaBytes);
     const ScanMeta *meta1 = reinterpret_cast<const ScanMeta *>(ws + (size_t)h1 * kMetaBytes);
-    // clamped so that any workspace content keeps every read inside the head's data
-    const int nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);  // 4-group K-blocks
-    const int nkb1 = min(max(meta1->n_kblocks, 1), kMaxKBlocks);
     const int tid = threadIdx.x;
+    int nkb0, nkb1;  // 4-group K-blocks of the two heads
+    if constexpr (kFused) {
+        __shared__ int tc[kD];
+        PrepIn<1> in;
+        load_prep_in<1>(fz.q, fz.scale, fz.zero, G, h0, in);
+        float qp[FATHOM_MAX_G], vp;
+        plan_load<kScanThreads>(fz.q, fz.var, G, h0, qp, vp);
+        plan_from<kScanThreads>(qp, vp, G, fz.B, tc);
+        const bool writer = a == (long)h0 * nss;  // the head's first super-step
+        if (writer && fz.depth && tid < kD) fz.depth[(size_t)h0 * kD + tid] = (uint8_t)tc[tid];
+        // the plane list goes to the first tile (free until the first copies), the A
+        // operands and thresholds to head slot 0, where the scan reads them
+        uint32_t *plist = reinterpret_cast<uint32_t *>(lds + 2 * kHeadBytes);
+        const int np = prepare_head<1, kScanThreads>(
+            in, tc, H, G, planes, n, word_stride, fz.k, const_cast<char *>(ws), h0, plist,
+            reinterpret_cast<uint2 *>(lds), reinterpret_cast<int32_t *>(lds + kXthrOff), writer);
+        __syncthreads();
+        const int ngroups = (np + kGroupBits - 1) / kGroupBits;
+        nkb0 = nkb1 = min(max(1, (ngroups + kKBlockGroups - 1) / kKBlockGroups), kMaxKBlocks);
+        // the row table as the records give it: row r of K-block kb is plane r & 7 of
+        // group 4 kb + (r >> 3); absent rows read the head's first planned row
+        uint32_t *lrow = reinterpret_cast<uint32_t *>(lds + kRowsOff);
+        const uint32_t dead = np > 0 ? plist[0] * (uint32_t)word_stride * 4u : 0u;
+        const int nk2 = 2 * ((nkb0 + 1) >> 1);
+        for (int e = tid; e < nk2 * 32; e += kScanThreads) {
+            const int kb = e >> 5, r = e & 31;
+            const int p = (kKBlockGroups * kb + (r >> 3)) * kGroupBits + (r & 7);
+            lrow[((kb >> 1) * 32 + r) * 2 + (kb & 1)] =
+                kb < nkb0 && p < np ? plist[p] * (uint32_t)word_stride * 4u : dead;
+        }
+        __syncthreads();
+    } else {
+    // clamped so that any workspace content keeps every read inside the head's data
+    nkb0 = min(max(meta0->n_kblocks, 1), kMaxKBlocks);
+    nkb1 = min(max(meta1->n_kblocks, 1), kMaxKBlocks);
     // The head slots' LDS from the operand records.  Every record of the kMaxKBlocks a
     // head may have is loaded, unconditionally and in the same round as the K-block counts
     // above (the ones past a head's count are dropped), so that one memory latency, not
@@ -931,13 +996,16 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         }
     }
     __syncthreads();
+    }
 
     const int lane = tid & 63, wave = tid >> 6;
     const int s = lane & 3, wq = (lane >> 2) & 3, jq = lane >> 4;
     const size_t head_words = (size_t)kMaxPlanesPerHead * word_stride;
     float C0[QS], S0[QS], C1[QS], S1[QS];
-    load_head_consts<QS>(meta0, G, jq, C0, S0);
-    load_head_consts<QS>(meta1, G, jq, C1, S1);
+    if constexpr (!kFilter) {  // only the full scores use them
+        load_head_consts<QS>(meta0, G, jq, C0, S0);
+        load_head_consts<QS>(meta1, G, jq, C1, S1);
+    }
     const bool small = max(nkb0, nkb1) < kMaxKBlocks;
     const int npr0 = (nkb0 + 1) >> 1, npr1 = (nkb1 + 1) >> 1;  // K-pairs per super-step
     // super-steps of the run, counted from a: [0, h1rel) in head h0, [h1rel, len) in h1
@@ -1115,7 +1183,7 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
         }
     }
     if (pk >= 0) combine();
-    if constexpr (kFilter) {  // the run's kept counts and overflow bits into its rows
+    if constexpr (kFilter && !kFused) {  // the run's kept counts and overflow bits into its rows
         if ((lane & 15) == 0) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
@@ -1132,6 +1200,27 @@ __attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) voi
             }
         }
     }
+}
+
+template <int QS, bool kWide, bool kFilter>
+__global__ __launch_bounds__(kScanThreads)
+__attribute__((amdgpu_waves_per_eu(QS == 1 ? FATHOM_SCAN_WAVES_PER_EU : 2))) void k_scan_main(
+    const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H, ScanSplit sp,
+    const char *__restrict__ ws, float *__restrict__ scores, uint32_t *__restrict__ masks) {
+    scan_body<QS, kWide, kFilter, false>(planes, n, word_stride, G, H, sp, ws, scores, masks,
+                                         FrontIn{});
+}
+
+constexpr long kFrontMaxGroups = 256;  // (head, super-step) workgroups of the fused front
+
+// A decode step's front for few heads of one-chunk rows: plan, prepare and filtering scan
+// in one kernel, one workgroup per (head, super-step).  It saves the scan's reload of the
+// records and a launch; the prepare work is repeated by each workgroup of a head.
+__global__ __launch_bounds__(kScanThreads)
+__attribute__((amdgpu_waves_per_eu(FATHOM_SCAN_WAVES_PER_EU))) void k_front_fused(
+    const uint32_t *__restrict__ planes, int n, int word_stride, int G, int H, ScanSplit sp,
+    char *__restrict__ ws, float *__restrict__ cand, uint32_t *__restrict__ masks, FrontIn fz) {
+    scan_body<1, false, true, true>(planes, n, word_stride, G, H, sp, ws, cand, masks, fz);
 }
 
 // Resident workgroups of a kernel instance over the device (asked once per device).
@@ -1227,6 +1316,31 @@ hipError_t launch_scan_main(const fathom_store &st, int G, float *scores, void *
     const char *w = static_cast<const char *>(ws);
     return query_sets(G) == 1 ? launch_main_q<1>(st, G, scores, w, masks, s)
                               : launch_main_q<2>(st, G, scores, w, masks, s);
+}
+
+bool front_fused_applies(const fathom_store &st, int G) {
+    const int W = (st.n_tokens + 31) >> 5;
+    const long nss = (W + kSuperWords - 1) / kSuperWords;
+    const bool wide = (uint64_t)kMaxPlanesPerHead * (uint64_t)st.word_stride * 4u > 0xFFFFFFFFull;
+    return query_sets(G) == 1 && !wide && st.n_tokens <= kTopkChunk &&
+           (long)st.n_heads * nss <= kFrontMaxGroups;
+}
+
+hipError_t launch_front_fused(const fathom_store &st, const float *q, int G, int B, int k,
+                              uint8_t *depth, void *ws, float *cand, uint32_t *masks,
+                              hipStream_t s) {
+    if (!front_fused_applies(st, G)) return hipErrorInvalidValue;
+    const int W = (st.n_tokens + 31) >> 5;
+    ScanSplit sp;
+    sp.nss = (W + kSuperWords - 1) / kSuperWords;
+    sp.run = 1;
+    sp.flat = 0;
+    sp.wgs_per_head = sp.nss;
+    FrontIn fz{q, st.var, st.scale, st.zero, B, k, depth};
+    hipLaunchKernelGGL(k_front_fused, dim3((unsigned)(st.n_heads * sp.nss)), dim3(kScanThreads),
+                       scan_lds_bytes<1>(), s, st.planes, st.n_tokens, st.word_stride, G,
+                       st.n_heads, sp, static_cast<char *>(ws), cand, masks, fz);
+    return hipGetLastError();
 }
 
 }  // namespace fathom

@@ -266,7 +266,7 @@ __device__ __forceinline__ void select_chunk(
     int64_t row, int chunk, const float *__restrict__ vals, const int32_t *__restrict__ in_idx,
     int64_t row_len, int64_t in_stride, int k, float *__restrict__ out_val,
     int32_t *__restrict__ out_idx, int64_t out_stride, const FilterArgs &fa,
-    int32_t *lds_idx = nullptr) {
+    int32_t *lds_idx = nullptr, bool direct_rescore = false) {
     __shared__ __align__(16) uint32_t hist[4096];
     __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t scan_sh[17];
@@ -291,8 +291,10 @@ __device__ __forceinline__ void select_chunk(
         const int word = chunk * kThreads + tid;
         if constexpr (!kCandOut && kDirect) {
             // Run alone (a row of one chunk), the select itself counts the kept keys
-            // that clear the row's threshold exactly (otherwise the lean select did).
-            bool rescore = meta->cnt[g] < (uint32_t)k || ((meta->ovf >> g) & 1u);
+            // that clear the row's threshold exactly (otherwise the lean select did);
+            // whether the candidates are complete its caller found from the masks (the
+            // scan's overflow bit, when it set one, says the same).
+            bool rescore = direct_rescore || ((meta->ovf >> g) & 1u);
             if (!rescore) {
                 const uint32_t lenmask = vmask;
                 vmask = load_kept(reinterpret_cast<const int2 *>(vals + row * fa.cstride),
@@ -588,11 +590,13 @@ __device__ __forceinline__ void select_kept(
     ScanMeta *meta =
         reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws) + (size_t)h * kMetaBytes);
     // a row chunk that needs the full select: listed for the redo kernel, or (kDirect)
-    // finished here by all NT threads (the condition is the same for every thread)
+    // finished here by all NT threads (the condition is the same for every thread), with
+    // every token rescored when `full` (its candidates may miss a winner)
+    bool full = false;
     auto hand_over = [&]() {
         if constexpr (kDirect)
             select_chunk<false, false, true, true>(row, 0, cand, nullptr, n, n, k, nullptr,
-                                                   out_idx, 0, fa, lds_idx);
+                                                   out_idx, 0, fa, lds_idx, full);
         else if (tid == 0)
             list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)(row * nch + chunk);
     };
@@ -605,7 +609,11 @@ __device__ __forceinline__ void select_kept(
 #pragma unroll
     for (int j = 0; j < WPT; ++j)
         mk[j] = fa.masks[row * fa.W + min(wg + j, (int64_t)fa.W - 1)];
-    const uint32_t kept = meta->cnt[g];
+    // the direct select's rows are one chunk: their kept count is the masks' and a block
+    // overflowed its records exactly when it kept more than it holds, so both come from
+    // the masks (the scan need not have counted them); else from the scan's counts
+    const uint32_t kept = kDirect ? 0u : meta->cnt[g];
+    const bool no_records = kDirect && meta->n_planes > 480;
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
         const int t0 = 32 * (wl + j);  // first chunk token of the word
@@ -613,7 +621,7 @@ __device__ __forceinline__ void select_kept(
         mk[j] = wg + j < fa.W ? mk[j] & lm : 0u;
     }
     // the row is rescored by the full select
-    const bool full = kept < (uint32_t)k || ((meta->ovf >> g) & 1u);
+    full = kDirect ? no_records : kept < (uint32_t)k || ((meta->ovf >> g) & 1u);
     uint32_t csum = 0u;
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
@@ -621,9 +629,24 @@ __device__ __forceinline__ void select_kept(
         c[j] = (uint32_t)__popc(mk[j]);
         csum += c[j];
     }
+    if constexpr (kDirect) {  // thread 8b + j holds word j of block b: the block's count
+        uint32_t bc = csum;
+        bc += (uint32_t)__shfl_xor((int)bc, 1, 64);
+        bc += (uint32_t)__shfl_xor((int)bc, 2, 64);
+        bc += (uint32_t)__shfl_xor((int)bc, 4, 64);
+        const uint32_t cap = fa.qs == 1 ? 64u : (uint32_t)kBlockRecords;
+        // flag it in bits 20 and up of the first word's count: the prefix's total then
+        // carries the overflowing blocks (C <= 32768 < 2^20)
+        if ((tid & 7) == 0 && bc > cap) csum += 1u << 20;
+    }
     for (int b = tid; b < kSelBins; b += NT) hist[b] = 0u;
     uint32_t C;
-    const uint32_t pos0 = block_prefix1<NT>(csum, sh[0], &C);
+    uint32_t pos0 = block_prefix1<NT>(csum, sh[0], &C);
+    if constexpr (kDirect) {
+        full = full || (C >> 20) != 0 || (C & 0xFFFFFu) < (uint32_t)k;
+        C &= 0xFFFFFu;
+        pos0 &= 0xFFFFFu;
+    }
     if (full || C > (uint32_t)kSelCap) {
         hand_over();
         return;
