@@ -92,7 +92,7 @@ size_t step_ws_bytes(int H, int G, int n, int k) {
     return round256(scan_ws_bytes(H, G)) + round256(cand_bytes(H, G, n)) +
            round256(topk_ws_bytes(H * G, n, k)) + round256((size_t)H * G * k * sizeof(int32_t)) +
            round256((size_t)H * FATHOM_D) + round256(filter_mask_bytes(H, G, n)) +
-           round256(filter_redo_bytes(H, G, n));
+           round256(filter_redo_bytes(H, G, n)) + round256(attn_part_bytes(H * G, n, k));
 }
 
 size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
@@ -445,6 +445,8 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     uint32_t *masks = reinterpret_cast<uint32_t *>(w);
     w += round256(filter_mask_bytes(H, G, n));
     uint32_t *redo = reinterpret_cast<uint32_t *>(w);
+    w += round256(filter_redo_bytes(H, G, n));
+    float *part = reinterpret_cast<float *>(w);  // the split attention's partial results
 
     const hipStream_t s = as_stream(stream);
     auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], s)) : FATHOM_OK; };
@@ -462,7 +464,7 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
         FATHOM_TRY(mark(1));
         FATHOM_TRY(mark(2));
         FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k, idx,
-                                                          q, K, V, sm_scale, out, s)));
+                                                          q, K, V, sm_scale, out, part, s)));
         FATHOM_TRY(mark(3));
         return mark(4);
     }
@@ -480,7 +482,8 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
             // few rows of one chunk (a layer of a decode step): select and attention in one
             // kernel; its time falls in the select phase, the attention phase is empty
             FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k,
-                                                              idx, q, K, V, sm_scale, out, s)));
+                                                              idx, q, K, V, sm_scale, out,
+                                                              part, s)));
             FATHOM_TRY(mark(3));
             return mark(4);
         }

@@ -5,16 +5,25 @@
 namespace fathom {
 namespace {
 
-constexpr int kSmallRows = 256;  // (head, query) rows up to which workgroups have 1024 threads
+constexpr int kSmallRows = 256;  // (head, query) rows up to which a row is cut into shares
 
-template <int NT>
-__global__ __launch_bounds__(NT) void k_sparse_attn(
+__global__ __launch_bounds__(256) void k_sparse_attn(
     const float *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
     float sm_scale, uint16_t *__restrict__ out) {
     const int32_t *ix = idx + (size_t)blockIdx.x * k;
-    attend_row<NT>(q, K, V, G, n, [ix](int r) { return ix[r]; }, k, sm_scale, out,
-                   (int)blockIdx.x);
+    attend_row<256>(q, K, V, G, n, [ix](int r) { return ix[r]; }, k, sm_scale, out,
+                    (int)blockIdx.x);
+}
+
+// Few rows: one workgroup of kShares waves a row.
+__global__ __launch_bounds__(kShares * 64) void k_sparse_attn_shares(
+    const float *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
+    float sm_scale, uint16_t *__restrict__ out) {
+    const int32_t *ix = idx + (size_t)blockIdx.x * k;
+    attend_row_shares(q, K, V, G, n, [ix](int r) { return ix[r]; }, k, sm_scale, out,
+                      (int)blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src,
@@ -58,11 +67,11 @@ hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t 
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s) {
     if (H * G <= kSmallRows)
-        hipLaunchKernelGGL(k_sparse_attn<1024>, dim3(H * G), dim3(1024), 0, s, q, K, V, G, n,
-                           idx, k, sm_scale, out);
+        hipLaunchKernelGGL(k_sparse_attn_shares, dim3(H * G), dim3(kShares * 64), 0, s, q, K,
+                           V, G, n, idx, k, sm_scale, out);
     else
-        hipLaunchKernelGGL(k_sparse_attn<256>, dim3(H * G), dim3(256), 0, s, q, K, V, G, n,
-                           idx, k, sm_scale, out);
+        hipLaunchKernelGGL(k_sparse_attn, dim3(H * G), dim3(256), 0, s, q, K, V, G, n, idx, k,
+                           sm_scale, out);
     return hipGetLastError();
 }
 

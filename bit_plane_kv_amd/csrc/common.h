@@ -39,7 +39,8 @@ constexpr int kDigits = 4;                   // signed base-256 digits per weigh
 //   (c*4 + j, channels ascending, planes ascending within a channel); uint32
 //   cnt_exact[8] (candidates whose exact score clears the threshold, counted by the
 //   select); uint32 ovf (bit g: a 256-token block of query g had more candidates than
-//   its record area holds); int32 xthr[8][8] (the filter's integer thresholds, below).
+//   its record area holds); int32 xthr[8][8] (the filter's integer thresholds, below);
+//   uint32 attn_done[8] (workgroups of query g's split attention that have finished).
 //   record (kblock, lane), lane = 16*kb + 4*w + s:  uint32 row of plane s and of plane
 //   s+4 of group 4*kblock + kb (kSkipRow: no plane, load nothing), then for each set of
 //   4 queries the 8 bytes of A row (lane & 15) = (query 4*set + ((lane & 15) >> 2),
@@ -60,6 +61,7 @@ struct ScanMeta {
     uint32_t cnt_exact[FATHOM_MAX_G];
     uint32_t ovf;
     int32_t xthr[FATHOM_MAX_G][8];
+    uint32_t attn_done[FATHOM_MAX_G];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
 
@@ -195,11 +197,14 @@ hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand
 // the same select fused with the attention of each row (rows of one chunk, few rows, small
 // k: filtered_attend_applies); idx still receives the winners
 bool filtered_attend_applies(int R, int n, int k);
+// the partial results of the fused select-attend's split attention (0 where it does not
+// apply)
+size_t attn_part_bytes(int R, int n, int k);
 hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,
                                        const uint32_t *masks, void *scan_ws, int k,
                                        int32_t *idx, const float *q, const uint16_t *K,
                                        const uint16_t *V, float sm_scale, uint16_t *out,
-                                       hipStream_t s);
+                                       float *part, hipStream_t s);
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s);
