@@ -696,8 +696,9 @@ def grouped_lines(args, kern):
     """The grouped store (fp16 scale and zero per 128-token group: 68 B per token per KV
     head, the index size of the blog's "Where this does not work") on the bench workload:
     its build, a decode-time append of one token to every head (the last group
-    re-quantized and every variance recomputed), and its scan at the bench budget, with
-    one sampled head checked against the oracle."""
+    re-quantized and every variance recomputed), its scan at the bench budget, with
+    one sampled head checked against the oracle, and its decode step (plan, scan of every
+    score, top-k, attention: fathom_step_grouped) over all heads and over one layer's 8."""
     import torch
     import oracle
     from bit_plane_kv_amd import fathom as F
@@ -730,6 +731,34 @@ def grouped_lines(args, kern):
     ref = oracle.scores_grouped(codes, s16, z16, ref_depth, q[h:h + 1].cpu().numpy())
     got = scores[h:h + 1].cpu().numpy()
     rel = float((np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+    # the decode step over the grouped store: all heads at once, then one layer (8 heads)
+    k, sm = cfg.k, float(np.float32(1.0 / np.sqrt(128)))
+    Kb = keys.to(torch.bfloat16)
+    V = synth.values_torch(args.seed, cfg.cfg_id, list(range(H)), n, dev)
+    out = torch.empty((H, G, 128), dtype=torch.bfloat16, device=dev)
+    ws = F.step_grouped_workspace(gs, G, k, dev)
+    step_ms = timed_ms(lambda: F.fathom_step_grouped(gs, q, Kb, V, B, k, sm, out=out, ws=ws),
+                       stream, 10, flush, sink)
+    hl = min(H, 8)
+    gl = F.GStore(gs.planes[:hl], gs.scale16[:hl], gs.zero16[:hl], gs.sums[:hl], gs.var[:hl],
+                  gs.prefix[:hl], gs.prefix_groups[:hl], n)
+    wl = F.step_grouped_workspace(gl, G, k, dev)
+    layer_ms = timed_ms(lambda: F.fathom_step_grouped(gl, q[:hl], Kb[:hl], V[:hl], B, k, sm,
+                                                      out=out[:hl], ws=wl), stream, 10, flush,
+                        sink)
+    # its winners for the sampled head: the oracle's top-k of the scores it computed
+    sh = F.GStore(gs.planes[h:h + 1], gs.scale16[h:h + 1], gs.zero16[h:h + 1],
+                  gs.sums[h:h + 1], gs.var[h:h + 1], gs.prefix[h:h + 1],
+                  gs.prefix_groups[h:h + 1], n)
+    s_h = torch.empty((1, G, n), dtype=torch.float32, device=dev)
+    i_h = torch.empty((1, G, k), dtype=torch.int32, device=dev)
+    F.fathom_step_grouped(sh, q[h:h + 1], Kb[h:h + 1], V[h:h + 1], B, k, sm, scores_out=s_h,
+                          idx_out=i_h)
+    torch.cuda.synchronize()
+    step_ok = bool(np.array_equal(i_h.cpu().numpy()[0],
+                                  oracle.topk(s_h.cpu().numpy()[0], k)) and
+                   torch.equal(s_h, scores[h:h + 1]))
+    del Kb, V, out, ws, wl
     ok = bool(np.array_equal(gs.scale16[h:h + 1, :ng].cpu().numpy().view(np.uint16)
                              .transpose(0, 2, 1), s16)
               and np.array_equal(depth[h:h + 1].cpu().numpy(), ref_depth) and rel <= 1e-5)
@@ -738,10 +767,16 @@ def grouped_lines(args, kern):
            "scan_ms": round(scan_ms, 4),
            "scan_ms_per_channel_store_matrix_cores": round(kern["scan_ms"], 4),
            "scan_gkeys_per_s": round(H * n / (scan_ms * 1e-3) / 1e9, 1),
-           "oracle_check_head": h, "score_rel_err": rel, "ok": ok}
+           "oracle_check_head": h, "score_rel_err": rel, "ok": ok,
+           "decode_step": {"k": k, "ms_all_heads": round(step_ms, 4),
+                           "ms_one_layer": round(layer_ms, 4), "layer_kv_heads": hl,
+                           "timing": "fathom_step_grouped (plan, full scan, top-k, attention), "
+                                     "cold caches, mean of 10 launches",
+                           "winners_check_head": h, "winners_ok": step_ok}}
     log(f"[bench] grouped store: build {build_ms:.2f} ms, append {append_ms * 1e3:.1f} us, "
         f"scan {scan_ms * 1e3:.1f} us (per-channel matrix-core scan "
-        f"{kern['scan_ms'] * 1e3:.1f} us), check {ok}")
+        f"{kern['scan_ms'] * 1e3:.1f} us), check {ok}; decode step {step_ms * 1e3:.1f} us "
+        f"(one layer {layer_ms * 1e3:.1f} us), winners check {step_ok}")
     del keys, gs, scores, flush
     torch.cuda.empty_cache()
     return res

@@ -95,6 +95,12 @@ size_t step_ws_bytes(int H, int G, int n, int k) {
            round256(filter_redo_bytes(H, G, n)) + round256(attn_part_bytes(H * G, n, k));
 }
 
+// the grouped step: every score, the top-k levels, the winners, the depths
+size_t step_grouped_ws_bytes(int H, int G, int n, int k) {
+    return round256((size_t)H * G * n * sizeof(float)) + round256(topk_ws_bytes(H * G, n, k)) +
+           round256((size_t)H * G * k * sizeof(int32_t)) + round256((size_t)H * FATHOM_D);
+}
+
 size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
     return round256(scan_ws_bytes(H, G)) + round256(cand_bytes(H, G, n)) +
            round256(filter_mask_bytes(H, G, n)) + round256(topk_ws_bytes(H * G, n, k)) +
@@ -194,6 +200,12 @@ int fathom_workspace_size(int op, int H, int G, int n, int k, size_t *bytes) {
         FATHOM_TRY(check_g(G));
         FATHOM_TRY(check_topk_k(n, k));
         *bytes = scan_topk_ws_bytes(H, G, n, k);
+        return FATHOM_OK;
+    case FATHOM_OP_STEP_GROUPED:
+        if (H < 1) return FATHOM_ERR_INVALID_ARG;
+        FATHOM_TRY(check_g(G));
+        FATHOM_TRY(check_topk_k(n, k));
+        *bytes = step_grouped_ws_bytes(H, G, n, k);
         return FATHOM_OK;
     default: return FATHOM_ERR_INVALID_ARG;
     }
@@ -320,6 +332,47 @@ int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const ui
     FATHOM_TRY(check_all({q, depth, scores}));
     return hip_status(launch_scan_grouped(*gs, q, depth, G, scores, is_pinned_host(gs->planes),
                                           as_stream(stream)));
+}
+
+int fathom_step_grouped(const fathom_gstore *gs, const float *q, const uint16_t *K,
+                        const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                        uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                        size_t ws_bytes, void *stream) {
+    FATHOM_TRY(check_gstore(gs));
+    if (!q || !K || !V || !out || !ws) return FATHOM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 2) ||
+        !aligned(ws, 16) || (scores_out && !aligned(scores_out, 16)) ||
+        (idx_out && !aligned(idx_out, 4)))
+        return FATHOM_ERR_INVALID_ARG;
+    FATHOM_TRY(check_g(G));
+    if (B < 0 || B > FATHOM_D * FATHOM_PLANES) return FATHOM_ERR_BUDGET;
+    const int H = gs->n_heads, n = gs->n_tokens;
+    FATHOM_TRY(check_topk_k(n, k));
+    if (ws_bytes < step_grouped_ws_bytes(H, G, n, k)) return FATHOM_ERR_WORKSPACE;
+    FATHOM_TRY(check_all({q, K, V, out, depth_out, scores_out, idx_out, ws}));
+
+    char *w = static_cast<char *>(ws);
+    float *scores = scores_out ? scores_out : reinterpret_cast<float *>(w);
+    w += round256((size_t)H * G * n * sizeof(float));
+    void *topk_ws = w;
+    w += round256(topk_ws_bytes(H * G, n, k));
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(w);
+    w += round256((size_t)H * G * k * sizeof(int32_t));
+    uint8_t *depth = depth_out ? depth_out : reinterpret_cast<uint8_t *>(w);
+
+    fathom_store view{};  // the plan reads planes' shape and var only
+    view.n_heads = H;
+    view.n_tokens = n;
+    view.d = gs->d;
+    view.word_stride = gs->word_stride;
+    view.planes = gs->planes;
+    view.var = gs->var;
+    const hipStream_t s = as_stream(stream);
+    FATHOM_TRY(hip_status(launch_plan(view, q, G, B, depth, s)));
+    FATHOM_TRY(hip_status(
+        launch_scan_grouped(*gs, q, depth, G, scores, is_pinned_host(gs->planes), s)));
+    FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
+    return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
 }
 
 int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream) {

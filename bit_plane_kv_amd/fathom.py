@@ -24,7 +24,7 @@ TOPK_CHUNK = 32768
 (OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NOT_MAPPED, ERR_HIP,
  ERR_SCRATCH) = range(8)
 STATIC_SCRATCH_BYTES = 64 << 20  # the static workspace of fathom_step_noalloc
-OP_QUANTIZE, OP_SCAN, OP_TOPK, OP_STEP, OP_SCAN_TOPK = range(5)
+OP_QUANTIZE, OP_SCAN, OP_TOPK, OP_STEP, OP_SCAN_TOPK, OP_STEP_GROUPED = range(6)
 
 
 class FathomError(RuntimeError):
@@ -82,6 +82,8 @@ _SIGS = {
                                     _P]),
     "fathom_plan_grouped": (_I, [ctypes.POINTER(fathom_gstore), _P, _I, _I, _P, _P]),
     "fathom_scan_grouped": (_I, [ctypes.POINTER(fathom_gstore), _P, _I, _P, _P, _P]),
+    "fathom_step_grouped": (_I, [ctypes.POINTER(fathom_gstore), _P, _P, _P, _I, _I, _I,
+                                 ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
     "fathom_scan_nibble": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P]),
     "fathom_stream_read": (_I, [_P, _SZ, _P, _P]),
     "fathom_stream_read_runs": (_I, [_P, _SZ, _SZ, _SZ, _P, _P]),
@@ -407,6 +409,27 @@ def fathom_sparse_attn(q, K, V, idx, sm_scale: float, out=None, stream=None):
     _check(lib().fathom_sparse_attn(_ptr(q), _ptr(K), _ptr(V), H, G, n, d, _ptr(idx), k,
                                     float(sm_scale), _ptr(out), _stream(stream)),
            "fathom_sparse_attn")
+    return out
+
+
+def step_grouped_workspace(gstore: GStore, G: int, k: int, device):
+    return _workspace(workspace_size(OP_STEP_GROUPED, gstore.n_heads, G, gstore.n_tokens, k),
+                      device)
+
+
+def fathom_step_grouped(gstore: GStore, q, K, V, B: int, k: int, sm_scale: float, out=None,
+                        depth_out=None, scores_out=None, idx_out=None, ws=None, stream=None):
+    import torch
+    H, G, d = q.shape
+    if out is None:
+        out = torch.empty((H, G, d), dtype=torch.bfloat16, device=q.device)
+    ws = step_grouped_workspace(gstore, G, k, q.device) if ws is None else ws
+    gs = gstore.descriptor()
+    _check(lib().fathom_step_grouped(ctypes.byref(gs), _ptr(q), _ptr(K), _ptr(V), G, int(B),
+                                     int(k), float(sm_scale), _ptr(out), _ptr(depth_out),
+                                     _ptr(scores_out), _ptr(idx_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "fathom_step_grouped")
     return out
 
 

@@ -124,7 +124,8 @@ enum fathom_op {
     FATHOM_OP_SCAN = 1,     /* fathom_scan / fathom_scan_prepare(d): uses H, G */
     FATHOM_OP_TOPK = 2,     /* fathom_topk: uses H as the row count R, n, k */
     FATHOM_OP_STEP = 3,     /* fathom_step: uses H, G, n, k */
-    FATHOM_OP_SCAN_TOPK = 4 /* fathom_scan_topk: uses H, G, n, k */
+    FATHOM_OP_SCAN_TOPK = 4, /* fathom_scan_topk: uses H, G, n, k */
+    FATHOM_OP_STEP_GROUPED = 5 /* fathom_step_grouped: uses H, G, n, k */
 };
 
 /* Bytes of workspace `op` needs for the given sizes (0 is possible).  Status only. */
@@ -264,6 +265,22 @@ int fathom_plan_grouped(const fathom_gstore *gs, const float *q, int G, int B,
  */
 int fathom_scan_grouped(const fathom_gstore *gs, const float *q, int G, const uint8_t *depth,
                         float *scores, void *stream);
+
+/*
+ * One decode step over the grouped store (blog, "That is the whole method", on the index
+ * of "Where this does not work"): fathom_plan_grouped -> fathom_scan_grouped (every
+ * score) -> fathom_topk -> fathom_sparse_attn, enqueued on `stream` with no host
+ * synchronization; the same results as those four calls made in turn.
+ *   q [H][G][d] fp32; K, V [H][n][d] bf16 bits (HBM or pinned host); out [H][G][d] bf16.
+ *   depth_out [H][d], scores_out [H][G][n] fp32 (16-byte aligned) and idx_out [H][G][k]
+ *   are optional (NULL: the intermediate lives in ws).
+ *   0 <= B <= d*4 (else FATHOM_ERR_BUDGET); k as for fathom_topk.
+ *   ws: FATHOM_OP_STEP_GROUPED bytes, 16-byte aligned (FATHOM_ERR_WORKSPACE if smaller).
+ */
+int fathom_step_grouped(const fathom_gstore *gs, const float *q, const uint16_t *K,
+                        const uint16_t *V, int G, int B, int k, float sm_scale, uint16_t *out,
+                        uint8_t *depth_out, float *scores_out, int32_t *idx_out, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /*
  * The ordinary 4-bit layout the pages compare the bit planes against (blog, "Where this

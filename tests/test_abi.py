@@ -198,6 +198,15 @@ def test_workspace_formulas():
                 r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
                 r256(H * G * ((n + 32767) // 32768) * 4))
         assert F.workspace_size(F.OP_SCAN_TOPK, H, G, n, k) == want
+    # grouped step: every score (fp32), the top-k levels, the winners, the depths
+    for H, G, n, k in [(2, 4, 100, 10), (288, 4, 32768, 512), (8, 4, 1 << 20, 512)]:
+        want = (r256(H * G * n * 4) + r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
+                r256(H * G * k * 4) + r256(H * 128))
+        assert F.workspace_size(F.OP_STEP_GROUPED, H, G, n, k) == want
+    with pytest.raises(F.FathomError):
+        F.workspace_size(F.OP_STEP_GROUPED, 8, 9, 100, 10)
+    with pytest.raises(F.FathomError):
+        F.workspace_size(F.OP_STEP_GROUPED, 8, 4, 100, 101)
     # quantize: min/max partials + integer sums
     q = F.workspace_size(F.OP_QUANTIZE, 2, 1, 4096, 1)
     assert q == 2 * 2 * 2 * 128 * 4 + 2 * 128 * 16

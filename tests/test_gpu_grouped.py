@@ -127,3 +127,60 @@ def test_grouped_scan_from_pinned_host_memory_equals_hbm():
     assert torch.equal(got, ref)
     s16, z16, codes = oracle.quantize_grouped(keys)
     check_rows(got.cpu().numpy(), oracle.scores_grouped(codes, s16, z16, depth.cpu().numpy(), q))
+
+
+@pytest.mark.parametrize("H,G,n,B,k", [(2, 4, 3000, 92, 64), (1, 8, 777, 136, 100),
+                                       (3, 4, 5000, 0, 512), (2, 2, 40000, 92, 512),
+                                       (1, 4, 130, 512, 130)])
+def test_grouped_step_matches_oracle(H, G, n, B, k):
+    """The grouped decode step against the oracle: the plan bit-exact, every score within
+    1e-5 of the oracle's fp64 scores, the winners exactly the oracle's top-k of the scores
+    the step computed, the output within 2e-2 of the oracle's attention over them."""
+    torch = torch_cuda()
+    print(f"[grouped step] H={H} G={G} n={n} B={B} k={k}", flush=True)
+    keys, q, K, V = inputs(124, H, G, n)
+    gs = _build(keys)
+    s16, z16, codes = oracle.quantize_grouped(keys)
+    var = oracle.var_grouped(codes, s16, z16)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    depth = torch.empty((H, 128), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((H, G, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    out = F.fathom_step_grouped(gs, q_t, Kd, Vd, B, k, sm, depth_out=depth, scores_out=scores,
+                                idx_out=idx)
+    torch.cuda.synchronize()
+    ref_depth = oracle.plan(q, var, B)
+    assert np.array_equal(depth.cpu().numpy(), ref_depth)
+    check_rows(scores.cpu().numpy(), oracle.scores_grouped(codes, s16, z16, ref_depth, q))
+    got = idx.cpu().numpy()
+    assert np.array_equal(got.reshape(H * G, k),
+                          oracle.topk(scores.cpu().numpy().reshape(H * G, n), k))
+    ref_out = oracle.attention(q, K, V, got, sm)
+    assert np.abs(out.float().cpu().numpy() - ref_out).max() <= 2e-2
+
+
+@pytest.mark.parametrize("H,G,n,k", [(2, 4, 5000, 128), (4, 4, 32768, 512)])
+def test_grouped_step_equals_its_four_calls(H, G, n, k):
+    """fathom_step_grouped with no optional outputs (intermediates in its workspace) gives
+    the outputs, bit for bit, of plan, scan, top-k and attention called one by one, also
+    when the same workspace serves a second step of other queries."""
+    torch = torch_cuda()
+    print(f"[grouped step calls] H={H} G={G} n={n} k={k}", flush=True)
+    keys, q, K, V = inputs(125, H, G, n)
+    gs = _build(keys)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    ws = F.step_grouped_workspace(gs, G, k, "cuda")
+    for rep in range(2):
+        q_t = to_dev(q) if rep == 0 else to_dev(q[:, ::-1].copy())
+        out = F.fathom_step_grouped(gs, q_t, Kd, Vd, 92, k, sm, ws=ws)
+        depth = F.fathom_plan_grouped(gs, q_t, 92)
+        scores = F.fathom_scan_grouped(gs, q_t, depth)
+        idx = F.fathom_topk(scores, k)
+        ref = F.fathom_sparse_attn(q_t, Kd, Vd, idx, sm)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
