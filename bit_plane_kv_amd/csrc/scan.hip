@@ -790,7 +790,9 @@ __device__ __forceinline__ void combine_filter(const v4i (&acc)[2][8][QS], const
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         const v4i d = acc[pos][m][set];
-                        lds_char *a = keep[m] && k < (uint32_t)kStage ? stage + 8u * k : dummy;
+                        // past the block's room the record lands in its last slot: such a
+                        // block overflowed, and its records are never copied out
+                        lds_char *a = keep[m] ? stage + 8u * min(k, (uint32_t)kStage - 1u) : dummy;
                         *reinterpret_cast<lds_v2i *>(a) = v2i{d[2] + d[3] * 256, d[0] + d[1] * 256};
                         k += keep[m] ? 1u : 0u;
                     }
