@@ -563,6 +563,10 @@ __device__ __forceinline__ uint32_t block_prefix1(uint32_t v, uint32_t *sh, uint
     return inc - v + before;
 }
 
+// A radix pass that leaves at most this many keys in the winning bin is the last: they
+// are ranked directly.
+constexpr int kFewKeys = 64;
+
 // The lean select's body for NT threads (256, or 1024 with kDirect).
 template <bool kCandOut, bool kDirect, int NT>
 __device__ __forceinline__ void select_kept(
@@ -581,6 +585,7 @@ __device__ __forceinline__ void select_kept(
     __shared__ uint32_t sh[2][NW];
     __shared__ uint32_t pick[2][3];
     __shared__ uint32_t smm[3][NW];  // per-wave min and max key, count clearing the threshold
+    __shared__ uint32_t few[kFewKeys], nfew, few_key, few_above;  // a small pivot bin's keys
     const int tid = threadIdx.x, chunk = blockIdx.x, nch = gridDim.x;
     const int64_t row = (int64_t)row0 + blockIdx.y;
     const int64_t start = (int64_t)chunk * kTopkChunk;
@@ -640,6 +645,7 @@ __device__ __forceinline__ void select_kept(
         if ((tid & 7) == 0 && bc > cap) csum += 1u << 20;
     }
     for (int b = tid; b < kSelBins; b += NT) hist[b] = 0u;
+    if (tid == 0) nfew = 0u;
     uint32_t C;
     uint32_t pos0 = block_prefix1<NT>(csum, sh[0], &C);
     if constexpr (kDirect) {
@@ -823,6 +829,33 @@ __device__ __forceinline__ void select_kept(
         const uint32_t in_bin = pick[pass & 1][2];
         shift = sd;
         if (in_bin == need) break;
+        if (shift > 0 && in_bin <= (uint32_t)kFewKeys) {
+            // A few keys left in the bin: rank them directly instead of another
+            // histogram pass.  The need-th largest of them is the last winning key; the
+            // keys equal to it are then taken in token order as after a last pass.
+            for (int i = tid; i < (int)C; i += NT) {
+                const uint32_t key = skey[i];
+                if (((uint64_t)key >> shift) == prefix) few[atomicAdd(&nfew, 1u)] = key;
+            }
+            __syncthreads();
+            if (tid < (int)in_bin) {
+                const uint32_t kv = few[tid];
+                uint32_t gt = 0u, eq = 0u;
+                for (uint32_t j = 0; j < in_bin; ++j) {
+                    gt += few[j] > kv;
+                    eq += few[j] == kv;
+                }
+                if (gt < need && need <= gt + eq) {  // the same for equal keys
+                    few_key = kv;
+                    few_above = gt;
+                }
+            }
+            __syncthreads();
+            prefix = few_key;
+            need -= few_above;
+            shift = 0;
+            break;
+        }
     }
     // ordered output: greater keys all win; of the keys equal to the prefix, the `need`
     // first in token order
