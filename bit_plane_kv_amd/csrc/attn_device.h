@@ -202,6 +202,8 @@ constexpr int kShares = 16;
 constexpr int kShareGroups = 8;
 constexpr int kSharesPerGroup = kShares / kShareGroups;
 constexpr int kPartFloats = kD + 4;  // a partial result: O[128], L, M, two unused
+static_assert(kShares % kShareGroups == 0 && kShareGroups * kD <= kShares * 64,
+              "the one-workgroup form merges every group's channels at once");
 
 // Share s of k winners: [s k / kShares, (s + 1) k / kShares).
 __device__ __forceinline__ int share_begin(int k, int s) {
