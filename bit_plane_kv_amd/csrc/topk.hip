@@ -116,7 +116,9 @@ __device__ __forceinline__ void find_bin(uint32_t *hist, uint32_t *scan_sh, uint
     __syncthreads();
 }
 
-constexpr int kCandCap = 4096;  // threshold-bin entries refined in LDS
+// A radix pass that leaves at most this many keys in the winning bin is the last: they
+// are ranked directly (each counts the larger and the equal ones).
+constexpr int kFewKeys = 64;
 
 // What the first level of a filtered select reads besides the candidates.
 struct FilterArgs {
@@ -268,10 +270,10 @@ __device__ __forceinline__ void select_chunk(
     int32_t *__restrict__ out_idx, int64_t out_stride, const FilterArgs &fa,
     int32_t *lds_idx = nullptr, bool direct_rescore = false) {
     __shared__ __align__(16) uint32_t hist[4096];
-    __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t scan_sh[17];
     __shared__ uint32_t pick[3];
-    __shared__ uint32_t ncand;
+    __shared__ uint32_t kmm[2][kThreads / 64];  // per-wave least and largest valid key
+    __shared__ uint32_t few[kFewKeys], nfew, few_key, few_above;
     const int tid = threadIdx.x;
     const int64_t start = (int64_t)chunk * kTopkChunk;
     const int len = (int)min((int64_t)kTopkChunk, row_len - start);
@@ -344,68 +346,93 @@ __device__ __forceinline__ void select_chunk(
         for (int e = 0; e < kEPT; ++e) key[e] = e < nvalid ? order_key(x[e]) : 0u;
     }
 
-    // ---- pass 1: top 12 bits of every key
+    // ---- radix select, 12 bits a pass, starting below the bits every valid key shares
+    //      (from their least and largest); a pass that leaves at most kFewKeys keys in the
+    //      winning bin is the last, those keys ranked directly
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int e = 0; e < kEPT; ++e) {
+        if ((vmask >> e) & 1u) {
+            kmin = min(kmin, key[e]);
+            kmax = max(kmax, key[e]);
+        }
+    }
+    kmin = __ockl_wfred_min_u32(kmin);
+    kmax = __ockl_wfred_max_u32(kmax);
     for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
-    if (tid == 0) ncand = 0u;
+    if (tid == 0) nfew = 0u;
+    if ((tid & 63) == 0) {
+        kmm[0][tid >> 6] = kmin;
+        kmm[1][tid >> 6] = kmax;
+    }
     __syncthreads();
     if (kCandOut && kMasked && kr == 0) {  // a chunk without candidates: all filler
         fill_slots(out_val, out_idx, row * out_stride + (int64_t)chunk * min(k, kTopkChunk), 0,
                    min(k, len));
         return;
     }
-    if (vmask == 0xFFFFFFFFu) {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) atomicAdd(&hist[key[e] >> 20], 1u);
-    } else {
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e)
-            if ((vmask >> e) & 1u) atomicAdd(&hist[key[e] >> 20], 1u);
+    for (int w = 0; w < kThreads / 64; ++w) {
+        kmin = min(kmin, kmm[0][w]);
+        kmax = max(kmax, kmm[1][w]);
     }
-    __syncthreads();
-    find_bin(hist, scan_sh, pick, 4096, (uint32_t)kr);
-    uint32_t prefix = pick[0];
-    uint32_t need = (uint32_t)kr - pick[1];
-    uint32_t in_bin = pick[2];
-    int shift = 20;
-
-    if (in_bin != need) {
-        // The k-th largest key lies inside bin `prefix`; refine on its in_bin entries.
-        const bool in_lds = in_bin <= (uint32_t)kCandCap;
-        const int ncands = (int)in_bin;  // entries of the first bin (the list's length)
-        if (in_lds) {  // compact the bin's keys into LDS (any order)
-#pragma unroll
-            for (int e = 0; e < kEPT; ++e) {
-                if (((vmask >> e) & 1u) && (key[e] >> 20) == prefix)
-                    cand[atomicAdd(&ncand, 1u)] = key[e];
-            }
-        }
-        for (int pass = 1; pass < 3; ++pass) {
-            const int sh = pass == 1 ? 8 : 0;
-            const int nb = pass == 1 ? 4096 : 256;
-            __syncthreads();  // previous readers of hist / pick are done
+    // the bits >= shift are the same in every valid key; pbits holds the settled high
+    // bits in place, hmask selects them
+    const uint32_t diff = kmin ^ kmax;
+    int shift = diff == 0u ? 0 : 32 - (int)__clz(diff);
+    uint32_t hmask = shift >= 32 ? 0u : 0xFFFFFFFFu << shift;
+    uint32_t pbits = kmin & hmask;
+    uint32_t need = (uint32_t)kr;
+    for (int pass = 0; shift > 0; ++pass) {
+        const int sd = max(0, shift - 12);
+        const uint32_t dmask = (1u << (shift - sd)) - 1u;
+        if (pass > 0) {  // find_bin ended with a barrier: every read of hist is done
             for (int b = tid; b < 4096; b += kThreads) hist[b] = 0u;
             __syncthreads();
-            if (in_lds) {
-                for (int c = tid; c < ncands; c += kThreads) {
-                    const uint32_t kv = cand[c];
-                    if ((kv >> shift) == prefix) atomicAdd(&hist[(kv >> sh) & (nb - 1)], 1u);
-                }
-            } else {
+        }
 #pragma unroll
-                for (int e = 0; e < kEPT; ++e) {
-                    if (((vmask >> e) & 1u) && (key[e] >> shift) == prefix)
-                        atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
+        for (int e = 0; e < kEPT; ++e) {
+            if (((vmask >> e) & 1u) && (key[e] & hmask) == pbits)
+                atomicAdd(&hist[(key[e] >> sd) & dmask], 1u);
+        }
+        __syncthreads();
+        // find_bin reads bins four at a time: at least 4 (the ones past the digit are 0)
+        find_bin(hist, scan_sh, pick, max(4, (int)dmask + 1), need);
+        pbits |= pick[0] << sd;
+        need -= pick[1];
+        const uint32_t in_bin = pick[2];
+        shift = sd;
+        hmask = 0xFFFFFFFFu << sd;
+        if (in_bin == need) break;  // every entry of the bin is a winner
+        if (shift > 0 && in_bin <= (uint32_t)kFewKeys) {
+            // the need-th largest of the bin's keys is the last winning key; the keys
+            // equal to it are then taken in position order as after a last pass
+#pragma unroll
+            for (int e = 0; e < kEPT; ++e) {
+                if (((vmask >> e) & 1u) && (key[e] & hmask) == pbits)
+                    few[atomicAdd(&nfew, 1u)] = key[e];
+            }
+            __syncthreads();
+            if (tid < (int)in_bin) {
+                const uint32_t kv = few[tid];
+                uint32_t gt = 0u, eq = 0u;
+                for (uint32_t jj = 0; jj < in_bin; ++jj) {
+                    gt += few[jj] > kv;
+                    eq += few[jj] == kv;
+                }
+                if (gt < need && need <= gt + eq) {  // the same for equal keys
+                    few_key = kv;
+                    few_above = gt;
                 }
             }
             __syncthreads();
-            find_bin(hist, scan_sh, pick, nb, need);
-            prefix = (prefix << (pass == 1 ? 12 : 8)) | pick[0];
-            shift = sh;
-            need -= pick[1];
-            in_bin = pick[2];
-            if (in_bin == need) break;  // every entry of the bin is a winner
+            pbits = few_key;
+            need -= few_above;
+            shift = 0;
+            break;
         }
     }
+    const uint32_t prefix = pbits >> shift;  // shift <= 20 here
 
     // ---- ordered output: greater entries all win; of the entries equal to the
     //      threshold prefix, the `need` lowest positions win.  Masks over the thread's
@@ -562,10 +589,6 @@ __device__ __forceinline__ uint32_t block_prefix1(uint32_t v, uint32_t *sh, uint
     *total = all;
     return inc - v + before;
 }
-
-// A radix pass that leaves at most this many keys in the winning bin is the last: they
-// are ranked directly.
-constexpr int kFewKeys = 64;
 
 // The lean select's body for NT threads (256, or 1024 with kDirect).
 template <bool kCandOut, bool kDirect, int NT>
