@@ -92,7 +92,7 @@ size_t step_ws_bytes(int H, int G, int n, int k) {
     return round256(scan_ws_bytes(H, G)) + round256(cand_bytes(H, G, n)) +
            round256(topk_ws_bytes(H * G, n, k)) + round256((size_t)H * G * k * sizeof(int32_t)) +
            round256((size_t)H * FATHOM_D) + round256(filter_mask_bytes(H, G, n)) +
-           round256(filter_redo_bytes(H, G, n)) + round256(attn_part_bytes(H * G, n, k));
+           round256(filter_redo_bytes(H, G, n)) + round256(attn_part_bytes(H * G));
 }
 
 // the grouped step: every score, the top-k levels, the winners, the depths
@@ -544,7 +544,8 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
             launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
     }
     FATHOM_TRY(mark(3));
-    FATHOM_TRY(hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
+    FATHOM_TRY(hip_status(
+        launch_sparse_attn_split(q, K, V, H, G, n, idx, k, sm_scale, out, part, scan_ws, s)));
     return mark(4);
 }
 

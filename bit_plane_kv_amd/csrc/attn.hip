@@ -26,6 +26,21 @@ __global__ __launch_bounds__(kShares * 64) void k_sparse_attn_shares(
                       (int)blockIdx.x);
 }
 
+// Few rows inside a decode step: kShareGroups workgroups a row (blockIdx.y = the group),
+// the parts in the step's workspace, each row's count in its head's meta block (cleared by
+// the step's prepare).
+__global__ __launch_bounds__(kShares * 64) void k_sparse_attn_split(
+    const float *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
+    float sm_scale, uint16_t *__restrict__ out, float *__restrict__ part, char *scan_ws) {
+    const int row = (int)blockIdx.x, h = row / G, g = row - h * G;
+    const int32_t *ix = idx + (size_t)row * k;
+    ScanMeta *meta = reinterpret_cast<ScanMeta *>(scan_ws + (size_t)h * kMetaBytes);
+    attend_group_split(q, K, V, G, n, [ix](int r) { return ix[r]; }, k, (int)blockIdx.y,
+                       sm_scale, row, part + (size_t)row * kShareGroups * kPartFloats,
+                       &meta->attn_done[g], out);
+}
+
 __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src,
                                                      size_t nvec, uint64_t *__restrict__ sink) {
     uint32_t a = 0, b = 0, c = 0, d = 0;
@@ -72,6 +87,22 @@ hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t 
     else
         hipLaunchKernelGGL(k_sparse_attn, dim3(H * G), dim3(256), 0, s, q, K, V, G, n, idx, k,
                            sm_scale, out);
+    return hipGetLastError();
+}
+
+size_t attn_part_bytes(int R) {
+    return R <= kSmallRows ? (size_t)R * kShareGroups * kPartFloats * sizeof(float) : 0;
+}
+
+hipError_t launch_sparse_attn_split(const float *q, const uint16_t *K, const uint16_t *V,
+                                    int H, int G, int n, const int32_t *idx, int k,
+                                    float sm_scale, uint16_t *out, float *part, void *scan_ws,
+                                    hipStream_t s) {
+    if (H * G > kSmallRows)
+        return launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s);
+    hipLaunchKernelGGL(k_sparse_attn_split, dim3(H * G, kShareGroups), dim3(kShares * 64), 0, s,
+                       q, K, V, G, n, idx, k, sm_scale, out, part,
+                       static_cast<char *>(scan_ws));
     return hipGetLastError();
 }
 

@@ -303,6 +303,53 @@ __device__ __forceinline__ void attend_group(const float *__restrict__ q,
     }
 }
 
+// Group grp of row hg in a workgroup of its own (blockIdx picks the group; every thread
+// calls it): the group's part goes to prow[grp] (prow: the row's kShareGroups parts of
+// kPartFloats floats) and the last of the row's groups to finish merges the parts into
+// out[hg], with the arithmetic and order of attend_row_shares.  `count` is the row's
+// counter, zero before the row's first group starts.
+// The parts meet through device-scope stores and loads (written through to, and read from,
+// the level of the memory system every CU sees), ordered by the count: each thread waits
+// until its stores are done before the workgroup takes the count, and the count's last
+// taker reads the parts after it.  A device-scope fence would do the same by writing back
+// and invalidating the whole L2, which costs tens of microseconds here.
+template <class Idx>
+__device__ __forceinline__ void attend_group_split(const float *__restrict__ q,
+                                                   const uint16_t *__restrict__ K,
+                                                   const uint16_t *__restrict__ V, int G,
+                                                   int n, const Idx &idx_of, int k, int grp,
+                                                   float sm_scale, int hg, float *prow,
+                                                   uint32_t *count, uint16_t *out) {
+    __shared__ bool last;
+    const int tid = threadIdx.x;
+    float *mine = prow + grp * kPartFloats;
+    attend_group(q, K, V, G, n, idx_of, k, grp, sm_scale, hg,
+                 [mine](int c, float O, float L, float M) {
+                     __hip_atomic_store(mine + c, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                     if (c == 0) {
+                         __hip_atomic_store(mine + kD, L, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+                         __hip_atomic_store(mine + kD + 1, M, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+                     }
+                 });
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread done
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(count, 1u) == kShareGroups - 1;
+    __syncthreads();
+    if (!last) return;
+    if (tid < kD) {
+        float O, L, M;
+        merge_parts<kShareGroups>(
+            [prow](int p, int j) {
+                return __hip_atomic_load(prow + p * kPartFloats + j, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            },
+            tid, O, L, M);
+        out[(size_t)hg * kD + tid] = float_to_bf16_bits(L > 0.0f ? O / L : 0.0f);
+    }
+}
+
 // All groups of row hg in one workgroup of kShares waves, the output written to out[hg].
 template <class Idx>
 __device__ __forceinline__ void attend_row_shares(const float *__restrict__ q,

@@ -197,9 +197,9 @@ hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand
 // the same select fused with the attention of each row (rows of one chunk, few rows, small
 // k: filtered_attend_applies); idx still receives the winners
 bool filtered_attend_applies(int R, int n, int k);
-// the partial results of the fused select-attend's split attention (0 where it does not
-// apply)
-size_t attn_part_bytes(int R, int n, int k);
+// the partial results of a step's split attention over R query rows (0 above 256 rows,
+// where a row is one workgroup)
+size_t attn_part_bytes(int R);
 hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,
                                        const uint32_t *masks, void *scan_ws, int k,
                                        int32_t *idx, const float *q, const uint16_t *K,
@@ -208,6 +208,13 @@ hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const floa
 hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t *V, int H,
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s);
+// the same inside a decode step: few rows split over several workgroups a row, with the
+// parts in `part` (attn_part_bytes(H*G)) and each row's counter in the prepared scan
+// workspace's meta blocks; the same results as launch_sparse_attn
+hipError_t launch_sparse_attn_split(const float *q, const uint16_t *K, const uint16_t *V,
+                                    int H, int G, int n, const int32_t *idx, int k,
+                                    float sm_scale, uint16_t *out, float *part, void *scan_ws,
+                                    hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint64_t *sink,
                               hipStream_t s);
 hipError_t launch_stream_runs(const void *src, size_t run_bytes, size_t stride_bytes,

@@ -939,10 +939,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_select_direct(
 // winners pass to the attention in LDS, so no index round trip through memory and no
 // second launch.  A row runs as kShareGroups workgroups (blockIdx.z = the group): each
 // makes the same select (it is deterministic) and attends its group's shares of the
-// winners, since the gather of one workgroup is bound by its CU's load rate.  Each leaves
-// its group's partial result in `part`; the last of the row to finish (by a counter in
-// the head's meta block, cleared by the scan's prepare) merges them into the output, in
-// the order and with the arithmetic of the one-workgroup attention.  k <= kFusedMaxK.
+// winners (attend_group_split: the last of the row to finish, by a counter in the head's
+// meta block cleared by the scan's prepare, merges the groups' parts).  k <= kFusedMaxK.
 constexpr int kFusedMaxK = 1024;
 __global__ __launch_bounds__(kThreads, 1) void k_select_attend(
     const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
@@ -951,46 +949,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_select_attend(
     float *__restrict__ part) {
     static_assert(kThreads >= kSharesPerGroup * 64, "a wave a share of the group");
     __shared__ int32_t widx[kFusedMaxK];
-    __shared__ bool last;
     select_kept<false, true, kThreads>(cand, n, row0, k, fa, nullptr, nullptr, out_idx, 0,
                                        widx);
     __syncthreads();  // every winner is in widx
-    const int row = row0 + (int)blockIdx.y, grp = (int)blockIdx.z, tid = (int)threadIdx.x;
-    float *prow = part + (size_t)row * kShareGroups * kPartFloats;
-    float *mine = prow + grp * kPartFloats;
-    // The parts meet through device-scope stores and loads (written through to, and read
-    // from, the level of the memory system every CU sees), ordered by the count: each
-    // thread waits until its stores are done before the workgroup takes the count, and
-    // the count's last taker reads the parts after it.  A device-scope fence would do the
-    // same by writing back and invalidating the whole L2, which here costs tens of us.
-    attend_group(q, K, V, fa.G, (int)n, [](int r) { return widx[r]; }, k, grp, sm_scale, row,
-                 [mine](int c, float O, float L, float M) {
-                     __hip_atomic_store(mine + c, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                     if (c == 0) {
-                         __hip_atomic_store(mine + kD, L, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-                         __hip_atomic_store(mine + kD + 1, M, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-                     }
-                 });
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread done
-    __syncthreads();
+    const int row = row0 + (int)blockIdx.y, grp = (int)blockIdx.z;
     const int h = row / fa.G, g = row - h * fa.G;
     ScanMeta *meta =
         reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws) + (size_t)h * kMetaBytes);
-    if (tid == 0) last = atomicAdd(&meta->attn_done[g], 1u) == kShareGroups - 1;
-    __syncthreads();
-    if (!last) return;
-    if (tid < kD) {
-        float O, L, M;
-        merge_parts<kShareGroups>(
-            [prow](int p, int j) {
-                return __hip_atomic_load(prow + p * kPartFloats + j, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            },
-            tid, O, L, M);
-        out[(size_t)row * kD + tid] = float_to_bf16_bits(L > 0.0f ? O / L : 0.0f);
-    }
+    attend_group_split(q, K, V, fa.G, (int)n, [](int r) { return widx[r]; }, k, grp, sm_scale,
+                       row, part + (size_t)row * kShareGroups * kPartFloats,
+                       &meta->attn_done[g], out);
 }
 
 template <bool kExplicit, bool kCandOut>
@@ -1077,10 +1045,6 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
 
 bool filtered_attend_applies(int R, int n, int k) {
     return topk_levels(n, k).n_levels == 0 && R <= kDirectRows && k <= kFusedMaxK;
-}
-
-size_t attn_part_bytes(int R, int n, int k) {
-    return filtered_attend_applies(R, n, k) ? (size_t)R * kShareGroups * kPartFloats * 4 : 0;
 }
 
 hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,
