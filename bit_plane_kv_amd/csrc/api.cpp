@@ -507,6 +507,10 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     // sample, or B = 0: every score of a row is the same), or the heads read more than
     // 480 planes (the filter keeps no records for them): scan all, then select
     const bool full = scores_out || sample_rank(n, k) == 0 || B == 0 || B > 480;
+    // K/V rows read from pinned host memory: one attention workgroup a row, which the link
+    // serves better than a row split over several (8.4 MB of a 1M-token layer's rows: 154
+    // against 171 us split), so select and attention stay separate launches
+    const bool host_kv = is_pinned_host(K) || is_pinned_host(V);
     FATHOM_TRY(mark(0));
     if (!full && filtered_attend_applies(H * G, n, k) && front_fused_applies(*st, G)) {
         // few heads of one-chunk rows (a layer of a decode step): plan, prepare and the
@@ -516,6 +520,14 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
             launch_front_fused(*st, q, G, B, k, depth, scan_ws, scores, masks, s)));
         FATHOM_TRY(mark(1));
         FATHOM_TRY(mark(2));
+        if (host_kv) {
+            FATHOM_TRY(hip_status(
+                launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
+            FATHOM_TRY(mark(3));
+            FATHOM_TRY(
+                hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
+            return mark(4);
+        }
         FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k, idx,
                                                           q, K, V, sm_scale, out, part, s)));
         FATHOM_TRY(mark(3));
@@ -531,7 +543,7 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     } else {  // the filtering scan keeps the candidates only
         FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
         FATHOM_TRY(mark(2));
-        if (filtered_attend_applies(H * G, n, k)) {
+        if (filtered_attend_applies(H * G, n, k) && !host_kv) {
             // few rows of one chunk (a layer of a decode step): select and attention in one
             // kernel; its time falls in the select phase, the attention phase is empty
             FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k,
@@ -544,8 +556,12 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
             launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
     }
     FATHOM_TRY(mark(3));
-    FATHOM_TRY(hip_status(
-        launch_sparse_attn_split(q, K, V, H, G, n, idx, k, sm_scale, out, part, scan_ws, s)));
+    // few rows from device memory: each row's attention split over several workgroups
+    if (host_kv)
+        FATHOM_TRY(hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
+    else
+        FATHOM_TRY(hip_status(launch_sparse_attn_split(q, K, V, H, G, n, idx, k, sm_scale, out,
+                                                       part, scan_ws, s)));
     return mark(4);
 }
 

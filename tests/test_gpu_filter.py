@@ -328,3 +328,35 @@ def test_timed_step_equals_step_and_times_its_phases(with_scores):
     assert abs(sum(ph) - ev[0].elapsed_time(ev[-1])) < 1e-3 + 1e-3 * sum(ph)
     with pytest.raises(ValueError):
         F.fathom_step_timed(st, q_t, Kd, Vd, B, k, sm, ev[:4])
+
+
+@pytest.mark.parametrize("H,G,n,k", [
+    (2, 4, 20000, 256),   # one-chunk rows, one query set: the fused front
+    (1, 4, 70000, 512),   # rows of several chunks: select levels, then the attention
+    (3, 8, 5000, 64),     # two query sets: the separate scan, then the select
+])
+def test_step_with_host_kv_equals_device_kv(H, G, n, k):
+    """K/V rows in pinned host memory keep one attention workgroup a row (select and
+    attention as separate launches); the winners and outputs are those of the step with
+    K/V in device memory, where a row's attention is split over several workgroups, bit
+    for bit (the same merge tree)."""
+    torch = torch_cuda()
+    B = 92
+    print(f"[step host kv] H={H} G={G} n={n} k={k}", flush=True)
+    keys, q, K, V = inputs(107, H, G, n)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    Kh = torch.from_numpy(K).view(torch.bfloat16).pin_memory()
+    Vh = torch.from_numpy(V).view(torch.bfloat16).pin_memory()
+    sm = float(np.float32(1 / np.sqrt(128)))
+    i1 = torch.empty((H, G, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    o1 = F.fathom_step(st, q_t, Kd, Vd, B, k, sm, idx_out=i1)
+    o2 = F.fathom_step(st, q_t, Kh, Vh, B, k, sm, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    ref = oracle.attention(q, K, V, i1.cpu().numpy(), sm)
+    assert np.abs(o2.float().cpu().numpy() - ref).max() <= 2e-2
