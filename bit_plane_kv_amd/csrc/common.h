@@ -40,7 +40,9 @@ constexpr int kDigits = 4;                   // signed base-256 digits per weigh
 //   cnt_exact[8] (candidates whose exact score clears the threshold, counted by the
 //   select); uint32 ovf (bit g: a 256-token block of query g had more candidates than
 //   its record area holds); int32 xthr[8][8] (the filter's integer thresholds, below);
-//   uint32 attn_done[8] (workgroups of query g's split attention that have finished).
+//   uint32 attn_done[8] (workgroups of query g's split attention that have finished);
+//   uint32 sel_done[8] (chunk selects of query g's row that have finished, rows of several
+//   chunks).
 //   record (kblock, lane), lane = 16*kb + 4*w + s:  uint32 row of plane s and of plane
 //   s+4 of group 4*kblock + kb (kSkipRow: no plane, load nothing), then for each set of
 //   4 queries the 8 bytes of A row (lane & 15) = (query 4*set + ((lane & 15) >> 2),
@@ -62,6 +64,7 @@ struct ScanMeta {
     uint32_t ovf;
     int32_t xthr[FATHOM_MAX_G][8];
     uint32_t attn_done[FATHOM_MAX_G];
+    uint32_t sel_done[FATHOM_MAX_G];
 };
 static_assert(sizeof(ScanMeta) <= kMetaBytes, "meta block");
 
@@ -123,9 +126,10 @@ inline size_t cand_bytes(int H, int G, int n) {
 inline size_t filter_mask_bytes(int H, int G, int n) {
     return (size_t)H * G * (size_t)((n + 31) / 32) * sizeof(uint32_t);
 }
-// the select's list of row chunks for the full select: one uint32 per chunk
+// the select's list of row chunks for the full select: two uint32 per chunk (a chunk is
+// listed by its own select, and again when its row of several chunks falls short)
 inline size_t filter_redo_bytes(int H, int G, int n) {
-    return (size_t)H * G * (size_t)((n + FATHOM_TOPK_CHUNK - 1) / FATHOM_TOPK_CHUNK) * 4;
+    return (size_t)H * G * (size_t)((n + FATHOM_TOPK_CHUNK - 1) / FATHOM_TOPK_CHUNK) * 8;
 }
 
 // ---------------------------------------------------------------------------------

@@ -523,6 +523,7 @@ __device__ __forceinline__ int prepare_head(const PrepIn<QS> &in, const int *tc,
             meta->cnt[tid] = 0u;
             meta->cnt_exact[tid] = 0u;
             meta->attn_done[tid] = 0u;
+            meta->sel_done[tid] = 0u;
         }
         if (tid == 0) meta->ovf = 0u;
     }

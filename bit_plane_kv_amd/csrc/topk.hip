@@ -500,21 +500,11 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_chunk(
                                                out_stride, fa);
 }
 
-// A row of several chunks whose chunks the filtered select did not hand over, but which
-// must be rescored: its exact candidate count, summed over its chunks by the select,
-// fell short of k.
-__device__ __forceinline__ bool rescore_whole_row(const FilterArgs &fa, int64_t row, int k) {
-    const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
-    const ScanMeta *meta = reinterpret_cast<const ScanMeta *>(fa.scan_ws + (size_t)h * kMetaBytes);
-    return meta->cnt[g] >= (uint32_t)k && !((meta->ovf >> g) & 1u) &&
-           meta->cnt_exact[g] < (uint32_t)k;
-}
-
-// The row chunks the filtered select handed over (listed as row * nch + chunk; their
-// count is the head-0 meta block's redo field), a grid-stride loop over the list: a
-// small grid, as the list is usually empty.  Rows of several chunks (kCandOut) whose
-// exact count fell short are then redone chunk by chunk, each workgroup checking its
-// own rows (r = blockIdx.x + gridDim.x * thread) first.
+// The row chunks the filtered select handed over, and every chunk of a row of several
+// chunks whose exact count fell short of k (listed as row * nch + chunk; their count is the
+// head-0 meta block's redo field; a chunk may be listed twice, which gives the same
+// output twice), a grid-stride loop over the list: a small grid, as the list is usually
+// empty.
 constexpr int kRedoGrid = 16;
 // The final select (!kCandOut) may use 128 VGPRs, so that it needs no scratch.
 template <bool kCandOut>
@@ -525,35 +515,10 @@ __global__ __launch_bounds__(kThreads, kCandOut ? 8 : 1) void k_topk_redo(
     const uint32_t total = reinterpret_cast<const ScanMeta *>(fa.scan_ws)->redo;
     for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
         const uint32_t item = list[it];
-        const int64_t row = (int64_t)(item / (uint32_t)nch);
-        if (kCandOut && rescore_whole_row(fa, row, k)) continue;  // redone below
-        select_chunk<false, kCandOut, true>(row, (int)(item % (uint32_t)nch), vals, nullptr,
-                                            row_len, row_len, k, out_val, out_idx, out_stride,
-                                            fa);
+        select_chunk<false, kCandOut, true>((int64_t)(item / (uint32_t)nch),
+                                            (int)(item % (uint32_t)nch), vals, nullptr, row_len,
+                                            row_len, k, out_val, out_idx, out_stride, fa);
         __syncthreads();  // LDS is reused by the next item
-    }
-    if constexpr (kCandOut) {
-        __shared__ uint32_t xrows[kThreads];
-        __shared__ uint32_t nx;
-        const int64_t R = (int64_t)fa.H * fa.G;
-        const int64_t step = (int64_t)gridDim.x * kThreads;
-        for (int64_t base = blockIdx.x; base < R; base += step) {
-            if (threadIdx.x == 0) nx = 0u;
-            __syncthreads();
-            const int64_t r = base + (int64_t)gridDim.x * threadIdx.x;
-            if (r < R && rescore_whole_row(fa, r, k)) xrows[atomicAdd(&nx, 1u)] = (uint32_t)r;
-            __syncthreads();
-            const uint32_t cnt = nx;
-            for (uint32_t i = 0; i < cnt; ++i) {
-                const int64_t row = xrows[i];
-                for (int c = 0; c < nch; ++c) {
-                    select_chunk<false, true, true>(row, c, vals, nullptr, row_len, row_len, k,
-                                                    out_val, out_idx, out_stride, fa);
-                    __syncthreads();
-                }
-            }
-            __syncthreads();  // xrows and nx are rewritten next round
-        }
     }
 }
 
@@ -920,12 +885,39 @@ __device__ __forceinline__ void select_kept(
     if (kCandOut) fill_slots(out_val, out_idx, obase, kr, min(k, len));
 }
 
+// kCandOut (rows of several chunks): the row's chunk selects count themselves done, and
+// the last lists all of the row's chunks for the full select when the row's exact count,
+// summed by its chunk selects, fell short of k although its candidates were complete (the
+// chunks of a row that kept fewer than k, or overflowed, were listed by their selects).
+// Each count waits for the workgroup's own exact-count atomic (thread 0's) to be done, and
+// the last reads the sum with a device-scope load after its own count.
 template <bool kCandOut>
 __global__ __launch_bounds__(256) void k_select_kept(
     const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
     uint32_t *__restrict__ list, float *__restrict__ out_val, int32_t *__restrict__ out_idx,
     int64_t out_stride) {
     select_kept<kCandOut, false, 256>(cand, n, row0, k, fa, list, out_val, out_idx, out_stride);
+    if constexpr (kCandOut) {
+        __shared__ bool last;
+        const int64_t row = (int64_t)row0 + blockIdx.y;
+        const int h = (int)(row / fa.G), g = (int)(row - (int64_t)h * fa.G);
+        ScanMeta *meta0 = reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws));
+        ScanMeta *meta = reinterpret_cast<ScanMeta *>(const_cast<char *>(fa.scan_ws) +
+                                                      (size_t)h * kMetaBytes);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_s_waitcnt(0);  // this workgroup's atomics are done
+            last = atomicAdd(&meta->sel_done[g], 1u) == gridDim.x - 1;
+        }
+        __syncthreads();
+        if (last && meta->cnt[g] >= (uint32_t)k && !((meta->ovf >> g) & 1u) &&
+            __hip_atomic_load(&meta->cnt_exact[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                (uint32_t)k) {
+            const uint32_t nch = gridDim.x;
+            for (uint32_t c = threadIdx.x; c < nch; c += 256)
+                list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)row * nch + c;
+        }
+    }
 }
 
 // Like the final select it may use 128 VGPRs, so that it needs no scratch.

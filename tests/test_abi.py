@@ -190,13 +190,14 @@ def test_workspace_formulas():
     assert F.workspace_size(F.OP_TOPK, 32, 1, 1 << 20, 512) == 32 * 32 * 512 * 8
     # scan + top-k: scan workspace, candidate record area (4 bytes per token, rows
     # rounded up to 256-token blocks), kept-token masks (4 bytes per 32 tokens), the top-k
-    # levels and the redo list (4 bytes per row chunk), each rounded up to 256 bytes
+    # levels and the redo list (8 bytes per row chunk: a chunk may be listed by its own
+    # select and again by its row's count check), each rounded up to 256 bytes
     r256 = lambda x: (x + 255) // 256 * 256
     for H, G, n, k in [(2, 4, 100, 10), (288, 4, 32768, 512), (3, 8, 70000, 512)]:
         want = (r256(F.workspace_size(F.OP_SCAN, H, G)) + r256(H * G * r256(n) * 4) +
                 r256(H * G * ((n + 31) // 32) * 4) +
                 r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
-                r256(H * G * ((n + 32767) // 32768) * 4))
+                r256(H * G * ((n + 32767) // 32768) * 8))
         assert F.workspace_size(F.OP_SCAN_TOPK, H, G, n, k) == want
     # grouped step: every score (fp32), the top-k levels, the winners, the depths
     for H, G, n, k in [(2, 4, 100, 10), (288, 4, 32768, 512), (8, 4, 1 << 20, 512)]:
