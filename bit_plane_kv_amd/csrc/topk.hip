@@ -890,7 +890,7 @@ __device__ __forceinline__ void select_kept(
 // summed by its chunk selects, fell short of k although its candidates were complete (the
 // chunks of a row that kept fewer than k, or overflowed, were listed by their selects).
 // Each count waits for the workgroup's own exact-count atomic (thread 0's) to be done, and
-// the last reads the sum with a device-scope load after its own count.
+// the last reads the sum with an atomic after its own count.
 template <bool kCandOut>
 __global__ __launch_bounds__(256) void k_select_kept(
     const float *__restrict__ cand, int64_t n, int row0, int k, FilterArgs fa,
@@ -910,9 +910,14 @@ __global__ __launch_bounds__(256) void k_select_kept(
             last = atomicAdd(&meta->sel_done[g], 1u) == gridDim.x - 1;
         }
         __syncthreads();
+        // the sum is read by an atomic add of 0, performed where the chunk selects' adds
+        // are: a load can be served by a copy of its line in this CU's caches, filled by
+        // the select's earlier load of the overflow word beside it
+        __shared__ uint32_t exact;
+        if (last && threadIdx.x == 0) exact = atomicAdd(&meta->cnt_exact[g], 0u);
+        __syncthreads();
         if (last && meta->cnt[g] >= (uint32_t)k && !((meta->ovf >> g) & 1u) &&
-            __hip_atomic_load(&meta->cnt_exact[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                (uint32_t)k) {
+            exact < (uint32_t)k) {
             const uint32_t nch = gridDim.x;
             for (uint32_t c = threadIdx.x; c < nch; c += 256)
                 list[atomicAdd(&meta0->redo, 1u)] = (uint32_t)row * nch + c;
