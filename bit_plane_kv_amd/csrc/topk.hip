@@ -3,7 +3,8 @@
 //
 // One 1024-thread workgroup ranks one chunk of up to 32768 entries held in registers
 // (32 consecutive positions per thread).  Radix select on order-preserving 32-bit keys
-// (12 + 12 + 8 bit digits, LDS histograms) finds the k-th largest key T and how many
+// (12-bit digits from just below the bits every key shares, LDS histograms; a winning bin
+// of at most 64 keys ranked directly) finds the k-th largest key T and how many
 // entries equal to T are needed; a block-wide scan of (greater, equal) counts in
 // position order then writes the winners in index order, taking the equal entries with
 // the lowest positions.  Rows longer than a chunk are cut into chunks whose top
