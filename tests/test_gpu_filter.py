@@ -360,3 +360,4 @@ def test_step_with_host_kv_equals_device_kv(H, G, n, k):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     ref = oracle.attention(q, K, V, i1.cpu().numpy(), sm)
     assert np.abs(o2.float().cpu().numpy() - ref).max() <= 2e-2
+
