@@ -1,5 +1,6 @@
 // C-ABI entry points of libfathom.so: argument checks on the host (nothing is enqueued
 // when they fail), device-visibility checks of the pointers, then the launches.
+#include <cstddef>
 #include <algorithm>
 #include <cstring>
 #include <mutex>
@@ -95,10 +96,12 @@ size_t step_ws_bytes(int H, int G, int n, int k) {
            round256(filter_redo_bytes(H, G, n)) + round256(attn_part_bytes(H * G));
 }
 
-// the grouped step: every score, the top-k levels, the winners, the depths
+// the grouped step: every score, the top-k levels, the winners, the depths, then the split
+// attention's parts and per-row counters
 size_t step_grouped_ws_bytes(int H, int G, int n, int k) {
     return round256((size_t)H * G * n * sizeof(float)) + round256(topk_ws_bytes(H * G, n, k)) +
-           round256((size_t)H * G * k * sizeof(int32_t)) + round256((size_t)H * FATHOM_D);
+           round256((size_t)H * G * k * sizeof(int32_t)) + round256((size_t)H * FATHOM_D) +
+           round256(attn_part_bytes(H * G)) + round256((size_t)H * G * sizeof(uint32_t));
 }
 
 size_t scan_topk_ws_bytes(int H, int G, int n, int k) {
@@ -359,6 +362,10 @@ int fathom_step_grouped(const fathom_gstore *gs, const float *q, const uint16_t 
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(w);
     w += round256((size_t)H * G * k * sizeof(int32_t));
     uint8_t *depth = depth_out ? depth_out : reinterpret_cast<uint8_t *>(w);
+    w += round256((size_t)H * FATHOM_D);
+    float *part = reinterpret_cast<float *>(w);
+    w += round256(attn_part_bytes(H * G));
+    uint32_t *count = reinterpret_cast<uint32_t *>(w);  // cleared by the plan
 
     fathom_store view{};  // the plan reads planes' shape and var only
     view.n_heads = H;
@@ -368,11 +375,16 @@ int fathom_step_grouped(const fathom_gstore *gs, const float *q, const uint16_t 
     view.planes = gs->planes;
     view.var = gs->var;
     const hipStream_t s = as_stream(stream);
-    FATHOM_TRY(hip_status(launch_plan(view, q, G, B, depth, s)));
+    FATHOM_TRY(hip_status(launch_plan(view, q, G, B, depth, s, count)));
     FATHOM_TRY(hip_status(
         launch_scan_grouped(*gs, q, depth, G, scores, is_pinned_host(gs->planes), s)));
     FATHOM_TRY(hip_status(launch_topk(scores, H * G, n, k, idx, topk_ws, s)));
-    return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
+    // few rows from device memory: each row's attention split over several workgroups (the
+    // same output bits as one workgroup a row)
+    if (is_pinned_host(K) || is_pinned_host(V))
+        return hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s));
+    return hip_status(
+        launch_sparse_attn_split(q, K, V, H, G, n, idx, k, sm_scale, out, part, count, G, s));
 }
 
 int fathom_pack_nibbles(const fathom_store *st, uint8_t *nib, void *stream) {
@@ -560,8 +572,11 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     if (host_kv)
         FATHOM_TRY(hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
     else
-        FATHOM_TRY(hip_status(launch_sparse_attn_split(q, K, V, H, G, n, idx, k, sm_scale, out,
-                                                       part, scan_ws, s)));
+        FATHOM_TRY(hip_status(launch_sparse_attn_split(
+            q, K, V, H, G, n, idx, k, sm_scale, out, part,
+            reinterpret_cast<uint32_t *>(static_cast<char *>(scan_ws) +
+                                         offsetof(ScanMeta, attn_done)),
+            (int)(kMetaBytes / sizeof(uint32_t)), s)));
     return mark(4);
 }
 

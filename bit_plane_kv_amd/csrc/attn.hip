@@ -27,18 +27,18 @@ __global__ __launch_bounds__(kShares * 64) void k_sparse_attn_shares(
 }
 
 // Few rows inside a decode step: kShareGroups workgroups a row (blockIdx.y = the group),
-// the parts in the step's workspace, each row's count in its head's meta block (cleared by
-// the step's prepare).
+// the parts in the step's workspace, row (h, g)'s count at count + h * cstride + g (cleared
+// by an earlier kernel of the step).
 __global__ __launch_bounds__(kShares * 64) void k_sparse_attn_split(
     const float *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
-    float sm_scale, uint16_t *__restrict__ out, float *__restrict__ part, char *scan_ws) {
+    float sm_scale, uint16_t *__restrict__ out, float *__restrict__ part, uint32_t *count,
+    int cstride) {
     const int row = (int)blockIdx.x, h = row / G, g = row - h * G;
     const int32_t *ix = idx + (size_t)row * k;
-    ScanMeta *meta = reinterpret_cast<ScanMeta *>(scan_ws + (size_t)h * kMetaBytes);
     attend_group_split(q, K, V, G, n, [ix](int r) { return ix[r]; }, k, (int)blockIdx.y,
                        sm_scale, row, part + (size_t)row * kShareGroups * kPartFloats,
-                       &meta->attn_done[g], out);
+                       count + (size_t)h * cstride + g, out);
 }
 
 __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src,
@@ -96,13 +96,12 @@ size_t attn_part_bytes(int R) {
 
 hipError_t launch_sparse_attn_split(const float *q, const uint16_t *K, const uint16_t *V,
                                     int H, int G, int n, const int32_t *idx, int k,
-                                    float sm_scale, uint16_t *out, float *part, void *scan_ws,
-                                    hipStream_t s) {
+                                    float sm_scale, uint16_t *out, float *part,
+                                    uint32_t *count, int cstride, hipStream_t s) {
     if (H * G > kSmallRows)
         return launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s);
     hipLaunchKernelGGL(k_sparse_attn_split, dim3(H * G, kShareGroups), dim3(kShares * 64), 0, s,
-                       q, K, V, G, n, idx, k, sm_scale, out, part,
-                       static_cast<char *>(scan_ws));
+                       q, K, V, G, n, idx, k, sm_scale, out, part, count, cstride);
     return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ size_t topk_ws_bytes(int R, int n, int k);
 hipError_t launch_quantize_store(const float *keys, int H, int n, const fathom_store &st,
                                  void *ws, hipStream_t s);
 hipError_t launch_plan(const fathom_store &st, const float *q, int G, int B,
-                       uint8_t *depth, hipStream_t s);
+                       uint8_t *depth, hipStream_t s, uint32_t *zero = nullptr);
 hipError_t launch_plan_fixed(const fathom_store &st, int n_channels, uint8_t *depth,
                              hipStream_t s);
 // k > 0: also sample the candidate thresholds for a top-k of k (0: no filtering)
@@ -213,12 +213,12 @@ hipError_t launch_sparse_attn(const float *q, const uint16_t *K, const uint16_t 
                               int G, int n, const int32_t *idx, int k, float sm_scale,
                               uint16_t *out, hipStream_t s);
 // the same inside a decode step: few rows split over several workgroups a row, with the
-// parts in `part` (attn_part_bytes(H*G)) and each row's counter in the prepared scan
-// workspace's meta blocks; the same results as launch_sparse_attn
+// parts in `part` (attn_part_bytes(H*G)) and row (h, g)'s counter at count + h * cstride + g
+// (zero before the launch); the same results as launch_sparse_attn
 hipError_t launch_sparse_attn_split(const float *q, const uint16_t *K, const uint16_t *V,
                                     int H, int G, int n, const int32_t *idx, int k,
-                                    float sm_scale, uint16_t *out, float *part, void *scan_ws,
-                                    hipStream_t s);
+                                    float sm_scale, uint16_t *out, float *part,
+                                    uint32_t *count, int cstride, hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint64_t *sink,
                               hipStream_t s);
 hipError_t launch_stream_runs(const void *src, size_t run_bytes, size_t stride_bytes,

@@ -5,11 +5,15 @@
 namespace fathom {
 namespace {
 
+// zero (if given): the head's G per-row counters are cleared, for a later kernel of the
+// same step that counts its workgroups per row.
 __global__ __launch_bounds__(256) void k_plan(const float *__restrict__ q,
                                               const float *__restrict__ var, int G, int B,
-                                              uint8_t *__restrict__ depth) {
+                                              uint8_t *__restrict__ depth,
+                                              uint32_t *__restrict__ zero) {
     __shared__ int cnt[kD];
     const int h = blockIdx.x, tid = threadIdx.x;
+    if (zero && tid < G) zero[(size_t)h * G + tid] = 0u;
     float qp[FATHOM_MAX_G], vp;
     plan_load<256>(q, var, G, h, qp, vp);
     plan_from<256>(qp, vp, G, B, cnt);
@@ -34,8 +38,8 @@ __global__ __launch_bounds__(128) void k_plan_fixed(const float *__restrict__ va
 }  // namespace
 
 hipError_t launch_plan(const fathom_store &st, const float *q, int G, int B,
-                       uint8_t *depth, hipStream_t s) {
-    hipLaunchKernelGGL(k_plan, dim3(st.n_heads), dim3(256), 0, s, q, st.var, G, B, depth);
+                       uint8_t *depth, hipStream_t s, uint32_t *zero) {
+    hipLaunchKernelGGL(k_plan, dim3(st.n_heads), dim3(256), 0, s, q, st.var, G, B, depth, zero);
     return hipGetLastError();
 }
 

@@ -199,10 +199,13 @@ def test_workspace_formulas():
                 r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
                 r256(H * G * ((n + 32767) // 32768) * 8))
         assert F.workspace_size(F.OP_SCAN_TOPK, H, G, n, k) == want
-    # grouped step: every score (fp32), the top-k levels, the winners, the depths
+    # grouped step: every score (fp32), the top-k levels, the winners, the depths, then (at
+    # most 256 rows) the split attention's parts (8 groups x 132 floats a row) and a counter
+    # per row
     for H, G, n, k in [(2, 4, 100, 10), (288, 4, 32768, 512), (8, 4, 1 << 20, 512)]:
+        part = H * G * 8 * 132 * 4 if H * G <= 256 else 0
         want = (r256(H * G * n * 4) + r256(F.workspace_size(F.OP_TOPK, H * G, 1, n, k)) +
-                r256(H * G * k * 4) + r256(H * 128))
+                r256(H * G * k * 4) + r256(H * 128) + r256(part) + r256(H * G * 4))
         assert F.workspace_size(F.OP_STEP_GROUPED, H, G, n, k) == want
     with pytest.raises(F.FathomError):
         F.workspace_size(F.OP_STEP_GROUPED, 8, 9, 100, 10)
