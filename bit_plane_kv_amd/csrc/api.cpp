@@ -524,43 +524,37 @@ static int step_impl(const fathom_store *st, const float *q, const uint16_t *K,
     // against 171 us split), so select and attention stay separate launches
     const bool host_kv = is_pinned_host(K) || is_pinned_host(V);
     FATHOM_TRY(mark(0));
-    if (!full && filtered_attend_applies(H * G, n, k) && front_fused_applies(*st, G)) {
+    const bool fused_front = !full && filtered_direct_applies(H * G, n, k) &&
+                             front_fused_applies(*st, G);
+    if (fused_front) {
         // few heads of one-chunk rows (a layer of a decode step): plan, prepare and the
-        // filtering scan in one kernel, then select and attention in one; the plan-prepare
-        // phase holds the first, the scan phase is empty
+        // filtering scan in one kernel; the plan-prepare phase holds it, the scan phase is
+        // empty
         FATHOM_TRY(hip_status(
             launch_front_fused(*st, q, G, B, k, depth, scan_ws, scores, masks, s)));
         FATHOM_TRY(mark(1));
         FATHOM_TRY(mark(2));
-        if (host_kv) {
-            FATHOM_TRY(hip_status(
-                launch_topk_filtered(*st, G, scores, masks, scan_ws, redo, k, idx, topk_ws, s)));
-            FATHOM_TRY(mark(3));
-            FATHOM_TRY(
-                hip_status(launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s)));
-            return mark(4);
+    } else {
+        FATHOM_TRY(
+            hip_status(launch_plan_prepare(*st, q, G, B, full ? 0 : k, depth, scan_ws, s)));
+        FATHOM_TRY(mark(1));
+        if (full) {
+            float *all = scores_out ? scores_out : scores;
+            FATHOM_TRY(hip_status(launch_scan_main(*st, G, all, scan_ws, s)));
+            FATHOM_TRY(mark(2));
+            FATHOM_TRY(hip_status(launch_topk(all, H * G, n, k, idx, topk_ws, s)));
+        } else {  // the filtering scan keeps the candidates only
+            FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
+            FATHOM_TRY(mark(2));
         }
-        FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k, idx,
-                                                          q, K, V, sm_scale, out, part, s)));
-        FATHOM_TRY(mark(3));
-        return mark(4);
     }
-    FATHOM_TRY(hip_status(launch_plan_prepare(*st, q, G, B, full ? 0 : k, depth, scan_ws, s)));
-    FATHOM_TRY(mark(1));
-    if (full) {
-        float *all = scores_out ? scores_out : scores;
-        FATHOM_TRY(hip_status(launch_scan_main(*st, G, all, scan_ws, s)));
-        FATHOM_TRY(mark(2));
-        FATHOM_TRY(hip_status(launch_topk(all, H * G, n, k, idx, topk_ws, s)));
-    } else {  // the filtering scan keeps the candidates only
-        FATHOM_TRY(hip_status(launch_scan_main(*st, G, scores, scan_ws, s, masks)));
-        FATHOM_TRY(mark(2));
+    if (!full) {
         if (filtered_attend_applies(H * G, n, k) && !host_kv) {
-            // few rows of one chunk (a layer of a decode step): select and attention in one
-            // kernel; its time falls in the select phase, the attention phase is empty
-            FATHOM_TRY(hip_status(launch_topk_filtered_attend(*st, G, scores, masks, scan_ws, k,
-                                                              idx, q, K, V, sm_scale, out,
-                                                              part, s)));
+            // as many rows as fill the CUs once (a layer of a decode step): select and
+            // attention in one kernel; its time falls in the select phase, the attention
+            // phase is empty
+            FATHOM_TRY(hip_status(launch_topk_filtered_attend(
+                *st, G, scores, masks, scan_ws, k, idx, q, K, V, sm_scale, out, part, s)));
             FATHOM_TRY(mark(3));
             return mark(4);
         }

@@ -28,8 +28,11 @@ __global__ __launch_bounds__(kShares * 64) void k_sparse_attn_shares(
 
 // Few rows inside a decode step: kShareGroups workgroups a row (blockIdx.y = the group),
 // the parts in the step's workspace, row (h, g)'s count at count + h * cstride + g (cleared
-// by an earlier kernel of the step).
-__global__ __launch_bounds__(kShares * 64) void k_sparse_attn_split(
+// by an earlier kernel of the step).  A workgroup is just the group's waves, so that many
+// fit on a CU.
+constexpr int kSplitThreads = kSharesPerGroup * 64;
+static_assert(kSplitThreads >= kD, "the group's and the row's merges take a thread a channel");
+__global__ __launch_bounds__(kSplitThreads) void k_sparse_attn_split(
     const float *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int G, int n, const int32_t *__restrict__ idx, int k,
     float sm_scale, uint16_t *__restrict__ out, float *__restrict__ part, uint32_t *count,
@@ -100,7 +103,7 @@ hipError_t launch_sparse_attn_split(const float *q, const uint16_t *K, const uin
                                     uint32_t *count, int cstride, hipStream_t s) {
     if (H * G > kSmallRows)
         return launch_sparse_attn(q, K, V, H, G, n, idx, k, sm_scale, out, s);
-    hipLaunchKernelGGL(k_sparse_attn_split, dim3(H * G, kShareGroups), dim3(kShares * 64), 0, s,
+    hipLaunchKernelGGL(k_sparse_attn_split, dim3(H * G, kShareGroups), dim3(kSplitThreads), 0, s,
                        q, K, V, G, n, idx, k, sm_scale, out, part, count, cstride);
     return hipGetLastError();
 }

@@ -198,8 +198,11 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
 hipError_t launch_topk_filtered(const fathom_store &st, int G, const float *cand,
                                 const uint32_t *masks, void *scan_ws, uint32_t *redo_list,
                                 int k, int32_t *idx, void *ws, hipStream_t s);
-// the same select fused with the attention of each row (rows of one chunk, few rows, small
-// k: filtered_attend_applies); idx still receives the winners
+// rows of one chunk, at most 256 of them, small k: the select of the filtering scan's
+// candidates runs one workgroup a row and finishes every row itself
+bool filtered_direct_applies(int R, int n, int k);
+// the same select fused with the attention of each row, for as many rows as fill the
+// device's CUs once (filtered_attend_applies); idx still receives the winners
 bool filtered_attend_applies(int R, int n, int k);
 // the partial results of a step's split attention over R query rows (0 above 256 rows,
 // where a row is one workgroup)

@@ -10,6 +10,8 @@
 // the lowest positions.  Rows longer than a chunk are cut into chunks whose top
 // min(k, chunk) survive as (value, index) candidates, in index order, for the next
 // level, until one chunk remains.
+#include <mutex>
+
 #include "attn_device.h"
 #include "common.h"
 
@@ -1041,8 +1043,33 @@ hipError_t launch_topk(const float *scores, int R, int n, int k, int32_t *idx, v
     return run_levels(scores, R, n, k, idx, ws, s, FilterArgs{}, nullptr);
 }
 
-bool filtered_attend_applies(int R, int n, int k) {
+bool filtered_direct_applies(int R, int n, int k) {
     return topk_levels(n, k).n_levels == 0 && R <= kDirectRows && k <= kFusedMaxK;
+}
+
+// Compute units of the current device (asked once per device; 256 if it cannot be asked).
+int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cus[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        cus[dev] = c;
+    }
+    return cus[dev];
+}
+
+// The fused select and attention launches kShareGroups 1024-thread workgroups a row, each
+// repeating the row's select, one a CU: it pays only while they all run in one round.
+// Beyond that the one-workgroup select and the split attention are far cheaper (at 256 rows
+// on 256 CUs: eight rounds of ~12 us against one select and one gather).
+bool filtered_attend_applies(int R, int n, int k) {
+    return filtered_direct_applies(R, n, k) && (long)R * kShareGroups <= (long)device_cus();
 }
 
 hipError_t launch_topk_filtered_attend(const fathom_store &st, int G, const float *cand,

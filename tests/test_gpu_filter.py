@@ -187,6 +187,12 @@ def test_scan_topk_repairs_rows_that_kept_too_few(H, G, n, k):
     (2, 4, 32768, 512, True),    # ... and rows it must rescore (the sample boosted)
     (1, 4, 32768, 1024, False),  # the largest k of the fused kernel
     (70, 4, 3000, 64, False),    # more than 256 rows: select, redo, then attention
+    # more rows than fill the CUs once with the fused select (8 workgroups a row), at most
+    # 256: the fused front, then a workgroup a row for the select, then the split attention
+    (16, 4, 20000, 256, False),
+    (16, 4, 32768, 512, True),   # ... and rows the select must rescore
+    (40, 4, 3000, 64, False),
+    (12, 8, 9000, 300, False),   # two query sets: the separate scan, then the same select
 ])
 def test_step_filtered_equals_step_full(H, G, n, k, boost):
     """The filtered step (scan with the keep test, select, attention) against the full
