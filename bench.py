@@ -231,6 +231,8 @@ def main():
         per_layer["outputs_max_abs_diff_vs_batched_step"] = float(
             (out.float() - out_layers.float()).abs().max())
         log(f"[bench] per-layer decode: {per_layer}")
+    by_heads = step_by_heads(F, st, q, K, V, B, k, sm_scale, dev, stream)
+    log(f"[bench] step by KV heads: {by_heads}")
 
     # ---------------- per-kernel times (cold caches between launches) ----------------
     kern = kernel_times(F, st, q, K, V, B, k, sm_scale, depth, scores, idx, out, dev,
@@ -317,6 +319,7 @@ def main():
                    "form (36 sequences x 1 layer), not one sequence's token; per-layer "
                    "sequential decode is under decode_per_layer",
         "decode_per_layer": per_layer,
+        "step_by_kv_heads": by_heads,
         "step_phases_ms": phases,
         "step_phase_rooflines": phase_rooflines,
         "cpu_baseline": cpu,
@@ -554,6 +557,40 @@ def step_phases(F, st, q, K, V, B, k, sm, out, ws, stream, steps):
     for i, name in enumerate(PHASES):
         res[name] = round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
     res["step"] = round(float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])), 4)
+    return res
+
+
+def step_by_heads(F, st, q, K, V, B, k, sm, dev, stream, reps=15,
+                  sizes=(8, 16, 32, 64, 128, 288)):
+    """One fathom_step over the first h KV heads of the cache, for several h: the shape the
+    library picks changes with the row count (h x G query rows), and this line shows the
+    step's GPU time across those shapes.  Each step runs after a 1 GiB streaming read
+    (cold last-level cache), bracketed by events on the launch stream; median of `reps`."""
+    import torch
+    G = q.shape[1]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2, dtype=torch.int64, device=dev)
+    n = st.n_tokens
+    res = []
+    for h in [x for x in sizes if x <= st.n_heads]:
+        sv = st.view_heads(0, h)
+        ws = F.step_workspace(sv, G, k, dev)
+        out = torch.empty((h, G, 128), dtype=torch.bfloat16, device=dev)
+        times = []
+        for r in range(reps + 2):
+            F.fathom_stream_read(flush, flush.numel(), sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            F.fathom_step(sv, q[:h], K[:h], V[:h], B, k, sm, out=out, ws=ws)
+            b.record(stream)
+            b.synchronize()
+            if r >= 2:
+                times.append(a.elapsed_time(b))
+        ms = float(np.median(times))
+        res.append({"kv_heads": h, "query_rows": h * G, "ms": round(ms, 4),
+                    "gkeys_per_s": round(h * n / (ms * 1e-3) / 1e9, 2)})
+        del ws, out
+    del flush
     return res
 
 
