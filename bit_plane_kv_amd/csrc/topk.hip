@@ -1048,7 +1048,7 @@ bool filtered_direct_applies(int R, int n, int k) {
 }
 
 // Compute units of the current device (asked once per device; 256 if it cannot be asked).
-int device_cus() {
+static int device_cus() {
     static std::mutex mu;
     static int cus[64] = {0};
     int dev = 0;
