@@ -223,6 +223,38 @@ def test_step_filtered_equals_step_full(H, G, n, k, boost):
     assert np.abs(bf16_to_f32(o2) - ref_out).max() <= 2e-2
 
 
+def test_step_rows_do_not_depend_on_the_kernels_shape():
+    """A row's winners and output bits are the same whichever shape the step takes for
+    the call: 8 KV heads x 4 queries (32 rows: select and attention in one kernel, eight
+    workgroups a row) against the same heads plus one more (36 rows: a select workgroup a
+    row, then the split attention), and the first 72 heads (288 rows: the lean select and
+    a workgroup a row for the attention, whose softmax merges in another order: there the
+    winners are compared exactly and the outputs within a rounding)."""
+    torch = torch_cuda()
+    H, G, n, B, k = 72, 4, 6000, 92, 256
+    print(f"[step shapes] H={H} G={G} n={n} B={B} k={k}", flush=True)
+    keys, q, K, V = inputs(131, H, G, n)
+    st, _ = store_from_keys(keys)
+    q_t = to_dev(q)
+    Kd = to_dev(K).view(torch.bfloat16)
+    Vd = to_dev(V).view(torch.bfloat16)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    res = {}
+    for h in (8, 9, 72):
+        idx = torch.empty((h, G, k), dtype=torch.int32, device="cuda")
+        out = F.fathom_step(st.view_heads(0, h), q_t[:h], Kd[:h], Vd[:h], B, k, sm, idx_out=idx)
+        res[h] = (idx, out)
+    torch.cuda.synchronize()
+    for h in (9, 72):
+        assert torch.equal(res[h][0][:8], res[8][0])
+    assert torch.equal(res[9][1][:8], res[8][1])
+    # at most one bf16 rounding step apart (8 significant bits)
+    a, b = res[72][1][:9].float(), res[9][1].float()
+    assert bool(((a - b).abs() <= torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 1e-6).all())
+    ref = oracle.attention(q, K, V, res[72][0].cpu().numpy(), sm)
+    assert np.abs(bf16_to_f32(res[72][1]) - ref).max() <= 2e-2
+
+
 @pytest.mark.parametrize("B,n,k", [(0, 9000, 100), (92, 3000, 2900), (92, 40000, 16384),
                                    (512, 33000, 512)])
 def test_step_without_scores_out_equals_step_with(B, n, k):
